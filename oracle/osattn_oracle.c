@@ -1,0 +1,269 @@
+/*
+ * osattn_oracle.c -- plain, slow, obviously-correct CPU oracle for exact
+ * scaled-dot-product attention and its gradient, in double precision.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the test-suite, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code, header, table or helper with the
+ * HIP library: it includes only the C standard library and OpenMP.
+ *
+ * What it computes (the definitions, written out with no blocking, fusion or
+ * online recurrence):
+ *
+ *   Forward -- TIGA-lang "Attention and dense relations" (注意力与稠密关系),
+ *   equations of the sections on full attention (全量注意力，无掩码), the causal
+ *   dense relation (因果稠密关系) and varlen causal attention
+ *   (用图组合表达 varlen 因果注意力):
+ *       s_hij  = <k_hj, q_hi> * scale                 (scale given; the pages
+ *                                                      use D^-1/2)
+ *       out_hi = sum_{j in A(i)} softmax_j(s_hi.) v_hj
+ *   with the admitted key set A(i):
+ *       dense          : all j < n_k
+ *       causal         : j <= i                (n_q == n_k)
+ *       varlen         : cu_b <= j < cu_{b+1}, where cu_b <= i < cu_{b+1}
+ *       varlen causal  : the varlen set intersected with j <= i
+ *   The softmax is the two-pass textbook form: pass 1 takes the row maximum
+ *   m_i, pass 2 forms p_ij = exp(s_ij - m_i) / l_i with
+ *   l_i = sum_j exp(s_ij - m_i), and the output is sum_j p_ij v_j.
+ *   The row statistics (m_i, l_i) are returned because the method persists
+ *   exactly this O(N) state for the backward (OCANNL "Module
+ *   Ir.Online_softmax", fourth rewrite bullet; TIGA-lang GAT section, the
+ *   training remark).  m is in natural-log units of the scaled score.
+ *
+ *   Backward -- OCANNL "Module Ir.Online_softmax", third rewrite bullet
+ *   (the composed backward).  Written in its chain-rule (Jacobian) form, NOT
+ *   with the per-row shortcut D = sum(dO * O), so that tests can check that
+ *   shortcut against this definition:
+ *       P_ij    = exp(s_ij - m_i) / l_i  on A(i), 0 elsewhere
+ *       dV_j    = sum_i P_ij dO_i
+ *       dP_ij   = <dO_i, v_j>
+ *       delta_i = sum_j P_ij dP_ij
+ *       dS_ij   = P_ij (dP_ij - delta_i)
+ *       dQ_i    = scale * sum_j dS_ij k_j
+ *       dK_j    = scale * sum_i dS_ij q_i
+ *
+ * Layout: every array is (H, N, D) row-major and contiguous, in double.
+ * Parallelism: OpenMP over independent (head, row) pairs only; every output
+ * element is produced by one thread with a fixed serial summation order, so
+ * results do not depend on the thread count.
+ *
+ * Return value of every entry point: 0 on success, -1 on an invalid
+ * argument (null pointer, non-positive size, malformed cu_seqlens, causal
+ * with n_q != n_k), -2 if a work buffer cannot be allocated.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Admitted key interval [lo, hi) of query row i (A(i) above). */
+static void admitted_keys(int64_t i, int64_t n_k, int causal,
+                          const int32_t *cu_seqlens, int num_seqs,
+                          int64_t *lo, int64_t *hi)
+{
+    int64_t a = 0, b = n_k;
+    if (cu_seqlens) {
+        for (int s = 0; s < num_seqs; ++s) {
+            if (cu_seqlens[s] <= i && i < cu_seqlens[s + 1]) {
+                a = cu_seqlens[s];
+                b = cu_seqlens[s + 1];
+                break;
+            }
+        }
+    }
+    if (causal && b > i + 1) b = i + 1;
+    *lo = a;
+    *hi = b;
+}
+
+static int check_args(int H, int64_t n_q, int64_t n_k, int D, int causal,
+                      const int32_t *cu_seqlens, int num_seqs)
+{
+    if (H <= 0 || n_q <= 0 || n_k <= 0 || D <= 0) return -1;
+    if (causal && n_q != n_k) return -1;
+    if (cu_seqlens) {
+        if (num_seqs <= 0 || n_q != n_k) return -1;
+        if (cu_seqlens[0] != 0 || cu_seqlens[num_seqs] != n_q) return -1;
+        for (int s = 0; s < num_seqs; ++s)
+            if (cu_seqlens[s + 1] < cu_seqlens[s]) return -1;
+    }
+    return 0;
+}
+
+static double dot(const double *a, const double *b, int D)
+{
+    double acc = 0.0;
+    for (int d = 0; d < D; ++d) acc += a[d] * b[d];
+    return acc;
+}
+
+/*
+ * Forward for a list of (head, row) pairs.  rows[r] = h * n_q + i; when rows
+ * is NULL all H * n_q pairs are computed in order.  Outputs are indexed by
+ * position in the list: o[r * D + d], m[r], l[r].
+ */
+int oracle_attn_fwd_rows(int H, int64_t n_q, int64_t n_k, int D,
+                         const double *q, const double *k, const double *v,
+                         double scale, int causal,
+                         const int32_t *cu_seqlens, int num_seqs,
+                         const int64_t *rows, int64_t n_rows,
+                         double *o, double *m, double *l)
+{
+    if (!q || !k || !v || !o || !m || !l) return -1;
+    if (check_args(H, n_q, n_k, D, causal, cu_seqlens, num_seqs)) return -1;
+    if (!rows) n_rows = (int64_t)H * n_q;
+    int status = 0;
+
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)n_k);
+        if (!s) {
+#pragma omp atomic write
+            status = -2;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            if (!s) continue;
+            int64_t flat = rows ? rows[r] : r;
+            int64_t h = flat / n_q, i = flat % n_q;
+            const double *qi = q + (h * n_q + i) * D;
+            const double *kh = k + h * n_k * D;
+            const double *vh = v + h * n_k * D;
+            double *oi = o + r * D;
+            int64_t lo, hi;
+            admitted_keys(i, n_k, causal, cu_seqlens, num_seqs, &lo, &hi);
+
+            /* scores, then pass 1: the row maximum */
+            double mx = -INFINITY;
+            for (int64_t j = lo; j < hi; ++j) {
+                s[j] = dot(kh + j * D, qi, D) * scale;
+                if (s[j] > mx) mx = s[j];
+            }
+            /* pass 2: normaliser, then normalised weights against v */
+            double sum = 0.0;
+            for (int64_t j = lo; j < hi; ++j) sum += exp(s[j] - mx);
+            for (int d = 0; d < D; ++d) oi[d] = 0.0;
+            for (int64_t j = lo; j < hi; ++j) {
+                double p = exp(s[j] - mx) / sum;
+                for (int d = 0; d < D; ++d) oi[d] += p * vh[j * D + d];
+            }
+            m[r] = mx;
+            l[r] = sum;
+        }
+        free(s);
+    }
+    return status;
+}
+
+int oracle_attn_fwd(int H, int64_t n_q, int64_t n_k, int D,
+                    const double *q, const double *k, const double *v,
+                    double scale, int causal,
+                    const int32_t *cu_seqlens, int num_seqs,
+                    double *o, double *m, double *l)
+{
+    return oracle_attn_fwd_rows(H, n_q, n_k, D, q, k, v, scale, causal,
+                                cu_seqlens, num_seqs, NULL, 0, o, m, l);
+}
+
+/*
+ * Backward in the chain-rule form above.  For each head it materialises the
+ * probability matrix P and the score gradient dS as (n_q, n_k) arrays
+ * (that is what the composed form does; it is the oracle, not the method).
+ * Optional outputs m_out, l_out, delta_out (H, n_q) may be NULL.
+ */
+int oracle_attn_bwd(int H, int64_t n_q, int64_t n_k, int D,
+                    const double *q, const double *k, const double *v,
+                    const double *dout, double scale, int causal,
+                    const int32_t *cu_seqlens, int num_seqs,
+                    double *dq, double *dk, double *dv,
+                    double *m_out, double *l_out, double *delta_out)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
+    if (check_args(H, n_q, n_k, D, causal, cu_seqlens, num_seqs)) return -1;
+
+    double *P = (double *)malloc(sizeof(double) * (size_t)(n_q * n_k));
+    double *dS = (double *)malloc(sizeof(double) * (size_t)(n_q * n_k));
+    if (!P || !dS) {
+        free(P);
+        free(dS);
+        return -2;
+    }
+
+    for (int h = 0; h < H; ++h) {
+        const double *qh = q + (int64_t)h * n_q * D;
+        const double *kh = k + (int64_t)h * n_k * D;
+        const double *vh = v + (int64_t)h * n_k * D;
+        const double *doh = dout + (int64_t)h * n_q * D;
+        double *dqh = dq + (int64_t)h * n_q * D;
+        double *dkh = dk + (int64_t)h * n_k * D;
+        double *dvh = dv + (int64_t)h * n_k * D;
+
+        /* Row-wise: P, dP, delta, dS, dQ. */
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t i = 0; i < n_q; ++i) {
+            double *Pi = P + i * n_k, *dSi = dS + i * n_k;
+            const double *qi = qh + i * D, *doi = doh + i * D;
+            int64_t lo, hi;
+            admitted_keys(i, n_k, causal, cu_seqlens, num_seqs, &lo, &hi);
+            for (int64_t j = 0; j < n_k; ++j) Pi[j] = dSi[j] = 0.0;
+
+            double mx = -INFINITY;
+            for (int64_t j = lo; j < hi; ++j) {
+                Pi[j] = dot(kh + j * D, qi, D) * scale; /* s_ij for now */
+                if (Pi[j] > mx) mx = Pi[j];
+            }
+            double sum = 0.0;
+            for (int64_t j = lo; j < hi; ++j) sum += exp(Pi[j] - mx);
+            for (int64_t j = lo; j < hi; ++j) Pi[j] = exp(Pi[j] - mx) / sum;
+
+            double delta = 0.0;
+            for (int64_t j = lo; j < hi; ++j) {
+                dSi[j] = dot(doi, vh + j * D, D); /* dP_ij for now */
+                delta += Pi[j] * dSi[j];
+            }
+            for (int64_t j = lo; j < hi; ++j) dSi[j] = Pi[j] * (dSi[j] - delta);
+
+            for (int d = 0; d < D; ++d) {
+                double acc = 0.0;
+                for (int64_t j = lo; j < hi; ++j) acc += dSi[j] * kh[j * D + d];
+                dqh[i * D + d] = scale * acc;
+            }
+            if (m_out) m_out[(int64_t)h * n_q + i] = mx;
+            if (l_out) l_out[(int64_t)h * n_q + i] = sum;
+            if (delta_out) delta_out[(int64_t)h * n_q + i] = delta;
+        }
+
+        /* Column-wise: dV and dK (P and dS are zero outside A(i)); each
+         * element sums over i in increasing order. */
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t j = 0; j < n_k; ++j) {
+            double *dvj = dvh + j * D, *dkj = dkh + j * D;
+            for (int d = 0; d < D; ++d) dvj[d] = dkj[d] = 0.0;
+            for (int64_t i = 0; i < n_q; ++i) {
+                double p = P[i * n_k + j], ds = dS[i * n_k + j];
+                for (int d = 0; d < D; ++d) {
+                    dvj[d] += p * doh[i * D + d];
+                    dkj[d] += ds * qh[i * D + d];
+                }
+            }
+            for (int d = 0; d < D; ++d) dkj[d] *= scale;
+        }
+    }
+    free(P);
+    free(dS);
+    return 0;
+}
+
+/* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
