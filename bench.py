@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Online-softmax attention throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME | --all]
+
+A step is one pass of the attention hot path over one batch of seeded
+synthetic input already resident in HBM: the forward (one fused kernel), or
+forward + backward for the workload that includes the backward.  After W
+untimed steps, K steps are timed between two device synchronisations; value is
+the algorithmic TFLOP/s of the whole step (forward 4 N_q N_k D H, halved for
+causal, summed per sequence for varlen; backward 2.5x the forward).  Rank 0
+prints ONE JSON line (one per workload with --all) that also carries:
+
+  roofline     : the dominant kernel's algorithmic FLOPs per launch over its
+                 average launch duration (HIP events around each launch on the
+                 launch stream), against MI355X's dense MFMA peak for its dtype;
+                 traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE /
+                 WRITE_SIZE counters recorded in profiles/traffic.json, or null
+                 when the kernel sources changed since they were recorded;
+  cpu_baseline : the f64 CPU oracle timed on this host's cores on a bounded
+                 row sample of the same workload (a reported baseline only);
+  parity       : max error of sampled output rows against that oracle.
+Only one GPU is used; --gpus above 1 exits with a message.
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOP/s and % of MFMA peak on 1×MI355X"
+DEFAULT_WORKLOAD = "dense_n1024_h4_d64_f16"
+# MI355X dense MFMA peaks (TFLOP/s) by MFMA input type.
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
+TOL = {"f32": 1e-4, "f16": 2e-3, "bf16": 1e-2}
+
+
+def fwd_flops(w) -> float:
+    if w.lengths is not None:
+        per = 2.0 if w.causal else 4.0
+        return float(sum(per * L * L * w.D * w.H for L in w.lengths))
+    f = 4.0 * w.n_q * w.n_k * w.D * w.H
+    return f / 2 if w.causal else f
+
+
+def bwd_flops(w) -> float:
+    return 2.5 * fwd_flops(w)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "online_softmax_attention_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, kernel: str):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(workload)
+    if not rec or rec.get("kernel") != kernel or rec.get("source_sha") != kernel_source_sha():
+        return None
+    return rec.get("traffic_bytes")
+
+
+def upload(inp, torch, np):
+    def up(x):
+        if x is None:
+            return None
+        if inp.w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    cu = None
+    if inp.cu_seqlens is not None:
+        cu = torch.tensor(inp.cu_seqlens, dtype=torch.int32, device="cuda")
+    return up(inp.q), up(inp.k), up(inp.v), up(inp.do), cu
+
+
+def sample_rows(w, np, per_head=24, seed=1):
+    rng = np.random.default_rng(seed)
+    rows = []
+    for h in range(w.H):
+        pick = set(rng.integers(0, w.n_q, per_head).tolist()) | {0, w.n_q - 1}
+        rows += [h * w.n_q + i for i in sorted(pick)]
+    return np.array(rows, dtype=np.int64)
+
+
+def admitted_count(w, i, cu):
+    if cu is not None:
+        b = int(np.searchsorted(cu, i, side="right")) - 1
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        return (i + 1 - lo) if w.causal else (hi - lo)
+    return (i + 1) if w.causal else w.n_k
+
+
+def cpu_baseline(w, inp, oracle, np, budget_s=10.0):
+    """Time the oracle forward on row chunks of the workload until ~budget_s."""
+    rng = np.random.default_rng(12345)
+    order = rng.permutation(w.H * w.n_q)
+    chunk = 256
+    flops = 0.0
+    spent = 0.0
+    rows_done = 0
+    passes = 0
+    pos = 0
+    cu = inp.cu_seqlens
+    while spent < budget_s and passes < 50:
+        rows = np.sort(order[pos:pos + chunk])
+        t0 = time.perf_counter()
+        oracle.attn_fwd(inp.q32, inp.k32, inp.v32, w.softmax_scale, causal=w.causal,
+                        cu_seqlens=cu, rows=rows)
+        spent += time.perf_counter() - t0
+        flops += sum(4.0 * admitted_count(w, int(r % w.n_q), cu) * w.D for r in rows)
+        rows_done += len(rows)
+        pos += chunk
+        if pos >= len(order):
+            pos = 0
+            passes += 1
+        chunk = min(chunk * 2, 16384)
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "f64 two-pass oracle forward on %d random (head, query) rows of the "
+                      "workload (%.1f s on host cores)" % (rows_done, spent)}
+
+
+def time_launches(fn, torch, n):
+    """Average device duration of fn() over n launches, HIP events per launch."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return sum(ms) / len(ms), sorted(ms)[len(ms) // 2]
+
+
+def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True):
+    w = W.WORKLOADS[name]
+    inp = W.make_inputs(w)
+    q, k, v, do, cu = upload(inp, torch, np)
+    max_seqlen = max(w.lengths) if w.lengths else None
+    H, D = w.H, w.D
+    o = torch.empty((H, w.n_q, D), dtype=torch.float32, device="cuda")
+    m = torch.empty((H, w.n_q), dtype=torch.float32, device="cuda")
+    l = torch.empty_like(m)
+    fwd_out = (o, m, l)
+
+    def fwd():
+        osa.fwd(q, k, v, scale=w.softmax_scale, causal=w.causal, cu_seqlens=cu,
+                max_seqlen=max_seqlen, check=False, out=fwd_out)
+
+    bw = None
+    if w.backward:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        nbytes = osa.bwd_workspace_bytes(q.dtype, H, w.n_q, w.n_k, D, w.causal, cu, max_seqlen or 0)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+
+        def bw():
+            osa.bwd(q, k, v, o, do, m, l, scale=w.softmax_scale, causal=w.causal, cu_seqlens=cu,
+                    max_seqlen=max_seqlen, check=False, workspace=ws, out=(dq, dk, dv))
+
+    def step():
+        fwd()
+        if bw is not None:
+            bw()
+
+    # parity on sampled rows before timing
+    step()
+    torch.cuda.synchronize()
+    rows = sample_rows(w, np)
+    ro, rm, rl = oracle.attn_fwd(inp.q32, inp.k32, inp.v32, w.softmax_scale, causal=w.causal,
+                                 cu_seqlens=inp.cu_seqlens, rows=rows)
+    og = o.reshape(-1, D).cpu().numpy()[rows]
+    err = float(np.max(np.abs(og - ro)))
+    parity = {"max_abs_err_o": err, "tol": TOL[w.dtype], "rows": int(len(rows)),
+              "ok": bool(err <= TOL[w.dtype])}
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    if steps <= 0:  # auto: about 0.5 s of timed work, at least 100 steps
+        t0 = time.perf_counter()
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        per = (time.perf_counter() - t0) / 10
+        steps = int(min(20000, max(100, 0.5 / max(per, 1e-7))))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / steps
+    step_flops = fwd_flops(w) + (bwd_flops(w) if w.backward else 0.0)
+    value = step_flops / (wall / steps) / 1e12
+
+    # dominant kernel: the fused forward (the only kernel of a forward step)
+    kern = "fwd16_kernel" if w.dtype != "f32" else "fwd32_kernel"
+    n_launch = max(100, min(steps, 2000))
+    avg_ms, med_ms = time_launches(fwd, torch, n_launch)
+    achieved = fwd_flops(w) / (avg_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": recorded_traffic(name, kern),
+                "kernel": kern, "launch_us_avg": avg_ms * 1e3, "launch_us_median": med_ms * 1e3,
+                "launches": n_launch, "flops_per_launch": fwd_flops(w)}
+    out = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+           "warmup": warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+           "data": "synthetic: seeded N(0,1) q,k,v%s (numpy default_rng seed %d) rounded to %s"
+                   % (",dO" if w.backward else "", w.seed, w.dtype),
+           "config": {"workload": name, "H": H, "n_q": w.n_q, "n_k": w.n_k, "D": D,
+                      "causal": w.causal, "varlen_seqs": len(w.lengths) if w.lengths else 0,
+                      "pass": "fwd+bwd" if w.backward else "fwd",
+                      "layout": "(H, N, D)", "output": "O f32, m and l f32"},
+           "pct_of_peak": 100.0 * value / peak,
+           "event_ms_per_step": e0.elapsed_time(e1) / steps,
+           "roofline": roofline, "parity": parity}
+    if with_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, inp, oracle, np)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=0, help="timed steps (0 = auto, ~0.5 s)")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--all", action="store_true", help="one JSON line per workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path "
+                         "(--gpus %d requested)\n" % args.gpus)
+        sys.exit(2)
+
+    import torch
+
+    import online_softmax_attention_amd as osa
+    import oracle
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        sys.stderr.write("bench.py needs a GPU\n")
+        sys.exit(1)
+    osa.load()
+    names = W.ORDER if args.all else [args.workload]
+    for name in names:
+        res = run_workload(name, args.steps, args.warmup, torch, np, osa, W, oracle,
+                           with_cpu=not args.no_cpu)
+        print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+/*
+ * osattn.h -- C ABI of the online-softmax attention library for AMD MI355X
+ * (gfx950).  Library: online_softmax_attention_amd/libosattn.so.
+ *
+ * What the library computes
+ * -------------------------
+ * Exact scaled-dot-product attention for H independent heads:
+ *
+ *     s_hij  = scale * <q_hi, k_hj>
+ *     O_hi   = sum_{j in A(i)} exp(s_hij - m_hi) v_hj / l_hi
+ *     m_hi   = max_{j in A(i)} s_hij,   l_hi = sum_{j in A(i)} exp(s_hij - m_hi)
+ *
+ * (TIGA-lang "Attention and dense relations": the equations of the full
+ * attention, causal dense relation and varlen causal sections.)  The admitted
+ * key set A(i) is every key (dense), keys j <= i (causal), the keys of the
+ * query's own sequence under cu_seqlens (varlen), or both (varlen causal).
+ * The forward is one fused pass per query tile that scans key/value blocks with
+ * the online-softmax recurrence: running row maximum, rescaled running sum and
+ * rescaled output numerator U, with O = U / l after the last block (OCANNL
+ * "Module Ir.Online_softmax", first and fourth rewrite bullets).  It never
+ * materialises an (N_q, N_k) buffer.  The backward recomputes the
+ * probabilities from (m, l) and uses the per-row term D_i = sum_d dO_id O_id
+ * (the same page, third bullet: the fused backward).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named q, k, v, o, d_o, dq, dk, dv, m, l, cu_seqlens and
+ *    workspace are DEVICE pointers.  The caller owns all memory; the library
+ *    allocates nothing and keeps no pointer after the enqueued work finishes.
+ *    Outputs must not alias inputs or each other.
+ *  - Tensors are 3-D (head, position, feature) with the feature index
+ *    contiguous (stride 1) and element strides stride_h (between heads) and
+ *    stride_n (between positions).  (H, N, D) row-major storage has
+ *    stride_h = N*D, stride_n = D; (N, H, D) storage has stride_h = D,
+ *    stride_n = H*D.  k and v share one stride pair; q, d_o and dq share one;
+ *    dk and dv use the k/v pair; o has its own pair.
+ *  - Element types: dtype OSATTN_F32, OSATTN_F16 or OSATTN_BF16 for q, k, v,
+ *    d_o, dq, dk, dv.  o is always f32.  m and l are f32, laid out (H, n_q)
+ *    contiguously; m is in natural-log units of the scaled score.
+ *  - Alignment: q, k, v, d_o, dq, dk, dv, o must be 16-byte aligned and their
+ *    strides multiples of 16 bytes' worth of elements (8 for f16/bf16, 4 for
+ *    f32); otherwise OSATTN_ERR_ALIGNMENT.
+ *  - Supported feature widths: d = 64 or 128 for the forward (any dtype);
+ *    d = 64 with dtype f32 for the backward.  Other combinations return
+ *    OSATTN_ERR_UNSUPPORTED.
+ *  - scale must be finite and > 0 (OSATTN_ERR_UNSUPPORTED otherwise).
+ *  - causal != 0 selects j <= i; without cu_seqlens it needs n_q == n_k.
+ *  - Varlen: cu_seqlens != NULL selects block-diagonal attention over
+ *    num_seqs packed sequences; n_q == n_k == cu_seqlens[num_seqs] tokens and
+ *    cu_seqlens holds num_seqs + 1 non-decreasing int32 values starting at 0
+ *    (cumulative lengths, the flash-attn varlen convention).  max_seqlen must
+ *    be >= every length (it sizes the launch grid).  The contents of
+ *    cu_seqlens live on the device and are NOT checked by the library (the
+ *    Python binding checks them); the kernels clamp them into [0, n_q], so
+ *    malformed values give wrong results but no out-of-bounds access.
+ *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *    default stream) and the call returns without synchronising.  A fault in
+ *    enqueued work surfaces at the caller's next synchronisation.
+ *  - Errors: every entry point returns an osattn_status.  All argument checks
+ *    happen on the host before any HIP call; a failed check enqueues nothing.
+ *    The library never aborts, prints or throws across the ABI.
+ *    osattn_last_error() gives a thread-local text for the last failure.
+ */
+#ifndef OSATTN_H
+#define OSATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum osattn_dtype {
+    OSATTN_F32 = 0,
+    OSATTN_F16 = 1,
+    OSATTN_BF16 = 2
+} osattn_dtype;
+
+typedef enum osattn_status {
+    OSATTN_OK = 0,
+    OSATTN_ERR_INVALID_ARG = 1,  /* null pointer, bad size, bad shape */
+    OSATTN_ERR_UNSUPPORTED = 2,  /* valid request this build does not serve */
+    OSATTN_ERR_ALIGNMENT = 3,    /* pointer or stride not 16-byte aligned */
+    OSATTN_ERR_HIP = 4,          /* the HIP runtime reported an error */
+    OSATTN_ERR_WORKSPACE = 5     /* workspace missing or too small */
+} osattn_status;
+
+/*
+ * Forward pass.  Computes o (f32), m and l as defined above for H heads of
+ * n_q queries against n_k keys of feature width d.
+ *
+ * Rows of o, m, l are written for every query position; each value is
+ * produced by exactly one workgroup (no atomics; results are deterministic).
+ */
+int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d,
+               const void *q, const void *k, const void *v,
+               int64_t q_stride_h, int64_t q_stride_n,
+               int64_t kv_stride_h, int64_t kv_stride_n,
+               float *o, int64_t o_stride_h, int64_t o_stride_n,
+               float *m, float *l,
+               float scale, int causal,
+               const int32_t *cu_seqlens, int num_seqs, int max_seqlen,
+               void *stream);
+
+/*
+ * Bytes of device workspace osattn_bwd needs for this problem (the per-row
+ * D vector and statistics, plus partial gradient sums when the launch splits
+ * a reduction across workgroups).  Returns 0 for unsupported or invalid
+ * requests (osattn_bwd then reports the reason).
+ */
+size_t osattn_bwd_workspace_bytes(int dtype, int H, int64_t n_q, int64_t n_k, int d,
+                                  int causal, const int32_t *cu_seqlens, int num_seqs,
+                                  int max_seqlen);
+
+/*
+ * Backward pass (OCANNL "Module Ir.Online_softmax", third bullet):
+ *   D_i  = sum_d dO_id O_id
+ *   P_ij = exp(s_ij - m_i) / l_i        (recomputed from q, k, m, l)
+ *   dV_j = sum_i P_ij dO_i
+ *   dS_ij = P_ij (<dO_i, v_j> - D_i)
+ *   dQ_i = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i
+ * o, m, l are the forward's outputs for the same q, k, v, scale and mask.
+ * dq uses the q strides, dk and dv the k/v strides; all are written in full.
+ * workspace (device, 256-byte aligned) must hold at least
+ * osattn_bwd_workspace_bytes(...) bytes; its contents on entry are ignored.
+ * No atomics are used: repeated calls give bit-identical gradients.
+ */
+int osattn_bwd(int dtype, int H, int64_t n_q, int64_t n_k, int d,
+               const void *q, const void *k, const void *v,
+               const float *o, const void *d_o,
+               int64_t q_stride_h, int64_t q_stride_n,
+               int64_t kv_stride_h, int64_t kv_stride_n,
+               int64_t o_stride_h, int64_t o_stride_n,
+               const float *m, const float *l,
+               float scale, int causal,
+               const int32_t *cu_seqlens, int num_seqs, int max_seqlen,
+               void *dq, void *dk, void *dv,
+               void *workspace, size_t workspace_bytes,
+               void *stream);
+
+/* Static text for a status code (never NULL). */
+const char *osattn_status_string(int status);
+
+/* Text describing the last failure on the calling thread ("" if none). */
+const char *osattn_last_error(void);
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+int osattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSATTN_H */

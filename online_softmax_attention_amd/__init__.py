@@ -1,0 +1,195 @@
+"""Online-softmax attention on AMD MI355X (gfx950): thin Python binding.
+
+This module only marshals arguments: it checks shapes, allocates outputs with
+torch, and calls the C ABI of libosattn.so (declared in include/osattn.h)
+through ctypes on torch's current HIP stream.  Every step of the attention
+computation runs in the library's HIP kernels; there is no fallback of any
+kind -- if the library is missing, every call raises.
+
+    o, m, l = fwd(q, k, v, scale=None, causal=False, cu_seqlens=None, max_seqlen=None)
+    dq, dk, dv = bwd(q, k, v, o, do, m, l, scale=None, causal=False, ...)
+
+Tensors are (H, N, D) by default (``layout="hnd"``) or (N, H, D)
+(``layout="nhd"``), with the feature dimension contiguous.  o is float32;
+m and l are float32 of shape (H, N_q), m in natural-log units of the scaled
+score.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libosattn.so")
+
+F32, F16, BF16 = 0, 1, 2
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_HIP, ERR_WORKSPACE = range(6)
+EXPORTS = ("osattn_fwd", "osattn_bwd", "osattn_bwd_workspace_bytes", "osattn_status_string",
+           "osattn_last_error", "osattn_version")
+
+_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+_lib = None
+
+
+class OsattnError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__("%s: %s (%s)" % (where, status_string(status), detail))
+        self.status = status
+
+
+def load(path: Optional[str] = None):
+    """Load libosattn.so (built by online_softmax_attention_amd.build)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError("libosattn.so is not built (%s); run online_softmax_attention_amd.build" % p)
+    lib = ctypes.CDLL(p)
+    i32, i64, f32, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+    lib.osattn_fwd.argtypes = [i32, i32, i64, i64, i32, vp, vp, vp, i64, i64, i64, i64,
+                               vp, i64, i64, vp, vp, f32, i32, vp, i32, i32, vp]
+    lib.osattn_fwd.restype = i32
+    lib.osattn_bwd_workspace_bytes.argtypes = [i32, i32, i64, i64, i32, i32, vp, i32, i32]
+    lib.osattn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.osattn_bwd.argtypes = [i32, i32, i64, i64, i32, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                               i64, i64, vp, vp, f32, i32, vp, i32, i32, vp, vp, vp, vp,
+                               ctypes.c_size_t, vp]
+    lib.osattn_bwd.restype = i32
+    lib.osattn_status_string.argtypes = [i32]
+    lib.osattn_status_string.restype = ctypes.c_char_p
+    lib.osattn_last_error.argtypes = []
+    lib.osattn_last_error.restype = ctypes.c_char_p
+    lib.osattn_version.argtypes = []
+    lib.osattn_version.restype = i32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().osattn_status_string(int(status)).decode()
+
+
+def last_error() -> str:
+    return load().osattn_last_error().decode()
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise OsattnError(status, where, last_error())
+
+
+def _hn(t: torch.Tensor, layout: str):
+    """(H, N, D, stride_h, stride_n) of a 3-D tensor in the given layout."""
+    if t.dim() != 3:
+        raise ValueError("expected a 3-D tensor, got shape %s" % (tuple(t.shape),))
+    if layout == "hnd":
+        H, N, D = t.shape
+        sh, sn = t.stride(0), t.stride(1)
+    elif layout == "nhd":
+        N, H, D = t.shape
+        sh, sn = t.stride(1), t.stride(0)
+    else:
+        raise ValueError("layout must be 'hnd' or 'nhd'")
+    if t.stride(2) != 1:
+        raise ValueError("the feature dimension must be contiguous")
+    return H, N, D, sh, sn
+
+
+def _cu_args(cu_seqlens, max_seqlen, n, check):
+    if cu_seqlens is None:
+        return None, 0, 0
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 device tensor")
+    if check or max_seqlen is None:
+        host = cu_seqlens.cpu().tolist()
+        if len(host) < 2 or host[0] != 0 or host[-1] != n:
+            raise ValueError("cu_seqlens must start at 0 and end at the token count %d" % n)
+        lens = [b - a for a, b in zip(host[:-1], host[1:])]
+        if min(lens) < 0:
+            raise ValueError("cu_seqlens must be non-decreasing")
+        longest = max(lens)
+        if max_seqlen is None:
+            max_seqlen = longest
+        elif max_seqlen < longest:
+            raise ValueError("max_seqlen %d is below the longest sequence %d" % (max_seqlen, longest))
+    return cu_seqlens, cu_seqlens.numel() - 1, int(max_seqlen)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
+        causal: bool = False, cu_seqlens: Optional[torch.Tensor] = None,
+        max_seqlen: Optional[int] = None, layout: str = "hnd", check: bool = True,
+        out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """Attention forward on the GPU; returns (o, m, l)."""
+    lib = load()
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype of float32/float16/bfloat16")
+    H, n_q, D, q_sh, q_sn = _hn(q, layout)
+    Hk, n_k, Dk, kv_sh, kv_sn = _hn(k, layout)
+    Hv, n_v, Dv, v_sh, v_sn = _hn(v, layout)
+    if (Hk, Dk) != (H, D) or (Hv, n_v, Dv) != (H, n_k, D) or (v_sh, v_sn) != (kv_sh, kv_sn):
+        raise ValueError("k and v must have the same shape and strides, matching q's H and D")
+    scale = D ** -0.5 if scale is None else float(scale)
+    cu, num_seqs, max_seqlen = _cu_args(cu_seqlens, max_seqlen, n_q, check)
+    if out is None:
+        shape = (H, n_q, D) if layout == "hnd" else (n_q, H, D)
+        o = torch.empty(shape, dtype=torch.float32, device=q.device)
+        m = torch.empty((H, n_q), dtype=torch.float32, device=q.device)
+        l = torch.empty((H, n_q), dtype=torch.float32, device=q.device)
+    else:
+        o, m, l = out
+    _, _, _, o_sh, o_sn = _hn(o, layout)
+    st = lib.osattn_fwd(_DT[q.dtype], H, n_q, n_k, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                        q_sh, q_sn, kv_sh, kv_sn, o.data_ptr(), o_sh, o_sn, m.data_ptr(),
+                        l.data_ptr(), scale, int(bool(causal)),
+                        None if cu is None else cu.data_ptr(), num_seqs, max_seqlen, _stream())
+    _check(st, "osattn_fwd")
+    return o, m, l
+
+
+def bwd_workspace_bytes(dtype: torch.dtype, H: int, n_q: int, n_k: int, D: int,
+                        causal: bool = False, cu_seqlens=None, max_seqlen: int = 0) -> int:
+    num_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    return int(load().osattn_bwd_workspace_bytes(
+        _DT[dtype], H, n_q, n_k, D, int(bool(causal)),
+        None if cu_seqlens is None else cu_seqlens.data_ptr(), num_seqs, int(max_seqlen or 0)))
+
+
+def bwd(q, k, v, o, do, m, l, scale: Optional[float] = None, causal: bool = False,
+        cu_seqlens=None, max_seqlen: Optional[int] = None, layout: str = "hnd",
+        check: bool = True, workspace: Optional[torch.Tensor] = None, out=None):
+    """Attention backward on the GPU; returns (dq, dk, dv) in the input dtype."""
+    lib = load()
+    H, n_q, D, q_sh, q_sn = _hn(q, layout)
+    _, n_k, _, kv_sh, kv_sn = _hn(k, layout)
+    _, _, _, o_sh, o_sn = _hn(o, layout)
+    _, _, _, do_sh, do_sn = _hn(do, layout)
+    if (do_sh, do_sn) != (q_sh, q_sn) or do.dtype != q.dtype:
+        raise ValueError("do must match q's dtype and strides")
+    scale = D ** -0.5 if scale is None else float(scale)
+    cu, num_seqs, max_seqlen = _cu_args(cu_seqlens, max_seqlen, n_q, check)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+    need = lib.osattn_bwd_workspace_bytes(_DT[q.dtype], H, n_q, n_k, D, int(bool(causal)),
+                                          None if cu is None else cu.data_ptr(), num_seqs,
+                                          max_seqlen)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=q.device)
+    st = lib.osattn_bwd(_DT[q.dtype], H, n_q, n_k, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                        o.data_ptr(), do.data_ptr(), q_sh, q_sn, kv_sh, kv_sn, o_sh, o_sn,
+                        m.data_ptr(), l.data_ptr(), scale, int(bool(causal)),
+                        None if cu is None else cu.data_ptr(), num_seqs, max_seqlen,
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                        workspace.numel(), _stream())
+    _check(st, "osattn_bwd")
+    return dq, dk, dv

@@ -1,0 +1,62 @@
+// Launch parameter blocks shared by the host dispatch code and the kernels.
+#pragma once
+
+#include <stdint.h>
+
+namespace osattn {
+
+// Mask kinds.  The relation decides which keys a query row admits.
+enum MaskKind : int {
+    kDense = 0,        // every key
+    kCausal = 1,       // keys j <= i
+    kVarlen = 2,       // keys of the row's own packed sequence
+    kVarlenCausal = 3  // both
+};
+
+struct FwdParams {
+    const void *q, *k, *v;
+    float *o, *m, *l;
+    int64_t q_sh, q_sn;    // element strides of q
+    int64_t kv_sh, kv_sn;  // element strides of k and v
+    int64_t o_sh, o_sn;    // element strides of o
+    int H;
+    int n_q, n_k;
+    int n_tiles;           // query tiles per (head, sequence)
+    int num_seqs;          // 1 unless varlen
+    const int32_t *cu;     // device cumulative lengths (varlen) or null
+    float scale;           // softmax scale
+    float scale_log2;      // scale * log2(e)
+};
+
+struct BwdParams {
+    const void *q, *k, *v, *d_o;
+    const float *o, *m, *l;
+    void *dq, *dk, *dv;
+    int64_t q_sh, q_sn;
+    int64_t kv_sh, kv_sn;
+    int64_t o_sh, o_sn;
+    int H;
+    int n_q, n_k;
+    int num_seqs;
+    const int32_t *cu;
+    float scale, scale_log2;
+    // workspace views
+    float *stat_delta;     // (H, n_q): D_i = <dO_i, O_i>
+    float *stat_mlog2;     // (H, n_q): m_i * log2(e)
+    float *stat_linv;      // (H, n_q): 1 / l_i
+    float *dq_part;        // (q_splits, H, n_q, D) when q_splits > 1
+    float *dk_part;        // (k_splits, H, n_k, D) when k_splits > 1
+    float *dv_part;
+    int q_tiles, k_tiles;  // tiles per (head, sequence) for the dQ / dKdV kernels
+    int q_splits;          // key-range splits of the dQ reduction
+    int k_splits;          // query-range splits of the dK/dV reduction
+};
+
+struct ReduceParams {
+    const float *part;     // (splits, H, n, D) contiguous
+    void *out;             // (H, n, D) with strides out_sh, out_sn
+    int64_t out_sh, out_sn;
+    int H, n, splits;
+};
+
+}  // namespace osattn

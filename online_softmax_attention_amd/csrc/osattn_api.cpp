@@ -1,0 +1,247 @@
+// C ABI of the attention library: host-side argument checks, the backward's
+// workspace plan, and dispatch to the HIP kernels.  Declared in osattn.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/osattn.h"
+#include "attn_params.h"
+
+namespace osattn {
+hipError_t launch_forward(int dtype, int d, int mask, FwdParams p, int max_seqlen, hipStream_t st);
+hipError_t launch_backward(int mask, BwdParams p, int seqs, hipStream_t st);
+}  // namespace osattn
+
+using namespace osattn;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return OSATTN_OK;
+}
+
+size_t elem_size(int dtype) { return dtype == OSATTN_F32 ? 4 : 2; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxLen = (int64_t)1 << 30;
+
+// Checks shared by the forward and the backward.  Returns OSATTN_OK or an
+// error status with g_err set.
+int check_common(int dtype, int H, int64_t n_q, int64_t n_k, int d, float scale, int causal,
+                 const int32_t *cu, int num_seqs, int max_seqlen) {
+    if (dtype != OSATTN_F32 && dtype != OSATTN_F16 && dtype != OSATTN_BF16)
+        return fail(OSATTN_ERR_INVALID_ARG, "dtype %d is not OSATTN_F32/F16/BF16", dtype);
+    if (H <= 0) return fail(OSATTN_ERR_INVALID_ARG, "H must be positive (got %d)", H);
+    if (n_q <= 0 || n_k <= 0)
+        return fail(OSATTN_ERR_INVALID_ARG, "n_q and n_k must be positive (got %lld, %lld)",
+                    (long long)n_q, (long long)n_k);
+    if (n_q > kMaxLen || n_k > kMaxLen)
+        return fail(OSATTN_ERR_UNSUPPORTED, "n_q and n_k must be <= 2^30");
+    if (d <= 0) return fail(OSATTN_ERR_INVALID_ARG, "d must be positive (got %d)", d);
+    if (!std::isfinite(scale)) return fail(OSATTN_ERR_UNSUPPORTED, "scale must be finite");
+    if (!(scale > 0.f)) return fail(OSATTN_ERR_UNSUPPORTED, "scale must be > 0");
+    if (cu) {
+        if (num_seqs <= 0) return fail(OSATTN_ERR_INVALID_ARG, "num_seqs must be positive with cu_seqlens");
+        if (n_q != n_k) return fail(OSATTN_ERR_INVALID_ARG, "varlen needs n_q == n_k (total tokens)");
+        if (max_seqlen <= 0 || max_seqlen > n_q)
+            return fail(OSATTN_ERR_INVALID_ARG, "max_seqlen must be in [1, n_q] (got %d)", max_seqlen);
+    } else if (causal && n_q != n_k) {
+        return fail(OSATTN_ERR_INVALID_ARG, "causal attention needs n_q == n_k (got %lld, %lld)",
+                    (long long)n_q, (long long)n_k);
+    }
+    return OSATTN_OK;
+}
+
+int check_tensor(const char *name, const void *p, int64_t sh, int64_t sn, size_t esize) {
+    if (!p) return fail(OSATTN_ERR_INVALID_ARG, "%s is NULL", name);
+    if (sh < 0 || sn < 0) return fail(OSATTN_ERR_INVALID_ARG, "%s has a negative stride", name);
+    if (!aligned16(p)) return fail(OSATTN_ERR_ALIGNMENT, "%s is not 16-byte aligned", name);
+    const int64_t q = 16 / (int64_t)esize;
+    if (sh % q || sn % q)
+        return fail(OSATTN_ERR_ALIGNMENT, "%s strides (%lld, %lld) are not multiples of %lld elements",
+                    name, (long long)sh, (long long)sn, (long long)q);
+    return OSATTN_OK;
+}
+
+int mask_kind(int causal, const int32_t *cu) {
+    if (cu) return causal ? kVarlenCausal : kVarlen;
+    return causal ? kCausal : kDense;
+}
+
+// ---------------------------------------------------------------- bwd plan
+struct BwdPlan {
+    int q_tiles, k_tiles, q_splits, k_splits, seqs;
+    size_t off_delta, off_mlog2, off_linv, off_dq, off_dk, off_dv, total;
+};
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int clampi(int64_t x, int lo, int hi) { return (int)(x < lo ? lo : (x > hi ? hi : x)); }
+
+BwdPlan plan_backward(int H, int64_t n_q, int64_t n_k, int d, const int32_t *cu, int num_seqs,
+                      int max_seqlen) {
+    BwdPlan pl{};
+    const bool varlen = cu != nullptr;
+    pl.seqs = varlen ? num_seqs : 1;
+    const int64_t qlen = varlen ? max_seqlen : n_q;
+    const int64_t klen = varlen ? max_seqlen : n_k;
+    pl.q_tiles = (int)((qlen + 127) / 128);
+    pl.k_tiles = (int)((klen + 127) / 128);
+    // Aim for ~512 workgroups (two per CU) per pass; a split keeps at least
+    // 256 positions of the reduced axis.
+    const int64_t target = 512;
+    const int64_t base_k = (int64_t)H * pl.seqs * pl.k_tiles;
+    const int64_t base_q = (int64_t)H * pl.seqs * pl.q_tiles;
+    pl.k_splits = varlen ? 1 : clampi((target + base_k - 1) / base_k, 1, clampi(n_q / 256, 1, 16));
+    pl.q_splits = varlen ? 1 : clampi((target + base_q - 1) / base_q, 1, clampi(n_k / 256, 1, 16));
+    size_t off = 0;
+    const size_t rowbytes = round256((size_t)H * n_q * sizeof(float));
+    pl.off_delta = off; off += rowbytes;
+    pl.off_mlog2 = off; off += rowbytes;
+    pl.off_linv = off;  off += rowbytes;
+    pl.off_dq = off;
+    if (pl.q_splits > 1) off += round256((size_t)pl.q_splits * H * n_q * d * sizeof(float));
+    pl.off_dk = off;
+    if (pl.k_splits > 1) off += round256((size_t)pl.k_splits * H * n_k * d * sizeof(float));
+    pl.off_dv = off;
+    if (pl.k_splits > 1) off += round256((size_t)pl.k_splits * H * n_k * d * sizeof(float));
+    pl.total = off;
+    return pl;
+}
+
+int check_bwd_supported(int dtype, int d) {
+    if (dtype != OSATTN_F32 || d != 64)
+        return fail(OSATTN_ERR_UNSUPPORTED,
+                    "backward supports dtype OSATTN_F32 with d = 64 (got dtype %d, d %d)", dtype, d);
+    return OSATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int osattn_version(void) { return 100; }
+
+const char *osattn_status_string(int status) {
+    switch (status) {
+        case OSATTN_OK: return "OSATTN_OK";
+        case OSATTN_ERR_INVALID_ARG: return "OSATTN_ERR_INVALID_ARG: invalid argument";
+        case OSATTN_ERR_UNSUPPORTED: return "OSATTN_ERR_UNSUPPORTED: unsupported combination";
+        case OSATTN_ERR_ALIGNMENT: return "OSATTN_ERR_ALIGNMENT: pointer or stride not 16-byte aligned";
+        case OSATTN_ERR_HIP: return "OSATTN_ERR_HIP: HIP runtime error";
+        case OSATTN_ERR_WORKSPACE: return "OSATTN_ERR_WORKSPACE: workspace missing or too small";
+        default: return "unknown osattn status";
+    }
+}
+
+const char *osattn_last_error(void) { return g_err; }
+
+int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q, const void *k,
+               const void *v, int64_t q_stride_h, int64_t q_stride_n, int64_t kv_stride_h,
+               int64_t kv_stride_n, float *o, int64_t o_stride_h, int64_t o_stride_n, float *m,
+               float *l, float scale, int causal, const int32_t *cu_seqlens, int num_seqs,
+               int max_seqlen, void *stream) {
+    int st = check_common(dtype, H, n_q, n_k, d, scale, causal, cu_seqlens, num_seqs, max_seqlen);
+    if (st) return st;
+    if (d != 64 && d != 128)
+        return fail(OSATTN_ERR_UNSUPPORTED, "forward supports d = 64 or 128 (got %d)", d);
+    const size_t es = elem_size(dtype);
+    if ((st = check_tensor("q", q, q_stride_h, q_stride_n, es))) return st;
+    if ((st = check_tensor("k", k, kv_stride_h, kv_stride_n, es))) return st;
+    if ((st = check_tensor("v", v, kv_stride_h, kv_stride_n, es))) return st;
+    if ((st = check_tensor("o", o, o_stride_h, o_stride_n, 4))) return st;
+    if (!m || !l) return fail(OSATTN_ERR_INVALID_ARG, "m and l must not be NULL");
+
+    FwdParams p{};
+    p.q = q; p.k = k; p.v = v;
+    p.o = o; p.m = m; p.l = l;
+    p.q_sh = q_stride_h; p.q_sn = q_stride_n;
+    p.kv_sh = kv_stride_h; p.kv_sn = kv_stride_n;
+    p.o_sh = o_stride_h; p.o_sn = o_stride_n;
+    p.H = H; p.n_q = (int)n_q; p.n_k = (int)n_k;
+    p.num_seqs = cu_seqlens ? num_seqs : 1;
+    p.cu = cu_seqlens;
+    p.scale = scale;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    const hipError_t e = launch_forward(dtype, d, mask_kind(causal, cu_seqlens), p, max_seqlen,
+                                        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(OSATTN_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t osattn_bwd_workspace_bytes(int dtype, int H, int64_t n_q, int64_t n_k, int d, int causal,
+                                  const int32_t *cu_seqlens, int num_seqs, int max_seqlen) {
+    if (check_common(dtype, H, n_q, n_k, d, 1.f, causal, cu_seqlens, num_seqs, max_seqlen)) return 0;
+    if (check_bwd_supported(dtype, d)) return 0;
+    return plan_backward(H, n_q, n_k, d, cu_seqlens, num_seqs, max_seqlen).total;
+}
+
+int osattn_bwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q, const void *k,
+               const void *v, const float *o, const void *d_o, int64_t q_stride_h,
+               int64_t q_stride_n, int64_t kv_stride_h, int64_t kv_stride_n, int64_t o_stride_h,
+               int64_t o_stride_n, const float *m, const float *l, float scale, int causal,
+               const int32_t *cu_seqlens, int num_seqs, int max_seqlen, void *dq, void *dk, void *dv,
+               void *workspace, size_t workspace_bytes, void *stream) {
+    int st = check_common(dtype, H, n_q, n_k, d, scale, causal, cu_seqlens, num_seqs, max_seqlen);
+    if (st) return st;
+    if ((st = check_bwd_supported(dtype, d))) return st;
+    const size_t es = elem_size(dtype);
+    if ((st = check_tensor("q", q, q_stride_h, q_stride_n, es))) return st;
+    if ((st = check_tensor("k", k, kv_stride_h, kv_stride_n, es))) return st;
+    if ((st = check_tensor("v", v, kv_stride_h, kv_stride_n, es))) return st;
+    if ((st = check_tensor("d_o", d_o, q_stride_h, q_stride_n, es))) return st;
+    if ((st = check_tensor("o", o, o_stride_h, o_stride_n, 4))) return st;
+    if ((st = check_tensor("dq", dq, q_stride_h, q_stride_n, es))) return st;
+    if ((st = check_tensor("dk", dk, kv_stride_h, kv_stride_n, es))) return st;
+    if ((st = check_tensor("dv", dv, kv_stride_h, kv_stride_n, es))) return st;
+    if (!m || !l) return fail(OSATTN_ERR_INVALID_ARG, "m and l must not be NULL");
+    const BwdPlan pl = plan_backward(H, n_q, n_k, d, cu_seqlens, num_seqs, max_seqlen);
+    if (!workspace) return fail(OSATTN_ERR_WORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(OSATTN_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
+    if (workspace_bytes < pl.total)
+        return fail(OSATTN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, pl.total);
+
+    char *ws = static_cast<char *>(workspace);
+    BwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.d_o = d_o;
+    p.o = o; p.m = m; p.l = l;
+    p.dq = dq; p.dk = dk; p.dv = dv;
+    p.q_sh = q_stride_h; p.q_sn = q_stride_n;
+    p.kv_sh = kv_stride_h; p.kv_sn = kv_stride_n;
+    p.o_sh = o_stride_h; p.o_sn = o_stride_n;
+    p.H = H; p.n_q = (int)n_q; p.n_k = (int)n_k;
+    p.num_seqs = cu_seqlens ? num_seqs : 1;
+    p.cu = cu_seqlens;
+    p.scale = scale;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.stat_delta = reinterpret_cast<float *>(ws + pl.off_delta);
+    p.stat_mlog2 = reinterpret_cast<float *>(ws + pl.off_mlog2);
+    p.stat_linv = reinterpret_cast<float *>(ws + pl.off_linv);
+    p.dq_part = reinterpret_cast<float *>(ws + pl.off_dq);
+    p.dk_part = reinterpret_cast<float *>(ws + pl.off_dk);
+    p.dv_part = reinterpret_cast<float *>(ws + pl.off_dv);
+    p.q_tiles = pl.q_tiles; p.k_tiles = pl.k_tiles;
+    p.q_splits = pl.q_splits; p.k_splits = pl.k_splits;
+    const hipError_t e = launch_backward(mask_kind(causal, cu_seqlens), p, pl.seqs,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(OSATTN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

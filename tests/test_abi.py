@@ -1,0 +1,132 @@
+"""C-ABI boundary tests that need no GPU.
+
+The library must load, export every function include/osattn.h declares, and
+reject invalid arguments on the host -- before any HIP call -- with the
+documented status codes.  Pointers handed to rejected calls are fake values
+that must never be dereferenced; every case below fails a host check first.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import online_softmax_attention_amd as osa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "osattn.h")
+F32, F16, BF16 = osa.F32, osa.F16, osa.BF16
+
+# Fake, 256-byte aligned addresses; never dereferenced (every call fails first).
+A = 0x7F0000000000
+B, C, O, M, L = A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000, A + 0x500000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(osa.LIB_PATH):
+        import online_softmax_attention_amd.build as b
+        b.build()
+    return osa.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(osattn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(osa.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert osa.status_string(s).startswith("OSATTN_")
+    assert "unknown" in osa.status_string(99)
+    assert lib.osattn_version() >= 100
+
+
+# m defaults to NULL so that no combination of the other arguments can pass every
+# host check and reach a launch with the fake pointers.
+def fwd(lib, dtype=F16, H=2, n_q=128, n_k=128, d=64, q=A, k=B, v=C, qs=(128 * 64, 64),
+        kvs=(128 * 64, 64), o=O, os_=(128 * 64, 64), m=None, l=L, scale=0.125, causal=0,
+        cu=None, num_seqs=0, max_seqlen=0):
+    return lib.osattn_fwd(dtype, H, n_q, n_k, d, q, k, v, qs[0], qs[1], kvs[0], kvs[1], o,
+                          os_[0], os_[1], m, l, scale, causal, cu, num_seqs, max_seqlen, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), osa.ERR_INVALID_ARG),
+    (dict(H=0), osa.ERR_INVALID_ARG),
+    (dict(n_q=0), osa.ERR_INVALID_ARG),
+    (dict(n_k=0), osa.ERR_INVALID_ARG),
+    (dict(d=96), osa.ERR_UNSUPPORTED),
+    (dict(d=0), osa.ERR_INVALID_ARG),
+    (dict(scale=float("nan")), osa.ERR_UNSUPPORTED),
+    (dict(scale=float("inf")), osa.ERR_UNSUPPORTED),
+    (dict(scale=-1.0), osa.ERR_UNSUPPORTED),
+    (dict(q=None), osa.ERR_INVALID_ARG),
+    (dict(k=None), osa.ERR_INVALID_ARG),
+    (dict(v=None), osa.ERR_INVALID_ARG),
+    (dict(o=None), osa.ERR_INVALID_ARG),
+    (dict(m=M, l=None), osa.ERR_INVALID_ARG),
+    (dict(q=A + 8), osa.ERR_ALIGNMENT),
+    (dict(o=O + 4), osa.ERR_ALIGNMENT),
+    (dict(qs=(128 * 64, 60)), osa.ERR_ALIGNMENT),
+    (dict(kvs=(-64, 64)), osa.ERR_INVALID_ARG),
+    (dict(os_=(128 * 64, 66)), osa.ERR_ALIGNMENT),
+    (dict(causal=1, n_k=100), osa.ERR_INVALID_ARG),
+    (dict(cu=A, num_seqs=0, max_seqlen=10), osa.ERR_INVALID_ARG),
+    (dict(cu=A, num_seqs=2, max_seqlen=0), osa.ERR_INVALID_ARG),
+    (dict(cu=A, num_seqs=2, max_seqlen=200), osa.ERR_INVALID_ARG),
+    (dict(cu=A, num_seqs=2, max_seqlen=64, n_k=100), osa.ERR_INVALID_ARG),
+    (dict(n_q=(1 << 30) + 1, n_k=(1 << 30) + 1), osa.ERR_UNSUPPORTED),
+])
+def test_fwd_rejects_on_host(lib, kw, status):
+    assert fwd(lib, **kw) == status
+    assert osa.last_error() != ""
+
+
+def test_fwd_stride_units_follow_dtype(lib):
+    # f32 strides must be multiples of 4 elements, 16-bit strides of 8.
+    assert fwd(lib, dtype=F32, qs=(128 * 64, 66)) == osa.ERR_ALIGNMENT
+    assert fwd(lib, dtype=F16, qs=(128 * 64, 68)) == osa.ERR_ALIGNMENT
+    assert fwd(lib, dtype=F32, qs=(128 * 64, 68)) == osa.ERR_INVALID_ARG  # reaches m == NULL
+
+
+# The workspace defaults to NULL so no case can pass every host check.
+def bwd(lib, dtype=F32, H=1, n_q=256, n_k=128, d=64, ptrs=None, ws=None, ws_bytes=1 << 30,
+        causal=0, scale=0.125):
+    p = dict(q=A, k=B, v=C, o=O, do=A + 0x600000, m=M, l=L, dq=A + 0x700000,
+             dk=A + 0x800000, dv=A + 0x900000)
+    p.update(ptrs or {})
+    return lib.osattn_bwd(dtype, H, n_q, n_k, d, p["q"], p["k"], p["v"], p["o"], p["do"],
+                          n_q * d, d, n_k * d, d, n_q * d, d, p["m"], p["l"], scale, causal,
+                          None, 0, 0, p["dq"], p["dk"], p["dv"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=F16), osa.ERR_UNSUPPORTED),
+    (dict(d=128), osa.ERR_UNSUPPORTED),
+    (dict(ws=None), osa.ERR_WORKSPACE),
+    (dict(ws=A, ws_bytes=16), osa.ERR_WORKSPACE),
+    (dict(ws=A + 16), osa.ERR_ALIGNMENT),
+    (dict(ptrs={"do": None}), osa.ERR_INVALID_ARG),
+    (dict(ptrs={"dk": None}), osa.ERR_INVALID_ARG),
+    (dict(ptrs={"dq": A + 4}), osa.ERR_ALIGNMENT),
+    (dict(causal=1), osa.ERR_INVALID_ARG),
+])
+def test_bwd_rejects_on_host(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+def test_bwd_workspace_bytes(lib):
+    n = lib.osattn_bwd_workspace_bytes(F32, 1, 8192, 2048, 64, 0, None, 0, 0)
+    assert n >= 3 * 8192 * 4 and n % 256 == 0
+    assert lib.osattn_bwd_workspace_bytes(F16, 1, 8192, 2048, 64, 0, None, 0, 0) == 0
+    assert lib.osattn_bwd_workspace_bytes(F32, 1, 8192, 2048, 128, 0, None, 0, 0) == 0
+    assert lib.osattn_bwd_workspace_bytes(F32, 0, 8192, 2048, 64, 0, None, 0, 0) == 0

@@ -1,0 +1,228 @@
+"""GPU parity: the HIP path (through the C ABI) against the f64 CPU oracle.
+
+Every case draws seeded inputs (workloads.py), runs the library on the GPU and
+the oracle on the same stored bytes (widened exactly), and compares element by
+element within the stated tolerances (tests/gpu_util.py).  Sizes span several
+128-row query tiles and ragged tails; the full-size workloads compare sampled
+rows, which the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests.gpu_util import (TOL, assert_fwd_close, assert_grad_close, cu_dev, host, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd(osa, inp, causal, cu=None, layout="hnd"):
+    w = inp.w
+    q, k, v = (to_dev(x, w.dtype) for x in (inp.q, inp.k, inp.v))
+    if layout == "nhd":
+        q, k, v = (x.permute(1, 0, 2).contiguous() for x in (q, k, v))
+    o, m, l = osa.fwd(q, k, v, scale=w.softmax_scale, causal=causal, cu_seqlens=cu_dev(cu),
+                      layout=layout)
+    torch.cuda.synchronize()
+    o = host(o)
+    if layout == "nhd":
+        o = o.transpose(1, 0, 2)
+    return o, host(m), host(l)
+
+
+def small(name, H, n_q, n_k, D, dtype, causal, seed, lengths=None, backward=False):
+    return W.Workload(name, H, n_q, n_k, D, dtype, causal, seed, backward=backward,
+                      lengths=lengths)
+
+
+# ------------------------------------------------------------ named workloads
+def test_workload_dense_n128_f32_full(osattn, oracle):
+    inp = W.make_inputs(W.WORKLOADS["dense_n128_h1_d64_f32"])
+    o, m, l = run_fwd(osattn, inp, causal=False)
+    ro, rm, rl = oracle.attn_fwd(inp.q32, inp.k32, inp.v32, inp.w.softmax_scale)
+    assert_fwd_close(o, m, l, ro, rm, rl, "f32", "dense N=128 f32")
+
+
+def test_workload_dense_n1024_f16_full(osattn, oracle):
+    inp = W.make_inputs(W.WORKLOADS["dense_n1024_h4_d64_f16"])
+    o, m, l = run_fwd(osattn, inp, causal=False)
+    ro, rm, rl = oracle.attn_fwd(inp.q32, inp.k32, inp.v32, inp.w.softmax_scale)
+    assert_fwd_close(o, m, l, ro, rm, rl, "f16", "dense N=1024 H=4 f16")
+
+
+def sample_rows(H, n, extra=(), count=48, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for h in range(H):
+        for i in list(extra) + [0, 1, 127, 128, 129, n - 1] + list(rng.integers(0, n, 8)):
+            if 0 <= i < n:
+                rows.add(h * n + int(i))
+    rows = sorted(rows)
+    if len(rows) > count * H:
+        keep = rng.choice(len(rows), count * H, replace=False)
+        rows = sorted(rows[i] for i in keep)
+    return np.array(rows, dtype=np.int64)
+
+
+def check_sampled(o, m, l, inp, causal, rows, dtype, what):
+    w = inp.w
+    ro, rm, rl = oracle_rows(inp, causal, rows)
+    H, n, D = o.shape
+    assert_fwd_close(o.reshape(-1, D)[rows], m.reshape(-1)[rows], l.reshape(-1)[rows],
+                     ro, rm, rl, dtype, what)
+
+
+def oracle_rows(inp, causal, rows):
+    import oracle
+    return oracle.attn_fwd(inp.q32, inp.k32, inp.v32, inp.w.softmax_scale, causal=causal,
+                           cu_seqlens=inp.cu_seqlens, rows=rows)
+
+
+def test_workload_causal_n4096_bf16_sampled(osattn):
+    inp = W.make_inputs(W.WORKLOADS["causal_n4096_h16_d128_bf16"])
+    o, m, l = run_fwd(osattn, inp, causal=True)
+    rows = sample_rows(16, 4096, extra=(255, 256, 2047, 2048, 4095), count=12)
+    check_sampled(o, m, l, inp, True, rows, "bf16", "causal N=4096 H=16 D=128 bf16")
+
+
+def test_workload_varlen_16k_f16_sampled(osattn):
+    w = W.WORKLOADS["varlen_causal_16k_h8_d64_f16"]
+    inp = W.make_inputs(w)
+    o, m, l = run_fwd(osattn, inp, causal=True, cu=inp.cu_seqlens)
+    cu = inp.cu_seqlens
+    edges = sorted(set(int(x) for x in cu[:-1]) | set(int(x) - 1 for x in cu[1:]))
+    rows = sample_rows(w.H, w.n_q, extra=edges, count=40)
+    check_sampled(o, m, l, inp, True, rows, "f16", "varlen causal 16k f16")
+
+
+def test_workload_rect_f32_fwd_bwd_full(osattn, oracle):
+    w = W.WORKLOADS["rect_sq8192_sk2048_h1_d64_f32_fwdbwd"]
+    inp = W.make_inputs(w)
+    q, k, v, do = (to_dev(x, "f32") for x in (inp.q, inp.k, inp.v, inp.do))
+    o, m, l = osattn.fwd(q, k, v, scale=w.softmax_scale)
+    dq, dk, dv = osattn.bwd(q, k, v, o, do, m, l, scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attn_fwd(inp.q32, inp.k32, inp.v32, w.softmax_scale)
+    assert_fwd_close(host(o), host(m), host(l), ro, rm, rl, "f32", "rect f32 fwd")
+    rdq, rdk, rdv, *_ = oracle.attn_bwd(inp.q32, inp.k32, inp.v32, inp.do32, w.softmax_scale)
+    for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        assert_grad_close(host(g), r, "f32", name)
+
+
+# -------------------------------------------------- reduced, full comparison
+FWD_CASES = [
+    # (dtype, D, causal, n_q, n_k, H)
+    ("f16", 64, False, 300, 300, 2), ("f16", 64, True, 300, 300, 2),
+    ("f16", 128, False, 257, 190, 2), ("f16", 128, True, 384, 384, 1),
+    ("bf16", 64, False, 129, 513, 2), ("bf16", 128, True, 700, 700, 2),
+    ("bf16", 64, True, 33, 33, 3), ("f32", 64, False, 1, 1, 1), ("f32", 64, True, 1, 1, 2),
+    ("f32", 64, False, 127, 200, 2), ("f32", 64, True, 255, 255, 1),
+    ("f32", 128, False, 129, 77, 1), ("f32", 128, True, 300, 300, 1),
+    ("f16", 64, False, 128, 1, 1), ("f16", 128, False, 5, 1000, 2),
+]
+
+
+@pytest.mark.parametrize("dtype,D,causal,n_q,n_k,H", FWD_CASES)
+def test_fwd_parity_small(osattn, oracle, dtype, D, causal, n_q, n_k, H):
+    inp = W.make_inputs(small("c", H, n_q, n_k, D, dtype, causal, 1000 + n_q + D))
+    o, m, l = run_fwd(osattn, inp, causal)
+    ro, rm, rl = oracle.attn_fwd(inp.q32, inp.k32, inp.v32, inp.w.softmax_scale, causal=causal)
+    assert_fwd_close(o, m, l, ro, rm, rl, dtype, "%s D=%d causal=%s %dx%d" % (dtype, D, causal, n_q, n_k))
+
+
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128), ("f32", 64), ("f16", 128)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_parity(osattn, oracle, dtype, D, causal):
+    lengths = [384, 1, 96, 640, 57, 0, 129, 128]  # includes the page's example lengths
+    n = sum(lengths)
+    inp = W.make_inputs(small("v", 3, n, n, D, dtype, causal, 20260821, lengths=lengths))
+    o, m, l = run_fwd(osattn, inp, causal, cu=inp.cu_seqlens)
+    ro, rm, rl = oracle.attn_fwd(inp.q32, inp.k32, inp.v32, inp.w.softmax_scale, causal=causal,
+                                 cu_seqlens=inp.cu_seqlens)
+    assert_fwd_close(o, m, l, ro, rm, rl, dtype, "varlen %s D=%d causal=%s" % (dtype, D, causal))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_nhd_layout(osattn, oracle, dtype):
+    inp = W.make_inputs(small("nhd", 3, 200, 200, 64, dtype, True, 77))
+    o, m, l = run_fwd(osattn, inp, True, layout="nhd")
+    ro, rm, rl = oracle.attn_fwd(inp.q32, inp.k32, inp.v32, inp.w.softmax_scale, causal=True)
+    assert_fwd_close(o, m, l, ro, rm, rl, dtype, "nhd layout")
+
+
+# ------------------------------------------------- pins on the GPU path
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128), ("f32", 64)])
+def test_gpu_zero_query_is_mean_of_values(osattn, dtype, D):
+    inp = W.make_inputs(small("z", 2, 300, 300, D, dtype, False, 5))
+    inp.q[...] = 0
+    o, m, l = run_fwd(osattn, inp, causal=False)
+    np.testing.assert_allclose(o, np.broadcast_to(inp.v32.astype(np.float64).mean(1, keepdims=True), o.shape),
+                               atol=TOL[dtype])
+    np.testing.assert_array_equal(m, 0.0)
+    np.testing.assert_allclose(l, 300.0, rtol=1e-6)
+    oc, mc, lc = run_fwd(osattn, inp, causal=True)
+    prefix = np.cumsum(inp.v32.astype(np.float64), axis=1) / np.arange(1, 301)[None, :, None]
+    np.testing.assert_allclose(oc, prefix, atol=TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)])
+def test_gpu_first_rows_return_their_value_exactly(osattn, dtype, D):
+    inp = W.make_inputs(small("r0", 2, 260, 260, D, dtype, True, 6))
+    o, m, l = run_fwd(osattn, inp, causal=True)
+    np.testing.assert_array_equal(o[:, 0], inp.v32[:, 0])
+    np.testing.assert_array_equal(l[:, 0], 1.0)
+    lengths = [5, 1, 200, 54]
+    cu = W.cu_from_lengths(lengths)
+    o, m, l = run_fwd(osattn, inp, causal=True, cu=cu)
+    for b in range(len(lengths)):
+        np.testing.assert_array_equal(o[:, cu[b]], inp.v32[:, cu[b]])
+
+
+def test_gpu_deterministic(osattn):
+    inp = W.make_inputs(small("det", 4, 1000, 1000, 128, "bf16", True, 8))
+    a = run_fwd(osattn, inp, causal=True)
+    b = run_fwd(osattn, inp, causal=True)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_gpu_masked_tail_keys_do_not_leak(osattn):
+    """Huge keys/values past a sequence end must not change earlier rows."""
+    inp = W.make_inputs(small("t", 2, 200, 200, 64, "f16", True, 9))
+    cu = W.cu_from_lengths([130, 70])
+    o1, _, _ = run_fwd(osattn, inp, causal=False, cu=cu)
+    inp.k[:, 130:] = np.float16(60.0)
+    inp.v[:, 130:] = np.float16(6e4)
+    o2, _, _ = run_fwd(osattn, inp, causal=False, cu=cu)
+    np.testing.assert_array_equal(o1[:, :130], o2[:, :130])
+
+
+# ---------------------------------------------------------------- backward
+BWD_CASES = [
+    # (causal, n_q, n_k, H, lengths)
+    (False, 300, 200, 2, None), (True, 300, 300, 2, None), (False, 1, 1, 1, None),
+    (True, 129, 129, 1, None), (False, 1000, 77, 1, None),
+    (True, 0, 0, 2, [384, 1, 96, 640, 57]), (False, 0, 0, 2, [130, 0, 7, 300]),
+]
+
+
+@pytest.mark.parametrize("causal,n_q,n_k,H,lengths", BWD_CASES)
+def test_bwd_parity_f32(osattn, oracle, causal, n_q, n_k, H, lengths):
+    if lengths is not None:
+        n_q = n_k = sum(lengths)
+    w = small("b", H, n_q, n_k, 64, "f32", causal, 3000 + n_q, lengths=lengths, backward=True)
+    inp = W.make_inputs(w)
+    q, k, v, do = (to_dev(x, "f32") for x in (inp.q, inp.k, inp.v, inp.do))
+    cu = cu_dev(inp.cu_seqlens)
+    o, m, l = osattn.fwd(q, k, v, scale=w.softmax_scale, causal=causal, cu_seqlens=cu)
+    dq, dk, dv = osattn.bwd(q, k, v, o, do, m, l, scale=w.softmax_scale, causal=causal,
+                            cu_seqlens=cu)
+    dq2, dk2, dv2 = osattn.bwd(q, k, v, o, do, m, l, scale=w.softmax_scale, causal=causal,
+                               cu_seqlens=cu)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, *_ = oracle.attn_bwd(inp.q32, inp.k32, inp.v32, inp.do32, w.softmax_scale,
+                                        causal=causal, cu_seqlens=inp.cu_seqlens)
+    for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        assert_grad_close(host(g), r, "f32", name)
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):  # no atomics: bit-identical reruns
+        assert torch.equal(a, b)
