@@ -246,6 +246,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--all", action="store_true", help="one JSON line per workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run 10 plain device copies of BYTES bytes (calibrates the "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters against a known size)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -261,6 +264,15 @@ def main():
     if not torch.cuda.is_available():
         sys.stderr.write("bench.py needs a GPU\n")
         sys.exit(1)
+    if args.copy_probe:
+        n = args.copy_probe // 4
+        src = torch.arange(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n * 4, "copies": 10}), flush=True)
+        return
     osa.load()
     names = W.ORDER if args.all else [args.workload]
     for name in names:

@@ -165,17 +165,24 @@ def test_gpu_zero_query_is_mean_of_values(osattn, dtype, D):
     np.testing.assert_allclose(oc, prefix, atol=TOL[dtype])
 
 
+# A row that admits one key returns that key's value.  The kernel forms the
+# exponent as fma(s, c, -m c) with c = scale log2(e); for s = m that is the
+# rounding residue of m c (|.| <= 2^-24 |m c|), not 0, so p = l = 1 + O(2^-24)
+# and O = v (1 + O(2^-23)): equal to v up to a few f32 ulps.
+FIRST_ROW_RTOL = 5e-7
+
+
 @pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)])
-def test_gpu_first_rows_return_their_value_exactly(osattn, dtype, D):
+def test_gpu_first_rows_return_their_value(osattn, dtype, D):
     inp = W.make_inputs(small("r0", 2, 260, 260, D, dtype, True, 6))
     o, m, l = run_fwd(osattn, inp, causal=True)
-    np.testing.assert_array_equal(o[:, 0], inp.v32[:, 0])
-    np.testing.assert_array_equal(l[:, 0], 1.0)
+    np.testing.assert_allclose(o[:, 0], inp.v32[:, 0], rtol=FIRST_ROW_RTOL, atol=0)
+    np.testing.assert_allclose(l[:, 0], 1.0, rtol=FIRST_ROW_RTOL)
     lengths = [5, 1, 200, 54]
     cu = W.cu_from_lengths(lengths)
     o, m, l = run_fwd(osattn, inp, causal=True, cu=cu)
     for b in range(len(lengths)):
-        np.testing.assert_array_equal(o[:, cu[b]], inp.v32[:, cu[b]])
+        np.testing.assert_allclose(o[:, cu[b]], inp.v32[:, cu[b]], rtol=FIRST_ROW_RTOL, atol=0)
 
 
 def test_gpu_deterministic(osattn):
