@@ -40,6 +40,8 @@
  *  - Alignment: q, k, v, d_o, dq, dk, dv, o must be 16-byte aligned and their
  *    strides multiples of 16 bytes' worth of elements (8 for f16/bf16, 4 for
  *    f32); otherwise OSATTN_ERR_ALIGNMENT.
+ *  - Row strides: stride_n * element size must be <= 4 MiB for q and k/v
+ *    (OSATTN_ERR_UNSUPPORTED otherwise).
  *  - Supported feature widths: d = 64 or 128 for the forward (any dtype);
  *    d = 64 with dtype f32 for the backward.  Other combinations return
  *    OSATTN_ERR_UNSUPPORTED.

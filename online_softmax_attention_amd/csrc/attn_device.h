@@ -68,13 +68,82 @@ __device__ __forceinline__ u32x4 load16(const void *p, bool ok) {
 
 // Row-major LDS tile of 16-byte chunks with an XOR swizzle: chunk c of row r
 // lives at chunk c ^ (r & 7).  Eight consecutive rows read at the same logical
-// chunk then hit eight different bank groups.
+// chunk then hit eight different bank groups.  (Used by the f32 kernels.)
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
-// Transposed V tile (16-bit types): row = feature d, columns = key slots.
-// Eight consecutive d rows map a logical chunk to eight distinct physical
-// chunks, and so do rows d, d + 8, ..., d + 56 (the writer's pattern).
-__device__ __forceinline__ int swz_t(int d, int chunk) { return chunk ^ ((d ^ (d >> 3)) & 7); }
+// Swizzles of the 16-bit forward tiles for gfx950's 64 x 4-byte LDS banks, where
+// a 16-byte-per-lane access is served 16 lanes at a time and must then touch 16
+// distinct 16-byte bank groups.
+//  - A row of >= 256 bytes spans all banks, so 16 consecutive rows read at one
+//    logical chunk need 16 distinct physical chunks: XOR with (row & 15).
+//  - A 128-byte row covers half the banks and the next row the other half, so
+//    rows of equal parity must differ: XOR with ((row >> 1) & 7).
+template <int ROW_BYTES>
+__device__ __forceinline__ int swz_k(int row, int chunk) {
+    return ROW_BYTES >= 256 ? (chunk ^ (row & 15)) : (chunk ^ ((row >> 1) & 7));
+}
+// Transposed V tile (row = feature d): the readers take 16 consecutive d at one
+// logical chunk, the writers rows d = 8 d8 + x for 16 values of d8.
+// (d ^ (d >> 3)) & 15 is a permutation on both patterns.
+template <int ROW_BYTES>
+__device__ __forceinline__ int swz_v(int d, int chunk) {
+    return ROW_BYTES >= 256 ? (chunk ^ ((d ^ (d >> 3)) & 15)) : (chunk ^ ((d >> 1) & 7));
+}
+
+// Swizzle of a row-major V tile read by ds_read_b64_tr_b16: 16 lanes read four
+// consecutive key rows x 32 bytes, and a wave half reads those rows x 64 bytes.
+// XOR-ing the chunk index with a per-row quarter (256-byte rows) or half
+// (128-byte rows, whose neighbours sit in the other bank half) puts the four
+// rows' windows on disjoint banks.
+template <int ROW_BYTES>
+__device__ __forceinline__ int swz_vt(int row, int chunk) {
+    return ROW_BYTES >= 256 ? (chunk ^ ((row & 3) << 2)) : (chunk ^ (((row >> 1) & 1) << 2));
+}
+
+#define OSATTN_LDS __attribute__((address_space(3)))
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane 4 r + c names 4 consecutive 16-bit elements of row r (columns
+// 4c .. 4c+3) of a 4 x 16 block; lane j then receives column j of that block,
+// one element per row (verified on the device by a lane-layout probe).
+__device__ __forceinline__ i16x4 lds_read_tr16(const void *lds_addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((OSATTN_LDS i16x4 *)(lds_addr));
+}
+
+// 16 bytes per lane from a raw buffer straight into LDS: lane L writes bytes
+// [lds_base + 16 L, lds_base + 16 L + 16); lds_base must be wave-uniform.
+// Past-the-end chunks arrive as zeros.  Completion is counted by vmcnt.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *lds_base, int byte_off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (OSATTN_LDS void *)(lds_base), 16, byte_off, 0, 0, 0);
+}
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the memory fence __syncthreads() carries (that
+// fence would wait for every outstanding LDS DMA, defeating the prefetch).
+// Callers order their own LDS traffic with explicit vmcnt / lgkmcnt waits;
+// the empty asm keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0,
+// which is how the kernels guard ragged tails without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const int n = bytes < 0 ? 0 : (bytes > 0x7ffffff0LL ? 0x7ffffff0 : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
 
 // Key slot order of the transposed V tile.  Register r of an S^T accumulator
 // tile holds key 8 * (r / 4) + 4 * g + (r % 4); the P.V product consumes

@@ -125,130 +125,274 @@ __device__ __forceinline__ void fwd_epilogue(const FwdParams &p, const FwdWork &
 }
 
 // ------------------------------------------------------------ fp16 / bf16
-// MFMA v_mfma_f32_32x32x16_{f16,bf16}; f32 accumulation; P rounded to T (RNE)
-// as the operand of the P.V product, the row sum taken from the f32 P.
-template <typename T, int D, int BC, int MASK>
-__global__ void __launch_bounds__(kThreads, 2) fwd16_kernel(FwdParams p) {
+// v_mfma_f32_32x32x16_{f16,bf16}, f32 accumulation; P is rounded to T (RNE) as
+// the operand of the P.V product while the row sum takes the f32 P.
+//
+// A workgroup of 8 waves owns one 128-row query tile at a time: wave w serves
+// rows 32 (w & 3) .. +32 and key half w >> 2 of every key block, so two waves
+// per SIMD overlap one's exponentials with the other's MFMAs.  The two halves
+// keep separate running states (m, l, U) that are merged through LDS once per
+// tile with the same combine rule the recurrence uses between blocks.
+//
+// K and V blocks travel HBM/L2 -> LDS by buffer_load ... lds (no staging
+// registers), double-buffered with one barrier per block; the buffer range
+// check zero-fills rows past the tail.  Both tiles stay row-major in LDS: K is
+// read as the A operand of S^T = K Q^T with 16-byte reads, V as the A operand
+// of U^T = V^T P^T with ds_read_b64_tr_b16, which gathers the 8 keys of one
+// feature column per lane in hardware.  Causal work items pair tile i with tile
+// T-1-i so every workgroup scans T+1 blocks, which balances the launch without
+// a work queue.
+//
+// Rescaling is lazy: the exponent reference m_ref only moves when a row's block
+// maximum exceeds it by more than kLazyLog2 (so p <= 2^kLazyLog2); the exact
+// row maximum is tracked beside it and l is re-expressed against it at the end.
+// In exact arithmetic this is the same recurrence with a stale but consistent
+// reference; it skips the per-block rescale of U for almost every block.
+constexpr int kT16 = 512;
+constexpr float kLazyLog2 = 8.f;
+
+template <int D>
+struct Fwd16Cfg {
+    static constexpr int BC = (D == 64) ? 256 : 128;  // keys per block
+    static constexpr int KH = BC / 2;                 // keys per wave group
+    static constexpr int ROW = D * 2;                 // bytes per K / V row in LDS
+    static constexpr int CPR = ROW / 16;              // 16-byte chunks per row
+    static constexpr int TILE = BC * ROW;             // bytes of one K (or V) block
+    static constexpr int STAGE = 2 * TILE;            // K then V
+    static constexpr int NDMA = TILE / (kT16 * 16);   // DMA instructions per tile per thread
+    static constexpr int NS = KH / 32, NKK = D / 16, NPV = KH / 16, NDT = D / 32;
+    static_assert(NDMA * kT16 * 16 == TILE, "block must split evenly over the DMA lanes");
+};
+
+// Tree reductions over one lane's score registers.
+template <int NS>
+__device__ __forceinline__ float tree_max(const f32x16 (&S)[NS]) {
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float x = kNegInf;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) x = fmaxf(x, fmaxf(S[s][2 * i], S[s][2 * i + 1]));
+        t[i] = x;
+    }
+    return fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])), fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
+}
+
+template <typename T, int D, int MASK>
+__device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h, int q_lo,
+                                           int q_hi, int kv_lo, int kv_hi) {
+    typedef Fwd16Cfg<D> C;
     typedef typename Half8<T>::vec vec8;
     constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
-    constexpr int KCH = D / 8;                  // 16-byte chunks per K row
-    constexpr int VCH = BC / 8;                 // 16-byte chunks per transposed V row
-    constexpr int KLD = BC * KCH / kThreads;    // K chunks each thread stages per block
-    constexpr int NS = BC / 32;                 // S^T tiles per block
-    constexpr int NDT = D / 32;                 // output feature tiles
-    constexpr int NKK = D / 16;                 // k-steps of K Q^T
-    constexpr int NPV = BC / 16;                // k-steps of V^T P^T
-    static_assert((BC / 4) * (D / 8) == kThreads, "one 4-key x 8-feature V unit per thread");
-    static_assert(KLD * kThreads == BC * KCH, "K block must split evenly over the threads");
-
-    __shared__ u32x4 sK[BC * KCH];
-    __shared__ u32x4 sV[D * VCH];
-
-    const FwdWork w = fwd_work<MASK>(p);
-    if (!w.ok) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rg = wave & 3, kg = wave >> 2;
     const int c32 = lane & 31, g = lane >> 5;
-    const T *qh = static_cast<const T *>(p.q) + (int64_t)w.h * p.q_sh;
-    const T *kh = static_cast<const T *>(p.k) + (int64_t)w.h * p.kv_sh;
-    const T *vh = static_cast<const T *>(p.v) + (int64_t)w.h * p.kv_sh;
+    constexpr int esz = (int)sizeof(T);
 
-    // F0: this lane's query row, as the B operand (8 features per k-step).
-    const int qrow = w.q_lo + wave * 32 + c32;
-    const bool qok = qrow < w.q_hi;
-    vec8 qreg[NKK];
+    // F0: this lane's query row as the B operand (zero past the tile end).
+    const int qrow = q_lo + 32 * rg + c32;
+    const T *qb = static_cast<const T *>(p.q) + (int64_t)h * p.q_sh + (int64_t)q_lo * p.q_sn;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (int64_t)(q_hi - q_lo) * p.q_sn * esz);
+    vec8 qreg[C::NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-        qreg[kk] = __builtin_bit_cast(vec8, load16(qh + (int64_t)qrow * p.q_sn + 16 * kk + 8 * g, qok));
+    for (int kk = 0; kk < C::NKK; ++kk)
+        qreg[kk] = __builtin_bit_cast(vec8, bload16(rq, ((32 * rg + c32) * (int)p.q_sn + 16 * kk + 8 * g) * esz));
 
-    // F1: K rows copied as 16-byte chunks; V as 4-key x 8-feature units that
-    // are transposed in registers into the (feature, key-slot) LDS tile.
-    const int v_d8 = tid % (D / 8), v_k4 = tid / (D / 8);
-    u32x4 kreg[KLD], vreg[4];
-    auto gload = [&](int k0) {
+    const T *kh = static_cast<const T *>(p.k) + (int64_t)h * p.kv_sh;
+    const T *vh = static_cast<const T *>(p.v) + (int64_t)h * p.kv_sh;
+    const int kv_sn = (int)p.kv_sn;
+
+    // F1: DMA block [k0, k0 + BC) of K and V into stage `buf`.  DMA
+    // instruction i of this wave fills LDS bytes [(8 i + wave) 1 KiB, +1 KiB)
+    // of each tile; each lane fetches the global chunk its swizzled LDS slot
+    // holds.  Rows at or past kv_hi arrive as zeros.
+    int dma_off[C::NDMA];
 #pragma unroll
-        for (int i = 0; i < KLD; ++i) {
-            const int id = tid + i * kThreads, row = id / KCH, ch = id % KCH;
-            const int key = k0 + row;
-            kreg[i] = load16(kh + (int64_t)key * p.kv_sn + ch * 8, key < w.kv_hi);
-        }
+    for (int i = 0; i < C::NDMA; ++i) {
+        const int byte = (8 * i + wave) * 1024 + 16 * lane;
+        const int row = byte / C::ROW, pch = (byte % C::ROW) / 16;
+        (void)pch;
+        dma_off[i] = row * kv_sn * esz;  // + logical chunk, per tile below
+    }
+    auto issue = [&](int k0, int buf) {
+        const int64_t bytes = (int64_t)(kv_hi - k0) * kv_sn * esz;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh + (int64_t)k0 * kv_sn, bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh + (int64_t)k0 * kv_sn, bytes);
+        char *sk = smem + buf * C::STAGE;
+        char *sv = sk + C::TILE;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = k0 + 4 * v_k4 + i;
-            vreg[i] = load16(vh + (int64_t)key * p.kv_sn + v_d8 * 8, key < w.kv_hi);
-        }
-    };
-    auto lds_store = [&]() {
-#pragma unroll
-        for (int i = 0; i < KLD; ++i) {
-            const int id = tid + i * kThreads, row = id / KCH, ch = id % KCH;
-            sK[row * KCH + swz(row, ch)] = kreg[i];
-        }
-        const int slot0 = key_slot(4 * v_k4);  // 4 consecutive keys -> 4 consecutive slots
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-            const unsigned a0 = vreg[0][w2], a1 = vreg[1][w2], a2 = vreg[2][w2], a3 = vreg[3][w2];
-            const int d0 = v_d8 * 8 + 2 * w2, d1 = d0 + 1;
-            uint2 lo, hi;
-            lo.x = (a0 & 0xffffu) | (a1 << 16);
-            lo.y = (a2 & 0xffffu) | (a3 << 16);
-            hi.x = (a0 >> 16) | (a1 & 0xffff0000u);
-            hi.y = (a2 >> 16) | (a3 & 0xffff0000u);
-            reinterpret_cast<uint2 *>(&sV[d0 * VCH + swz_t(d0, slot0 >> 3)])[(slot0 >> 2) & 1] = lo;
-            reinterpret_cast<uint2 *>(&sV[d1 * VCH + swz_t(d1, slot0 >> 3)])[(slot0 >> 2) & 1] = hi;
+        for (int i = 0; i < C::NDMA; ++i) {
+            const int byte = (8 * i + wave) * 1024 + 16 * lane;
+            const int row = byte / C::ROW, pch = (byte % C::ROW) / 16;
+            dma16(rk, sk + (8 * i + wave) * 1024, dma_off[i] + swz_k<C::ROW>(row, pch) * 16);
+            dma16(rv, sv + (8 * i + wave) * 1024, dma_off[i] + swz_vt<C::ROW>(row, pch) * 16);
         }
     };
 
-    f32x16 U[NDT];
+    f32x16 U[C::NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) U[dt] = zero_vec<f32x16>();
-    float m_run = kNegInf, l_run = 0.f;
+    for (int dt = 0; dt < C::NDT; ++dt) U[dt] = zero_vec<f32x16>();
+    float m_ref = kNegInf, m_true = kNegInf, l_run = 0.f;
     const float c = p.scale_log2;
-    const int nblk = (w.kv_hi - w.kv_lo + BC - 1) / BC;
+    const int nblk = (kv_hi - kv_lo + C::BC - 1) / C::BC;
+    const int wrow_lo = q_lo + 32 * rg, wrow_hi = wrow_lo + 31;
 
-    gload(w.kv_lo);
-    for (int kb = 0; kb < nblk; ++kb) {
-        const int k0 = w.kv_lo + kb * BC;
-        __syncthreads();
-        lds_store();
-        __syncthreads();
-        if (kb + 1 < nblk) gload(k0 + BC);
+    issue(kv_lo, 0);
+    for (int j = 0; j < nblk; ++j) {
+        // Block j has landed (this thread's DMA) and, after the barrier, for
+        // every thread; every wave has also finished reading block j-1, so
+        // its stage can take block j+1.
+        wait_vmcnt<0>();
+        bare_barrier();
+        if (j + 1 < nblk) issue(kv_lo + (j + 1) * C::BC, (j + 1) & 1);
 
-        // F2: S^T = K Q^T (raw dot products).
-        f32x16 S[NS];
+        const int k0 = kv_lo + j * C::BC;
+        const int kw0 = k0 + kg * C::KH;  // first key of this wave's half
+        const char *sk = smem + (j & 1) * C::STAGE;
+        const char *sv = sk + C::TILE;
+        if (kw0 < kv_hi && (!causal || kw0 <= wrow_hi)) {
+            // F2: S^T = K Q^T for the wave's KH keys (raw dot products).
+            f32x16 S[C::NS];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            S[s] = zero_vec<f32x16>();
-            const u32x4 *krow = &sK[(32 * s + c32) * KCH];
+            for (int s = 0; s < C::NS; ++s) S[s] = zero_vec<f32x16>();
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-                S[s] = Half8<T>::mma(__builtin_bit_cast(vec8, krow[swz(c32, 2 * kk + g)]), qreg[kk], S[s]);
+            for (int kk = 0; kk < C::NKK; ++kk)
+#pragma unroll
+                for (int s = 0; s < C::NS; ++s) {
+                    const int row = kg * C::KH + 32 * s + c32;
+                    const vec8 a = *reinterpret_cast<const vec8 *>(sk + row * C::ROW + swz_k<C::ROW>(row, 2 * kk + g) * 16);
+                    S[s] = Half8<T>::mma(a, qreg[kk], S[s]);
+                }
+            // F3: mask blocks that cross the tail or the diagonal.
+            if (kw0 + C::KH > kv_hi || (causal && kw0 + C::KH - 1 > wrow_lo))
+                mask_block<C::NS, causal>(S, kw0, g, kv_hi, qrow);
+            // F4: block row maximum (in-lane tree, then the other lane half).
+            float mx = tree_max<C::NS>(S);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            m_true = fmaxf(m_true, mx);
+            // F5 (lazy): move the exponent reference only on a large increase.
+            if (__any((mx - m_ref) * c > kLazyLog2)) {
+                const float m_new = fmaxf(m_ref, mx);
+                const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_ref - m_new) * c);
+#pragma unroll
+                for (int dt = 0; dt < C::NDT; ++dt) U[dt] *= alpha;
+                l_run *= alpha;
+                m_ref = m_new;
+            }
+            const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
+            float ps[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < C::NPV; ++t) {
+                f32x8 x;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float pv = fast_exp2(fmaf(S[t >> 1][8 * (t & 1) + e], c, -mc));
+                    x[e] = pv;
+                    ps[e] += pv;
+                }
+                const vec8 P = __builtin_convertvector(x, vec8);
+                // F6: U += V^T P^T; keys 16 t + 8 x + 4 g + 0..3 of this half.
+                const int r0 = kg * C::KH + 16 * t + 4 * g + ((lane & 15) >> 2);
+                const int cc = lane & 3, hh = (lane >> 4) & 1;
+#pragma unroll
+                for (int dt = 0; dt < C::NDT; ++dt) {
+                    const int ch = 4 * dt + 2 * hh + (cc >> 1);
+                    const i16x4 lo = lds_read_tr16(sv + r0 * C::ROW + swz_vt<C::ROW>(r0, ch) * 16 + 8 * (cc & 1));
+                    const i16x4 hi = lds_read_tr16(sv + (r0 + 8) * C::ROW + swz_vt<C::ROW>(r0 + 8, ch) * 16 + 8 * (cc & 1));
+                    const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    U[dt] = Half8<T>::mma(a, P, U[dt]);
+                }
+            }
+            l_run += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
         }
-        // F3: mask only blocks that straddle the diagonal or the tail.
-        if (k0 + BC > w.kv_hi || (causal && k0 + BC - 1 > w.q_lo))
-            mask_block<NS, causal>(S, k0, g, w.kv_hi, qrow);
-        // F4, F5
-        const float alpha = online_update<NS>(S, m_run, l_run, c);
-        vec8 P[NPV];
+    }
+    __syncthreads();  // every wave is done with the last stage
+
+    // F7: merge the two key halves of each row, then O = U / l.
+    l_run += __shfl_xor(l_run, 32);
+    float *st = reinterpret_cast<float *>(smem);           // 4 x 3 x 64 floats
+    f32x4 *su = reinterpret_cast<f32x4 *>(smem + 4096);    // (rg, D/8, 64) float4
+    if (kg == 1) {
+        st[(rg * 3 + 0) * 64 + lane] = m_ref;
+        st[(rg * 3 + 1) * 64 + lane] = m_true;
+        st[(rg * 3 + 2) * 64 + lane] = l_run;
 #pragma unroll
-        for (int t = 0; t < NPV; ++t) {
-            f32x8 x;
+        for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = S[t >> 1][8 * (t & 1) + e];
-            P[t] = __builtin_convertvector(x, vec8);
-        }
-        // F6: U = alpha U + V^T P^T.
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) U[dt] *= alpha;
-#pragma unroll
-        for (int t = 0; t < NPV; ++t)
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const int d = 32 * dt + c32;
-                const vec8 a = __builtin_bit_cast(vec8, sV[d * VCH + swz_t(d, 2 * t + g)]);
-                U[dt] = Half8<T>::mma(a, P[t], U[dt]);
+            for (int j = 0; j < 4; ++j) {
+                f32x4 v = {U[dt][4 * j], U[dt][4 * j + 1], U[dt][4 * j + 2], U[dt][4 * j + 3]};
+                su[(rg * (D / 8) + dt * 4 + j) * 64 + lane] = v;
             }
     }
-    fwd_epilogue<NDT>(p, w, qrow, g, U, m_run, l_run);
+    __syncthreads();
+    if (kg == 0) {
+        const float m1 = st[(rg * 3 + 0) * 64 + lane];
+        const float t1 = st[(rg * 3 + 1) * 64 + lane];
+        const float l1 = st[(rg * 3 + 2) * 64 + lane];
+        float M = fmaxf(m_ref, m1);
+        M = (M == kNegInf) ? 0.f : M;
+        const float a0 = fast_exp2((m_ref - M) * c), a1 = fast_exp2((m1 - M) * c);
+        const float l = l_run * a0 + l1 * a1;
+        const float mt = fmaxf(m_true, t1);
+        if (qrow < q_hi) {
+            const float inv = 1.f / l;
+            const float f0 = a0 * inv, f1 = a1 * inv;
+            float *orow = p.o + (int64_t)h * p.o_sh + (int64_t)qrow * p.o_sn;
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 u1 = su[(rg * (D / 8) + dt * 4 + j) * 64 + lane];
+                    f32x4 val;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) val[e] = U[dt][4 * j + e] * f0 + u1[e] * f1;
+                    *reinterpret_cast<f32x4 *>(orow + 32 * dt + 8 * j + 4 * g) = val;
+                }
+            if (g == 0) {
+                p.m[(int64_t)h * p.n_q + qrow] = mt * p.scale;
+                p.l[(int64_t)h * p.n_q + qrow] = l * fast_exp2((M - mt) * c);
+            }
+        }
+    }
+    __syncthreads();  // the next tile's prologue reuses this LDS
+}
+
+template <typename T, int D, int MASK>
+__global__ void __launch_bounds__(kT16) fwd16_kernel(FwdParams p) {
+    constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
+    constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
+    __shared__ __attribute__((aligned(16))) char smem[2 * Fwd16Cfg<D>::STAGE];
+    const int b = blockIdx.x;
+    const int h = b % p.H;
+    int rest = b / p.H;
+    int seq_lo = 0, seq_hi = p.n_q, ntile = p.n_tiles;
+    if (varlen) {
+        const Span s = seq_bounds(p.cu, rest % p.num_seqs, p.n_q);
+        rest /= p.num_seqs;
+        seq_lo = s.lo;
+        seq_hi = s.hi;
+        ntile = (seq_hi - seq_lo + kBR - 1) / kBR;
+    }
+    int t0, t1;
+    if (causal || varlen) {
+        // pair (T-1-i, i); varlen pairs are issued longest sequences first
+        const int pairs_max = (p.n_tiles + 1) / 2;
+        const int i = varlen ? pairs_max - 1 - rest : rest;
+        if (i >= (ntile + 1) / 2) return;
+        t0 = ntile - 1 - i;
+        t1 = (i == t0) ? -1 : i;
+    } else {
+        t0 = rest;
+        t1 = -1;
+    }
+#pragma unroll 1
+    for (int k = 0; k < 2; ++k) {
+        const int tile = k == 0 ? t0 : t1;
+        if (tile < 0) break;
+        const int q_lo = seq_lo + tile * kBR, q_hi = min(q_lo + kBR, seq_hi);
+        const int kv_hi = causal ? q_hi : (varlen ? seq_hi : p.n_k);
+        fwd16_tile<T, D, MASK>(p, smem, h, q_lo, q_hi, seq_lo, kv_hi);
+    }
 }
 
 // ---------------------------------------------------------------------- f32
@@ -356,33 +500,38 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) fwd32_kernel(FwdPar
 
 // ------------------------------------------------------------------ launch
 template <int MASK>
-static void launch_fwd_mask(int dtype, int d, const FwdParams &p, int grid, hipStream_t st) {
-    const dim3 gr(grid), bl(kThreads);
+static void launch_fwd_mask(int dtype, int d, const FwdParams &p, int grid16, int grid32,
+                            hipStream_t st) {
     if (dtype == 1) {
-        if (d == 64) hipLaunchKernelGGL((fwd16_kernel<_Float16, 64, 128, MASK>), gr, bl, 0, st, p);
-        else hipLaunchKernelGGL((fwd16_kernel<_Float16, 128, 64, MASK>), gr, bl, 0, st, p);
+        if (d == 64) hipLaunchKernelGGL((fwd16_kernel<_Float16, 64, MASK>), dim3(grid16), dim3(kT16), 0, st, p);
+        else hipLaunchKernelGGL((fwd16_kernel<_Float16, 128, MASK>), dim3(grid16), dim3(kT16), 0, st, p);
     } else if (dtype == 2) {
-        if (d == 64) hipLaunchKernelGGL((fwd16_kernel<__bf16, 64, 128, MASK>), gr, bl, 0, st, p);
-        else hipLaunchKernelGGL((fwd16_kernel<__bf16, 128, 64, MASK>), gr, bl, 0, st, p);
+        if (d == 64) hipLaunchKernelGGL((fwd16_kernel<__bf16, 64, MASK>), dim3(grid16), dim3(kT16), 0, st, p);
+        else hipLaunchKernelGGL((fwd16_kernel<__bf16, 128, MASK>), dim3(grid16), dim3(kT16), 0, st, p);
     } else {
-        if (d == 64) hipLaunchKernelGGL((fwd32_kernel<64, 64, MASK>), gr, bl, 0, st, p);
-        else hipLaunchKernelGGL((fwd32_kernel<128, 32, MASK>), gr, bl, 0, st, p);
+        if (d == 64) hipLaunchKernelGGL((fwd32_kernel<64, 64, MASK>), dim3(grid32), dim3(kThreads), 0, st, p);
+        else hipLaunchKernelGGL((fwd32_kernel<128, 32, MASK>), dim3(grid32), dim3(kThreads), 0, st, p);
     }
 }
 
 // Host entry used by the C ABI (arguments already validated).
 hipError_t launch_forward(int dtype, int d, int mask, FwdParams p, int max_seqlen,
                           hipStream_t st) {
-    const int rows = (mask >= kVarlen) ? max_seqlen : p.n_q;
+    const bool varlen = mask >= kVarlen, causal = mask == kCausal || mask == kVarlenCausal;
+    const int rows = varlen ? max_seqlen : p.n_q;
     p.n_tiles = (rows + kBR - 1) / kBR;
-    const int64_t grid = (int64_t)p.n_tiles * p.H * (mask >= kVarlen ? p.num_seqs : 1);
-    if (grid <= 0) return hipSuccess;
-    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const int64_t seqs = varlen ? p.num_seqs : 1;
+    // f32 kernel: one workgroup per (head, sequence, tile).
+    const int64_t grid32 = (int64_t)p.n_tiles * p.H * seqs;
+    // 16-bit kernel: tile pairs for causal / varlen, single tiles otherwise.
+    const int64_t grid16 = (int64_t)((causal || varlen) ? (p.n_tiles + 1) / 2 : p.n_tiles) * p.H * seqs;
+    if (grid32 <= 0) return hipSuccess;
+    if (grid32 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     switch (mask) {
-        case kDense: launch_fwd_mask<kDense>(dtype, d, p, (int)grid, st); break;
-        case kCausal: launch_fwd_mask<kCausal>(dtype, d, p, (int)grid, st); break;
-        case kVarlen: launch_fwd_mask<kVarlen>(dtype, d, p, (int)grid, st); break;
-        default: launch_fwd_mask<kVarlenCausal>(dtype, d, p, (int)grid, st); break;
+        case kDense: launch_fwd_mask<kDense>(dtype, d, p, (int)grid16, (int)grid32, st); break;
+        case kCausal: launch_fwd_mask<kCausal>(dtype, d, p, (int)grid16, (int)grid32, st); break;
+        case kVarlen: launch_fwd_mask<kVarlen>(dtype, d, p, (int)grid16, (int)grid32, st); break;
+        default: launch_fwd_mask<kVarlenCausal>(dtype, d, p, (int)grid16, (int)grid32, st); break;
     }
     return hipGetLastError();
 }

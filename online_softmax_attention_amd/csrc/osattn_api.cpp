@@ -39,6 +39,7 @@ size_t elem_size(int dtype) { return dtype == OSATTN_F32 ? 4 : 2; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int64_t kMaxLen = (int64_t)1 << 30;
+constexpr int64_t kMaxRowBytes = (int64_t)1 << 22;  // 4 MiB between consecutive rows
 
 // Checks shared by the forward and the backward.  Returns OSATTN_OK or an
 // error status with g_err set.
@@ -165,6 +166,10 @@ int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
     if ((st = check_tensor("k", k, kv_stride_h, kv_stride_n, es))) return st;
     if ((st = check_tensor("v", v, kv_stride_h, kv_stride_n, es))) return st;
     if ((st = check_tensor("o", o, o_stride_h, o_stride_n, 4))) return st;
+    // The kernels address one 256-row block with 32-bit byte offsets.
+    if (q_stride_n * (int64_t)es > kMaxRowBytes || kv_stride_n * (int64_t)es > kMaxRowBytes)
+        return fail(OSATTN_ERR_UNSUPPORTED, "row strides above %lld bytes are not supported",
+                    (long long)kMaxRowBytes);
     if (!m || !l) return fail(OSATTN_ERR_INVALID_ARG, "m and l must not be NULL");
 
     FwdParams p{};

@@ -130,3 +130,9 @@ def test_bwd_workspace_bytes(lib):
     assert lib.osattn_bwd_workspace_bytes(F16, 1, 8192, 2048, 64, 0, None, 0, 0) == 0
     assert lib.osattn_bwd_workspace_bytes(F32, 1, 8192, 2048, 128, 0, None, 0, 0) == 0
     assert lib.osattn_bwd_workspace_bytes(F32, 0, 8192, 2048, 64, 0, None, 0, 0) == 0
+
+
+def test_fwd_rejects_huge_row_stride(lib):
+    big = (1 << 22) // 2 + 8  # f16 elements: just above 4 MiB per row
+    assert fwd(lib, qs=(big * 128, big)) == osa.ERR_UNSUPPORTED
+    assert fwd(lib, kvs=(big * 128, big)) == osa.ERR_UNSUPPORTED
