@@ -89,11 +89,28 @@ typedef enum osattn_status {
 } osattn_status;
 
 /*
+ * Bytes of optional forward workspace for this problem, 0 when none is used.
+ * A non-zero size means the problem has too few 128-row query tiles to occupy
+ * the device (fp16/bf16, dense relation): given a workspace, osattn_fwd then
+ * splits each tile's key range over several workgroups that write partial
+ * (m, l, U) states to it, and a second kernel on the same stream combines
+ * them.  Queries the current device's compute-unit count.
+ */
+size_t osattn_fwd_workspace_bytes(int dtype, int H, int64_t n_q, int64_t n_k, int d,
+                                  int causal, const int32_t *cu_seqlens, int num_seqs,
+                                  int max_seqlen);
+
+/*
  * Forward pass.  Computes o (f32), m and l as defined above for H heads of
  * n_q queries against n_k keys of feature width d.
  *
- * Rows of o, m, l are written for every query position; each value is
- * produced by exactly one workgroup (no atomics; results are deterministic).
+ * workspace (device, 256-byte aligned, optional): NULL, or smaller than
+ * osattn_fwd_workspace_bytes(...), runs the unsplit forward; otherwise it
+ * holds the split partial states (contents on entry are ignored).  Calls that
+ * share a workspace must be ordered on one stream (concurrent calls race).
+ *
+ * Rows of o, m, l are written for every query position.  No atomics touch the
+ * outputs; results are deterministic for a given problem and device.
  */
 int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d,
                const void *q, const void *k, const void *v,
@@ -103,6 +120,7 @@ int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d,
                float *m, float *l,
                float scale, int causal,
                const int32_t *cu_seqlens, int num_seqs, int max_seqlen,
+               void *workspace, size_t workspace_bytes,
                void *stream);
 
 /*

@@ -27,8 +27,8 @@ LIB_PATH = os.path.join(_HERE, "libosattn.so")
 
 F32, F16, BF16 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_HIP, ERR_WORKSPACE = range(6)
-EXPORTS = ("osattn_fwd", "osattn_bwd", "osattn_bwd_workspace_bytes", "osattn_status_string",
-           "osattn_last_error", "osattn_version")
+EXPORTS = ("osattn_fwd", "osattn_fwd_workspace_bytes", "osattn_bwd", "osattn_bwd_workspace_bytes",
+           "osattn_status_string", "osattn_last_error", "osattn_version")
 
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 _lib = None
@@ -51,8 +51,10 @@ def load(path: Optional[str] = None):
     lib = ctypes.CDLL(p)
     i32, i64, f32, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
     lib.osattn_fwd.argtypes = [i32, i32, i64, i64, i32, vp, vp, vp, i64, i64, i64, i64,
-                               vp, i64, i64, vp, vp, f32, i32, vp, i32, i32, vp]
+                               vp, i64, i64, vp, vp, f32, i32, vp, i32, i32, vp, ctypes.c_size_t, vp]
     lib.osattn_fwd.restype = i32
+    lib.osattn_fwd_workspace_bytes.argtypes = [i32, i32, i64, i64, i32, i32, vp, i32, i32]
+    lib.osattn_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.osattn_bwd_workspace_bytes.argtypes = [i32, i32, i64, i64, i32, i32, vp, i32, i32]
     lib.osattn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.osattn_bwd.argtypes = [i32, i32, i64, i64, i32, vp, vp, vp, vp, vp, i64, i64, i64, i64,
@@ -124,11 +126,29 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+# Forward split-KV workspaces, one per (device, stream).
+_fwd_ws = {}
+
+
+def _fwd_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _fwd_ws.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _fwd_ws[key] = ws
+    return ws
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
         causal: bool = False, cu_seqlens: Optional[torch.Tensor] = None,
         max_seqlen: Optional[int] = None, layout: str = "hnd", check: bool = True,
-        out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
-    """Attention forward on the GPU; returns (o, m, l)."""
+        out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+        workspace: Optional[torch.Tensor] = None):
+    """Attention forward on the GPU; returns (o, m, l).
+
+    ``workspace``: optional device buffer for split-KV partial states (see
+    osattn_fwd_workspace_bytes); by default a cached one per (device, stream).
+    An empty tensor forces the unsplit forward."""
     lib = load()
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share one dtype of float32/float16/bfloat16")
@@ -147,10 +167,17 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float
     else:
         o, m, l = out
     _, _, _, o_sh, o_sn = _hn(o, layout)
+    cu_ptr = None if cu is None else cu.data_ptr()
+    if workspace is None:
+        need = lib.osattn_fwd_workspace_bytes(_DT[q.dtype], H, n_q, n_k, D, int(bool(causal)),
+                                              cu_ptr, num_seqs, max_seqlen)
+        workspace = _fwd_workspace(q.device, int(need)) if need else None
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.osattn_fwd(_DT[q.dtype], H, n_q, n_k, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                         q_sh, q_sn, kv_sh, kv_sn, o.data_ptr(), o_sh, o_sn, m.data_ptr(),
-                        l.data_ptr(), scale, int(bool(causal)),
-                        None if cu is None else cu.data_ptr(), num_seqs, max_seqlen, _stream())
+                        l.data_ptr(), scale, int(bool(causal)), cu_ptr, num_seqs, max_seqlen,
+                        ws_ptr, ws_bytes, _stream())
     _check(st, "osattn_fwd")
     return o, m, l
 

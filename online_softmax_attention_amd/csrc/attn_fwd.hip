@@ -151,37 +151,37 @@ __device__ __forceinline__ void fwd_epilogue(const FwdParams &p, const FwdWork &
 constexpr int kT16 = 512;
 constexpr float kLazyLog2 = 8.f;
 
-template <int D>
+// NST pipeline stages share 128 KiB of LDS: 2 stages of BC keys, or 4 stages
+// of half as many keys each (deeper prefetch).  Measured on MI355X, 4 stages
+// gained nothing at the shapes here (0.98x-1.03x), so launches use 2.
+template <int D, int NST>
 struct Fwd16Cfg {
-    static constexpr int BC = (D == 64) ? 256 : 128;  // keys per block
+    static constexpr int BC = ((D == 64) ? 256 : 128) * 2 / NST;  // keys per block
     static constexpr int KH = BC / 2;                 // keys per wave group
     static constexpr int ROW = D * 2;                 // bytes per K / V row in LDS
     static constexpr int CPR = ROW / 16;              // 16-byte chunks per row
     static constexpr int TILE = BC * ROW;             // bytes of one K (or V) block
     static constexpr int STAGE = 2 * TILE;            // K then V
     static constexpr int NDMA = TILE / (kT16 * 16);   // DMA instructions per tile per thread
-    static constexpr int NS = KH / 32, NKK = D / 16, NPV = KH / 16, NDT = D / 32;
+    static constexpr int NS = KH / 32, NKK = D / 16, NDT = D / 32;  // 32-key chunks per wave
+    static constexpr int NDMA_BLOCK = 2 * NDMA;      // DMA instructions per block per thread
     static_assert(NDMA * kT16 * 16 == TILE, "block must split evenly over the DMA lanes");
+    static_assert(NST * STAGE == 131072, "stages fill 128 KiB");
 };
 
-// Tree reductions over one lane's score registers.
-template <int NS>
-__device__ __forceinline__ float tree_max(const f32x16 (&S)[NS]) {
-    float t[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float x = kNegInf;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) x = fmaxf(x, fmaxf(S[s][2 * i], S[s][2 * i + 1]));
-        t[i] = x;
-    }
-    return fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])), fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
+// Wait until at most `blocks` blocks of this thread's DMA are still in flight.
+template <int NDMA_BLOCK, int NST>
+__device__ __forceinline__ void wait_dma_blocks(int blocks) {
+    if (NST > 2 && blocks >= 2) wait_vmcnt<2 * NDMA_BLOCK>();
+    else if (NST > 2 && blocks == 1) wait_vmcnt<NDMA_BLOCK>();
+    else wait_vmcnt<0>();
 }
 
-template <typename T, int D, int MASK>
+// split < 0: write O, m, l.  split >= 0: write this key range's partial state.
+template <typename T, int D, int MASK, int NST>
 __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h, int q_lo,
-                                           int q_hi, int kv_lo, int kv_hi) {
-    typedef Fwd16Cfg<D> C;
+                                           int q_hi, int kv_lo, int kv_hi, int split) {
+    typedef Fwd16Cfg<D, NST> C;
     typedef typename Half8<T>::vec vec8;
     constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -237,73 +237,94 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
     const int nblk = (kv_hi - kv_lo + C::BC - 1) / C::BC;
     const int wrow_lo = q_lo + 32 * rg, wrow_hi = wrow_lo + 31;
 
-    issue(kv_lo, 0);
+    // Prefetch distance NST - 1 blocks.
+    for (int j = 0; j < NST - 1 && j < nblk; ++j) issue(kv_lo + j * C::BC, j);
     for (int j = 0; j < nblk; ++j) {
         // Block j has landed (this thread's DMA) and, after the barrier, for
         // every thread; every wave has also finished reading block j-1, so
-        // its stage can take block j+1.
-        wait_vmcnt<0>();
+        // its stage can take block j + NST - 1.
+        wait_dma_blocks<C::NDMA_BLOCK, NST>(min(NST - 2, nblk - 1 - j));
         bare_barrier();
-        if (j + 1 < nblk) issue(kv_lo + (j + 1) * C::BC, (j + 1) & 1);
+        if (j + NST - 1 < nblk) issue(kv_lo + (j + NST - 1) * C::BC, (j + NST - 1) % NST);
 
         const int k0 = kv_lo + j * C::BC;
         const int kw0 = k0 + kg * C::KH;  // first key of this wave's half
-        const char *sk = smem + (j & 1) * C::STAGE;
+        const char *sk = smem + (j % NST) * C::STAGE;
         const char *sv = sk + C::TILE;
         if (kw0 < kv_hi && (!causal || kw0 <= wrow_hi)) {
-            // F2: S^T = K Q^T for the wave's KH keys (raw dot products).
-            f32x16 S[C::NS];
+            // The wave's KH keys are processed as 32-key chunks, software
+            // pipelined: chunk cc+1's S^T MFMAs are issued before chunk cc's
+            // exponentials so the two overlap in the same scheduling region.
+            auto qk = [&](int cc) {  // F2: S^T = K Q^T for one 32-key chunk
+                f32x16 S = zero_vec<f32x16>();
+                const int row = kg * C::KH + 32 * cc + c32;
+                const char *krow = sk + row * C::ROW;
 #pragma unroll
-            for (int s = 0; s < C::NS; ++s) S[s] = zero_vec<f32x16>();
-#pragma unroll
-            for (int kk = 0; kk < C::NKK; ++kk)
-#pragma unroll
-                for (int s = 0; s < C::NS; ++s) {
-                    const int row = kg * C::KH + 32 * s + c32;
-                    const vec8 a = *reinterpret_cast<const vec8 *>(sk + row * C::ROW + swz_k<C::ROW>(row, 2 * kk + g) * 16);
-                    S[s] = Half8<T>::mma(a, qreg[kk], S[s]);
+                for (int kk = 0; kk < C::NKK; ++kk) {
+                    const vec8 a = *reinterpret_cast<const vec8 *>(krow + swz_k<C::ROW>(row, 2 * kk + g) * 16);
+                    S = Half8<T>::mma(a, qreg[kk], S);
                 }
-            // F3: mask blocks that cross the tail or the diagonal.
-            if (kw0 + C::KH > kv_hi || (causal && kw0 + C::KH - 1 > wrow_lo))
-                mask_block<C::NS, causal>(S, kw0, g, kv_hi, qrow);
-            // F4: block row maximum (in-lane tree, then the other lane half).
-            float mx = tree_max<C::NS>(S);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            m_true = fmaxf(m_true, mx);
-            // F5 (lazy): move the exponent reference only on a large increase.
-            if (__any((mx - m_ref) * c > kLazyLog2)) {
-                const float m_new = fmaxf(m_ref, mx);
-                const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_ref - m_new) * c);
+                return S;
+            };
+            f32x16 S = qk(0);
 #pragma unroll
-                for (int dt = 0; dt < C::NDT; ++dt) U[dt] *= alpha;
-                l_run *= alpha;
-                m_ref = m_new;
+            for (int cc = 0; cc < C::NS; ++cc) {
+                const int kc0 = kw0 + 32 * cc;
+                // F3: mask chunks that cross the tail or the diagonal.
+                if (kc0 + 32 > kv_hi || (causal && kc0 + 31 > wrow_lo)) {
+                    f32x16 Sm[1] = {S};
+                    mask_block<1, causal>(Sm, kc0, g, kv_hi, qrow);
+                    S = Sm[0];
+                }
+                // F4: chunk row maximum (in-lane, then the other lane half).
+                float t[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    t[i] = fmaxf(fmaxf(S[4 * i], S[4 * i + 1]), fmaxf(S[4 * i + 2], S[4 * i + 3]));
+                float mx = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                m_true = fmaxf(m_true, mx);
+                // F5 (lazy): move the exponent reference only on a large increase.
+                if (__any((mx - m_ref) * c > kLazyLog2)) {
+                    const float m_new = fmaxf(m_ref, mx);
+                    const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_ref - m_new) * c);
+#pragma unroll
+                    for (int dt = 0; dt < C::NDT; ++dt) U[dt] *= alpha;
+                    l_run *= alpha;
+                    m_ref = m_new;
+                }
+                const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
+                f32x16 Sn;
+                if (cc + 1 < C::NS) Sn = qk(cc + 1);
+                float ps[4];
+                vec8 P[2];
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    f32x8 x;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = fast_exp2(fmaf(S[8 * hf + e], c, -mc));
+                    ps[2 * hf] = (x[0] + x[1]) + (x[2] + x[3]);
+                    ps[2 * hf + 1] = (x[4] + x[5]) + (x[6] + x[7]);
+                    P[hf] = __builtin_convertvector(x, vec8);
+                }
+                l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+                // F6: U += V^T P^T over the chunk's two 16-key slices; slice hf
+                // holds keys 32 cc + 16 hf + 8 x + 4 g + 0..3 (x = 0, 1).
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int r0 = kg * C::KH + 32 * cc + 16 * hf + 4 * g + ((lane & 15) >> 2);
+                    const int cq = lane & 3, hh = (lane >> 4) & 1;
+#pragma unroll
+                    for (int dt = 0; dt < C::NDT; ++dt) {
+                        const int ch = 4 * dt + 2 * hh + (cq >> 1);
+                        const i16x4 lo = lds_read_tr16(sv + r0 * C::ROW + swz_vt<C::ROW>(r0, ch) * 16 + 8 * (cq & 1));
+                        const i16x4 hi = lds_read_tr16(sv + (r0 + 8) * C::ROW + swz_vt<C::ROW>(r0 + 8, ch) * 16 + 8 * (cq & 1));
+                        const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                        U[dt] = Half8<T>::mma(a, P[hf], U[dt]);
+                    }
+                }
+                if (cc + 1 < C::NS) S = Sn;
             }
-            const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
-            float ps[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int t = 0; t < C::NPV; ++t) {
-                f32x8 x;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float pv = fast_exp2(fmaf(S[t >> 1][8 * (t & 1) + e], c, -mc));
-                    x[e] = pv;
-                    ps[e] += pv;
-                }
-                const vec8 P = __builtin_convertvector(x, vec8);
-                // F6: U += V^T P^T; keys 16 t + 8 x + 4 g + 0..3 of this half.
-                const int r0 = kg * C::KH + 16 * t + 4 * g + ((lane & 15) >> 2);
-                const int cc = lane & 3, hh = (lane >> 4) & 1;
-#pragma unroll
-                for (int dt = 0; dt < C::NDT; ++dt) {
-                    const int ch = 4 * dt + 2 * hh + (cc >> 1);
-                    const i16x4 lo = lds_read_tr16(sv + r0 * C::ROW + swz_vt<C::ROW>(r0, ch) * 16 + 8 * (cc & 1));
-                    const i16x4 hi = lds_read_tr16(sv + (r0 + 8) * C::ROW + swz_vt<C::ROW>(r0 + 8, ch) * 16 + 8 * (cc & 1));
-                    const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    U[dt] = Half8<T>::mma(a, P, U[dt]);
-                }
-            }
-            l_run += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
         }
     }
     __syncthreads();  // every wave is done with the last stage
@@ -329,12 +350,29 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
         const float m1 = st[(rg * 3 + 0) * 64 + lane];
         const float t1 = st[(rg * 3 + 1) * 64 + lane];
         const float l1 = st[(rg * 3 + 2) * 64 + lane];
-        float M = fmaxf(m_ref, m1);
-        M = (M == kNegInf) ? 0.f : M;
+        const float M_raw = fmaxf(m_ref, m1);
+        const float M = (M_raw == kNegInf) ? 0.f : M_raw;
         const float a0 = fast_exp2((m_ref - M) * c), a1 = fast_exp2((m1 - M) * c);
         const float l = l_run * a0 + l1 * a1;
         const float mt = fmaxf(m_true, t1);
-        if (qrow < q_hi) {
+        if (split >= 0 && qrow < q_hi) {
+            // Partial state of this key range: U and l against reference M_raw.
+            float *prow = p.part + (((int64_t)split * p.H + h) * p.n_q + qrow) * (D + 4);
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 u1 = su[(rg * (D / 8) + dt * 4 + j) * 64 + lane];
+                    f32x4 val;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) val[e] = U[dt][4 * j + e] * a0 + u1[e] * a1;
+                    *reinterpret_cast<f32x4 *>(prow + 32 * dt + 8 * j + 4 * g) = val;
+                }
+            if (g == 0) {
+                f32x4 stv = {M_raw, mt, l, 0.f};
+                *reinterpret_cast<f32x4 *>(prow + D) = stv;
+            }
+        } else if (qrow < q_hi) {
             const float inv = 1.f / l;
             const float f0 = a0 * inv, f1 = a1 * inv;
             float *orow = p.o + (int64_t)h * p.o_sh + (int64_t)qrow * p.o_sn;
@@ -357,12 +395,74 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
     __syncthreads();  // the next tile's prologue reuses this LDS
 }
 
-template <typename T, int D, int MASK>
+// Split-KV combine: one pass over a row's partial states (U_s, l_s against
+// reference m_s) with the rule the recurrence uses between blocks -- a running
+// reference M, rescale by 2^((M_old - M) c) when it grows, add U_s 2^((m_s - M) c)
+// -- then O = U / l, m = the largest exact row maximum, l re-expressed against
+// it.  A workgroup of 256 threads covers 32 rows, 8 threads per row.
+constexpr int kCombineRows = 32;
+
+template <int D>
+__global__ void __launch_bounds__(256) fwd_combine_kernel(FwdParams p) {
+    constexpr int QD = D / 8;  // features per thread
+    const int h = blockIdx.x % p.H, grp = blockIdx.x / p.H;
+    const int row = grp * kCombineRows + (threadIdx.x >> 3), part = threadIdx.x & 7;
+    if (row >= p.n_q) return;
+    const float c = p.scale_log2;
+    const int64_t split_stride = (int64_t)p.H * p.n_q * (D + 4);
+    const float *base = p.part + ((int64_t)h * p.n_q + row) * (D + 4);
+    float acc[QD];
+#pragma unroll
+    for (int d = 0; d < QD; ++d) acc[d] = 0.f;
+    float M = kNegInf, MT = kNegInf, L = 0.f;
+#pragma unroll 4
+    for (int s = 0; s < p.splits; ++s) {
+        const float *ps = base + s * split_stride;
+        const f32x4 stv = *reinterpret_cast<const f32x4 *>(ps + D);
+        f32x4 u[QD / 4];
+#pragma unroll
+        for (int i = 0; i < QD / 4; ++i) u[i] = *reinterpret_cast<const f32x4 *>(ps + part * QD + 4 * i);
+        MT = fmaxf(MT, stv[1]);
+        const float Mn = fmaxf(M, stv[0]);
+        if (Mn == kNegInf) continue;  // nothing admitted so far
+        const float a_old = fast_exp2((M - Mn) * c), a_new = fast_exp2((stv[0] - Mn) * c);
+        L = L * a_old + stv[2] * a_new;
+#pragma unroll
+        for (int i = 0; i < QD / 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[4 * i + e] = acc[4 * i + e] * a_old + u[i][e] * a_new;
+        M = Mn;
+    }
+    const float inv = 1.f / L;
+    float *orow = p.o + (int64_t)h * p.o_sh + (int64_t)row * p.o_sn + part * QD;
+#pragma unroll
+    for (int i = 0; i < QD / 4; ++i) {
+        f32x4 v = {acc[4 * i] * inv, acc[4 * i + 1] * inv, acc[4 * i + 2] * inv, acc[4 * i + 3] * inv};
+        *reinterpret_cast<f32x4 *>(orow + 4 * i) = v;
+    }
+    if (part == 0) {
+        p.m[(int64_t)h * p.n_q + row] = MT * p.scale;
+        p.l[(int64_t)h * p.n_q + row] = L * fast_exp2((M - MT) * c);
+    }
+}
+
+template <typename T, int D, int MASK, int NST>
 __global__ void __launch_bounds__(kT16) fwd16_kernel(FwdParams p) {
     constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
     constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
-    __shared__ __attribute__((aligned(16))) char smem[2 * Fwd16Cfg<D>::STAGE];
+    __shared__ __attribute__((aligned(16))) char smem[NST * Fwd16Cfg<D, NST>::STAGE];
     const int b = blockIdx.x;
+    if (!causal && !varlen && p.splits > 1) {
+        // Split-KV item; the split index varies slowest so that all splits of
+        // a tile land on one XCD when H * n_tiles is a multiple of 8.
+        const int items = p.H * p.n_tiles;
+        const int split = b / items, r = b % items;
+        const int h = r % p.H, tile = r / p.H;
+        const int q_lo = tile * kBR, q_hi = min(q_lo + kBR, p.n_q);
+        const int k_lo = split * p.split_len, k_hi = min(k_lo + p.split_len, p.n_k);
+        fwd16_tile<T, D, MASK, NST>(p, smem, h, q_lo, q_hi, k_lo, k_hi, split);
+        return;
+    }
     const int h = b % p.H;
     int rest = b / p.H;
     int seq_lo = 0, seq_hi = p.n_q, ntile = p.n_tiles;
@@ -391,7 +491,7 @@ __global__ void __launch_bounds__(kT16) fwd16_kernel(FwdParams p) {
         if (tile < 0) break;
         const int q_lo = seq_lo + tile * kBR, q_hi = min(q_lo + kBR, seq_hi);
         const int kv_hi = causal ? q_hi : (varlen ? seq_hi : p.n_k);
-        fwd16_tile<T, D, MASK>(p, smem, h, q_lo, q_hi, seq_lo, kv_hi);
+        fwd16_tile<T, D, MASK, NST>(p, smem, h, q_lo, q_hi, seq_lo, kv_hi, -1);
     }
 }
 
@@ -502,12 +602,15 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) fwd32_kernel(FwdPar
 template <int MASK>
 static void launch_fwd_mask(int dtype, int d, const FwdParams &p, int grid16, int grid32,
                             hipStream_t st) {
-    if (dtype == 1) {
-        if (d == 64) hipLaunchKernelGGL((fwd16_kernel<_Float16, 64, MASK>), dim3(grid16), dim3(kT16), 0, st, p);
-        else hipLaunchKernelGGL((fwd16_kernel<_Float16, 128, MASK>), dim3(grid16), dim3(kT16), 0, st, p);
-    } else if (dtype == 2) {
-        if (d == 64) hipLaunchKernelGGL((fwd16_kernel<__bf16, 64, MASK>), dim3(grid16), dim3(kT16), 0, st, p);
-        else hipLaunchKernelGGL((fwd16_kernel<__bf16, 128, MASK>), dim3(grid16), dim3(kT16), 0, st, p);
+    const dim3 g16(grid16), b16(kT16);
+    if (dtype == 1 || dtype == 2) {
+        if (dtype == 1) {
+            if (d == 64) hipLaunchKernelGGL((fwd16_kernel<_Float16, 64, MASK, 2>), g16, b16, 0, st, p);
+            else hipLaunchKernelGGL((fwd16_kernel<_Float16, 128, MASK, 2>), g16, b16, 0, st, p);
+        } else {
+            if (d == 64) hipLaunchKernelGGL((fwd16_kernel<__bf16, 64, MASK, 2>), g16, b16, 0, st, p);
+            else hipLaunchKernelGGL((fwd16_kernel<__bf16, 128, MASK, 2>), g16, b16, 0, st, p);
+        }
     } else {
         if (d == 64) hipLaunchKernelGGL((fwd32_kernel<64, 64, MASK>), dim3(grid32), dim3(kThreads), 0, st, p);
         else hipLaunchKernelGGL((fwd32_kernel<128, 32, MASK>), dim3(grid32), dim3(kThreads), 0, st, p);
@@ -524,7 +627,8 @@ hipError_t launch_forward(int dtype, int d, int mask, FwdParams p, int max_seqle
     // f32 kernel: one workgroup per (head, sequence, tile).
     const int64_t grid32 = (int64_t)p.n_tiles * p.H * seqs;
     // 16-bit kernel: tile pairs for causal / varlen, single tiles otherwise.
-    const int64_t grid16 = (int64_t)((causal || varlen) ? (p.n_tiles + 1) / 2 : p.n_tiles) * p.H * seqs;
+    const int64_t grid16 = (int64_t)((causal || varlen) ? (p.n_tiles + 1) / 2 : p.n_tiles) * p.H *
+                           seqs * ((causal || varlen) ? 1 : p.splits);
     if (grid32 <= 0) return hipSuccess;
     if (grid32 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     switch (mask) {
@@ -532,6 +636,11 @@ hipError_t launch_forward(int dtype, int d, int mask, FwdParams p, int max_seqle
         case kCausal: launch_fwd_mask<kCausal>(dtype, d, p, (int)grid16, (int)grid32, st); break;
         case kVarlen: launch_fwd_mask<kVarlen>(dtype, d, p, (int)grid16, (int)grid32, st); break;
         default: launch_fwd_mask<kVarlenCausal>(dtype, d, p, (int)grid16, (int)grid32, st); break;
+    }
+    if (p.splits > 1 && dtype != 0) {  // merge the partial states in a second launch
+        const dim3 gr(p.H * ((p.n_q + kCombineRows - 1) / kCombineRows)), bl(256);
+        if (d == 64) hipLaunchKernelGGL((fwd_combine_kernel<64>), gr, bl, 0, st, p);
+        else hipLaunchKernelGGL((fwd_combine_kernel<128>), gr, bl, 0, st, p);
     }
     return hipGetLastError();
 }

@@ -26,6 +26,12 @@ struct FwdParams {
     const int32_t *cu;     // device cumulative lengths (varlen) or null
     float scale;           // softmax scale
     float scale_log2;      // scale * log2(e)
+    // Split-KV (dense relation only): the key range is cut into `splits`
+    // pieces of `split_len` keys, one workgroup each; partial states go to
+    // `part` ((splits, H, n_q, D + 4) f32: U then m_ref, m_max, l) and a second
+    // launch combines them.  splits == 1: direct output.
+    float *part;
+    int splits, split_len;
 };
 
 struct BwdParams {

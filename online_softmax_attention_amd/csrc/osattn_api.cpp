@@ -79,6 +79,58 @@ int check_tensor(const char *name, const void *p, int64_t sh, int64_t sn, size_t
     return OSATTN_OK;
 }
 
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// ---------------------------------------------------------------- fwd plan
+// Split-KV applies to the 16-bit dense forward when its query tiles cannot
+// occupy half the device AND each would scan many key blocks alone (long keys,
+// few queries: decode-like shapes).  The key range is cut into 128-key-aligned
+// pieces.  A split costs a second (combine) launch of a few microseconds, which
+// is why short key ranges are not split: measured on MI355X, N=1024 H=4 D=64
+// ran 15 us unsplit vs 9 + 8 us split.
+struct FwdPlan {
+    int n_tiles, splits, split_len;
+    size_t total;
+};
+
+size_t round256_(size_t x) { return (x + 255) & ~(size_t)255; }
+
+FwdPlan plan_forward(int dtype, int H, int64_t n_q, int64_t n_k, int d, int causal,
+                     const int32_t *cu) {
+    FwdPlan pl{};
+    pl.n_tiles = (int)((n_q + 127) / 128);
+    pl.splits = 1;
+    pl.split_len = (int)n_k;
+    if (dtype != OSATTN_F32 && !causal && !cu) {
+        const int64_t items = (int64_t)H * pl.n_tiles;
+        const int64_t target = device_cus();
+        const int64_t blocks = (n_k + (d == 64 ? 255 : 127)) / (d == 64 ? 256 : 128);
+        if (2 * items <= target && blocks >= 16) {
+            const int64_t units = (n_k + 127) / 128;
+            int64_t splits = (target + items - 1) / items;
+            if (splits > units) splits = units;
+            if (splits > 64) splits = 64;
+            const int64_t per = (units + splits - 1) / splits;
+            pl.splits = (int)((units + per - 1) / per);
+            pl.split_len = (int)(per * 128);
+        }
+    }
+    if (pl.splits > 1) pl.total = round256_((size_t)pl.splits * H * n_q * (d + 4) * sizeof(float));
+    return pl;
+}
+
 int mask_kind(int causal, const int32_t *cu) {
     if (cu) return causal ? kVarlenCausal : kVarlen;
     return causal ? kCausal : kDense;
@@ -152,11 +204,18 @@ const char *osattn_status_string(int status) {
 
 const char *osattn_last_error(void) { return g_err; }
 
+size_t osattn_fwd_workspace_bytes(int dtype, int H, int64_t n_q, int64_t n_k, int d, int causal,
+                                  const int32_t *cu_seqlens, int num_seqs, int max_seqlen) {
+    if (check_common(dtype, H, n_q, n_k, d, 1.f, causal, cu_seqlens, num_seqs, max_seqlen)) return 0;
+    if (d != 64 && d != 128) return 0;
+    return plan_forward(dtype, H, n_q, n_k, d, causal, cu_seqlens).total;
+}
+
 int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q, const void *k,
                const void *v, int64_t q_stride_h, int64_t q_stride_n, int64_t kv_stride_h,
                int64_t kv_stride_n, float *o, int64_t o_stride_h, int64_t o_stride_n, float *m,
                float *l, float scale, int causal, const int32_t *cu_seqlens, int num_seqs,
-               int max_seqlen, void *stream) {
+               int max_seqlen, void *workspace, size_t workspace_bytes, void *stream) {
     int st = check_common(dtype, H, n_q, n_k, d, scale, causal, cu_seqlens, num_seqs, max_seqlen);
     if (st) return st;
     if (d != 64 && d != 128)
@@ -183,6 +242,16 @@ int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
     p.cu = cu_seqlens;
     p.scale = scale;
     p.scale_log2 = scale * 1.4426950408889634f;
+    p.splits = 1;
+    p.split_len = (int)n_k;
+    const FwdPlan pl = plan_forward(dtype, H, n_q, n_k, d, causal, cu_seqlens);
+    if (pl.splits > 1 && workspace && workspace_bytes >= pl.total) {
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+            return fail(OSATTN_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
+        p.part = static_cast<float *>(workspace);
+        p.splits = pl.splits;
+        p.split_len = pl.split_len;
+    }
     const hipError_t e = launch_forward(dtype, d, mask_kind(causal, cu_seqlens), p, max_seqlen,
                                         static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(OSATTN_ERR_HIP, "forward launch: %s", hipGetErrorString(e));

@@ -54,9 +54,10 @@ def test_status_strings(lib):
 # host check and reach a launch with the fake pointers.
 def fwd(lib, dtype=F16, H=2, n_q=128, n_k=128, d=64, q=A, k=B, v=C, qs=(128 * 64, 64),
         kvs=(128 * 64, 64), o=O, os_=(128 * 64, 64), m=None, l=L, scale=0.125, causal=0,
-        cu=None, num_seqs=0, max_seqlen=0):
+        cu=None, num_seqs=0, max_seqlen=0, ws=None, ws_bytes=0):
     return lib.osattn_fwd(dtype, H, n_q, n_k, d, q, k, v, qs[0], qs[1], kvs[0], kvs[1], o,
-                          os_[0], os_[1], m, l, scale, causal, cu, num_seqs, max_seqlen, None)
+                          os_[0], os_[1], m, l, scale, causal, cu, num_seqs, max_seqlen, ws,
+                          ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -122,6 +123,20 @@ def bwd(lib, dtype=F32, H=1, n_q=256, n_k=128, d=64, ptrs=None, ws=None, ws_byte
 ])
 def test_bwd_rejects_on_host(lib, kw, status):
     assert bwd(lib, **kw) == status
+
+
+def test_fwd_workspace_bytes(lib):
+    # decode-like dense shapes (few query tiles, long keys) split their key range
+    n = lib.osattn_fwd_workspace_bytes(F16, 4, 128, 16384, 64, 0, None, 0, 0)
+    assert n > 0 and n % 256 == 0
+    # short key ranges do not (a split costs a second launch)
+    assert lib.osattn_fwd_workspace_bytes(F16, 4, 1024, 1024, 64, 0, None, 0, 0) == 0
+    # causal, varlen and f32 problems never split
+    assert lib.osattn_fwd_workspace_bytes(F16, 4, 1024, 1024, 64, 1, None, 0, 0) == 0
+    assert lib.osattn_fwd_workspace_bytes(F32, 4, 1024, 1024, 64, 0, None, 0, 0) == 0
+    assert lib.osattn_fwd_workspace_bytes(F16, 4, 1024, 1024, 96, 0, None, 0, 0) == 0
+    # enough tiles to fill the device: no split
+    assert lib.osattn_fwd_workspace_bytes(BF16, 64, 8192, 8192, 128, 0, None, 0, 0) == 0
 
 
 def test_bwd_workspace_bytes(lib):

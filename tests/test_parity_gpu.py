@@ -233,3 +233,24 @@ def test_bwd_parity_f32(osattn, oracle, causal, n_q, n_k, H, lengths):
         assert_grad_close(host(g), r, "f32", name)
     for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):  # no atomics: bit-identical reruns
         assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------ split-KV forward
+@pytest.mark.parametrize("dtype,D,n_q,n_k,H", [("f16", 64, 128, 16384, 4), ("bf16", 128, 300, 2100, 2),
+                                               ("f16", 128, 129, 4097, 1), ("bf16", 64, 1, 8191, 3)])
+def test_split_kv_matches_oracle_and_unsplit(osattn, oracle, dtype, D, n_q, n_k, H):
+    lib = osattn.load()
+    inp = W.make_inputs(small("s", H, n_q, n_k, D, dtype, False, 4000 + n_k))
+    need = lib.osattn_fwd_workspace_bytes({"f16": 1, "bf16": 2}[dtype], H, n_q, n_k, D, 0, None, 0, 0)
+    assert need > 0, "these shapes are small enough to split"
+    q, k, v = (to_dev(x, dtype) for x in (inp.q, inp.k, inp.v))
+    ws = torch.full((need,), 0x7f, dtype=torch.uint8, device="cuda")  # contents are ignored
+    runs = [osattn.fwd(q, k, v, scale=inp.w.softmax_scale, workspace=ws) for _ in range(3)]
+    plain = osattn.fwd(q, k, v, scale=inp.w.softmax_scale,
+                       workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attn_fwd(inp.q32, inp.k32, inp.v32, inp.w.softmax_scale)
+    for o, m, l in runs + [plain]:
+        assert_fwd_close(host(o), host(m), host(l), ro, rm, rl, dtype, "split-KV %s" % dtype)
+    for a, b in zip(runs[0], runs[2]):  # the combine reads splits in a fixed order
+        assert torch.equal(a, b)
