@@ -4,22 +4,26 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME | --all]
 
 A step is one pass of the attention hot path over one batch of seeded
-synthetic input already resident in HBM: the forward (one fused kernel), or
-forward + backward for the workload that includes the backward.  After W
-untimed steps, K steps are timed between two device synchronisations; value is
-the algorithmic TFLOP/s of the whole step (forward 4 N_q N_k D H, halved for
-causal, summed per sequence for varlen; backward 2.5x the forward).  Rank 0
-prints ONE JSON line (one per workload with --all) that also carries:
+synthetic input already resident in HBM: the forward (one fused kernel, plus
+the combine kernel when the key range is split), or forward + backward for the
+workload that includes the backward.  After W untimed steps, K steps are timed
+between two device synchronisations, replayed from captured HIP graphs of 20
+steps so host launch overhead does not gate the GPU; value is the algorithmic
+TFLOP/s of the whole step (forward 4 N_q N_k D H, halved for causal, summed per
+sequence for varlen; backward 2.5x the forward).  Rank 0 prints ONE JSON line
+(one per workload with --all) that also carries:
 
-  roofline     : the dominant kernel's algorithmic FLOPs per launch over its
-                 average launch duration (HIP events around each launch on the
-                 launch stream), against MI355X's dense MFMA peak for its dtype;
+  roofline     : the forward kernel's algorithmic FLOPs per launch over its
+                 average device duration (HIP events around a replayed graph of
+                 back-to-back launches on the launch stream), against MI355X's
+                 dense MFMA peak for its dtype;
                  traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE /
                  WRITE_SIZE counters recorded in profiles/traffic.json, or null
                  when the kernel sources changed since they were recorded;
   cpu_baseline : the f64 CPU oracle timed on this host's cores on a bounded
                  row sample of the same workload (a reported baseline only);
-  parity       : max error of sampled output rows against that oracle.
+  parity       : max error of sampled output rows against that oracle, taken
+                 eagerly before timing and again after the last replayed step.
 Only one GPU is used; --gpus above 1 exits with a message.
 """
 import argparse
@@ -134,17 +138,14 @@ def cpu_baseline(w, inp, oracle, np, budget_s=10.0):
                       "workload (%.1f s on host cores)" % (rows_done, spent)}
 
 
-def time_launches(fn, torch, n):
-    """Average device duration of fn() over n launches, HIP events per launch."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n)]
-    for a, b in evs:
-        a.record()
-        fn()
-        b.record()
-    torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in evs]
-    return sum(ms) / len(ms), sorted(ms)[len(ms) // 2]
+def capture(fn, n, torch, stream):
+    """A graph of n back-to-back calls of fn() on `stream` (nothing allocates)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(n):
+                fn()
+    return g
 
 
 def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True):
@@ -157,10 +158,15 @@ def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True):
     m = torch.empty((H, w.n_q), dtype=torch.float32, device="cuda")
     l = torch.empty_like(m)
     fwd_out = (o, m, l)
+    num_seqs = 0 if cu is None else cu.numel() - 1
+    fws_bytes = osa.load().osattn_fwd_workspace_bytes(
+        osa._DT[q.dtype], H, w.n_q, w.n_k, D, int(w.causal),
+        None if cu is None else cu.data_ptr(), num_seqs, max_seqlen or 0)
+    fws = torch.empty(max(int(fws_bytes), 256), dtype=torch.uint8, device="cuda")
 
     def fwd():
         osa.fwd(q, k, v, scale=w.softmax_scale, causal=w.causal, cu_seqlens=cu,
-                max_seqlen=max_seqlen, check=False, out=fwd_out)
+                max_seqlen=max_seqlen, check=False, out=fwd_out, workspace=fws)
 
     bw = None
     if w.backward:
@@ -177,50 +183,74 @@ def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True):
         if bw is not None:
             bw()
 
-    # parity on sampled rows before timing
-    step()
-    torch.cuda.synchronize()
     rows = sample_rows(w, np)
     ro, rm, rl = oracle.attn_fwd(inp.q32, inp.k32, inp.v32, w.softmax_scale, causal=w.causal,
                                  cu_seqlens=inp.cu_seqlens, rows=rows)
-    og = o.reshape(-1, D).cpu().numpy()[rows]
-    err = float(np.max(np.abs(og - ro)))
-    parity = {"max_abs_err_o": err, "tol": TOL[w.dtype], "rows": int(len(rows)),
-              "ok": bool(err <= TOL[w.dtype])}
 
-    for _ in range(warmup):
+    def parity():
+        torch.cuda.synchronize()
+        og = o.reshape(-1, D).cpu().numpy()[rows]
+        return float(np.max(np.abs(og - ro)))
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
         step()
+        err_eager = parity()  # eager parity on sampled rows, before any timing
+        for _ in range(warmup):
+            step()
     torch.cuda.synchronize()
+
+    # Timed region: K steps replayed from captured graphs of G steps each, so
+    # that host launch overhead does not gate the GPU.
+    G = 20
+    g_steps = capture(step, G, torch, stream)
     if steps <= 0:  # auto: about 0.5 s of timed work, at least 100 steps
         t0 = time.perf_counter()
-        for _ in range(10):
-            step()
+        g_steps.replay()
         torch.cuda.synchronize()
-        per = (time.perf_counter() - t0) / 10
+        per = (time.perf_counter() - t0) / G
         steps = int(min(20000, max(100, 0.5 / max(per, 1e-7))))
+    steps = (steps + G - 1) // G * G
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
+    with torch.cuda.stream(stream):
+        e0.record()
+        for _ in range(steps // G):
+            g_steps.replay()
+        e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    err_graph = parity()  # outputs of the last replayed step
     ms_per_step = wall * 1e3 / steps
     step_flops = fwd_flops(w) + (bwd_flops(w) if w.backward else 0.0)
     value = step_flops / (wall / steps) / 1e12
+    parity_rec = {"max_abs_err_o": max(err_eager, err_graph), "tol": TOL[w.dtype],
+                  "rows": int(len(rows)), "ok": bool(max(err_eager, err_graph) <= TOL[w.dtype])}
 
-    # dominant kernel: the fused forward (the only kernel of a forward step)
+    # Roofline of the forward kernel: FLOPs per launch over its average device
+    # duration, from HIP events around replays of a graph of back-to-back
+    # forward launches on the launch stream.
     kern = "fwd16_kernel" if w.dtype != "f32" else "fwd32_kernel"
-    n_launch = max(100, min(steps, 2000))
-    avg_ms, med_ms = time_launches(fwd, torch, n_launch)
+    if fws_bytes:
+        kern += "+fwd_combine_kernel"
+    n_per, reps = 50, 10
+    g_fwd = capture(fwd, n_per, torch, stream)
+    with torch.cuda.stream(stream):
+        g_fwd.replay()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record()
+        for _ in range(reps):
+            g_fwd.replay()
+        f1.record()
+    torch.cuda.synchronize()
+    avg_ms = f0.elapsed_time(f1) / (n_per * reps)
     achieved = fwd_flops(w) / (avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak, "traffic": recorded_traffic(name, kern),
-                "kernel": kern, "launch_us_avg": avg_ms * 1e3, "launch_us_median": med_ms * 1e3,
-                "launches": n_launch, "flops_per_launch": fwd_flops(w)}
+                "kernel": kern, "launch_us_avg": avg_ms * 1e3, "launches": n_per * reps,
+                "flops_per_launch": fwd_flops(w)}
     out = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
            "warmup": warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
@@ -229,10 +259,11 @@ def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True):
            "config": {"workload": name, "H": H, "n_q": w.n_q, "n_k": w.n_k, "D": D,
                       "causal": w.causal, "varlen_seqs": len(w.lengths) if w.lengths else 0,
                       "pass": "fwd+bwd" if w.backward else "fwd",
-                      "layout": "(H, N, D)", "output": "O f32, m and l f32"},
+                      "layout": "(H, N, D)", "output": "O f32, m and l f32",
+                      "launch": "graphs of %d steps replayed" % G},
            "pct_of_peak": 100.0 * value / peak,
            "event_ms_per_step": e0.elapsed_time(e1) / steps,
-           "roofline": roofline, "parity": parity}
+           "roofline": roofline, "parity": parity_rec}
     if with_cpu:
         out["cpu_baseline"] = cpu_baseline(w, inp, oracle, np)
     return out
