@@ -90,11 +90,17 @@ typedef enum osattn_status {
 
 /*
  * Bytes of optional forward workspace for this problem, 0 when none is used.
- * A non-zero size means the problem has too few 128-row query tiles to occupy
- * the device (fp16/bf16, dense relation): given a workspace, osattn_fwd then
- * splits each tile's key range over several workgroups that write partial
- * (m, l, U) states to it, and a second kernel on the same stream combines
- * them.  Queries the current device's compute-unit count.
+ * Two fp16/bf16 cases use one:
+ *  - dense relation with too few 128-row query tiles to occupy the device:
+ *    osattn_fwd splits each tile's key range over several workgroups that
+ *    write partial (m, l, U) states to the workspace, and a second kernel on
+ *    the same stream combines them;
+ *  - varlen (cu_seqlens given): a first kernel writes a work list of the
+ *    (sequence, query tile) items, largest first, to the workspace, and the
+ *    forward takes its tiles in that order, which balances sequences of
+ *    mixed lengths over the device.
+ * Queries the current device's compute-unit count.  Returns 0 for invalid
+ * or unsupported requests.
  */
 size_t osattn_fwd_workspace_bytes(int dtype, int H, int64_t n_q, int64_t n_k, int d,
                                   int causal, const int32_t *cu_seqlens, int num_seqs,
@@ -105,9 +111,12 @@ size_t osattn_fwd_workspace_bytes(int dtype, int H, int64_t n_q, int64_t n_k, in
  * n_q queries against n_k keys of feature width d.
  *
  * workspace (device, 256-byte aligned, optional): NULL, or smaller than
- * osattn_fwd_workspace_bytes(...), runs the unsplit forward; otherwise it
- * holds the split partial states (contents on entry are ignored).  Calls that
- * share a workspace must be ordered on one stream (concurrent calls race).
+ * osattn_fwd_workspace_bytes(...), runs the forward without it (unsplit, and
+ * varlen tiles in their natural order); otherwise it holds the split partial
+ * states or the varlen work list (contents on entry are ignored).  Results
+ * are the same with or without it up to the order of the split merge (dense)
+ * and bitwise the same (varlen).  Calls that share a workspace must be ordered
+ * on one stream (concurrent calls race).
  *
  * Rows of o, m, l are written for every query position.  No atomics touch the
  * outputs; results are deterministic for a given problem and device.

@@ -446,6 +446,93 @@ __global__ void __launch_bounds__(256) fwd_combine_kernel(FwdParams p) {
     }
 }
 
+// ------------------------------------------------------- varlen work list
+// The hardware deals a grid's workgroups out in index order, and each XCD deals
+// its share to its shader engines in turn, waiting for the next engine in line
+// to have room.  On the natural varlen grid (head, sequence, tile pair) the
+// same sequences keep landing on the same engine, so one engine can hold most
+// of the long items while the others idle.  This kernel writes the varlen
+// items -- tile pairs (T-1-i, i) of one sequence, as in the causal grid -- as a
+// list ordered by the number of key blocks the pair scans, largest first: the
+// largest items start first and consecutive workgroups carry similar work.
+// Each entry holds the sequence bounds and both tiles, so a workgroup needs one
+// 16-byte load to start.  One workgroup builds the list with a counting sort in
+// LDS.  The order among items of equal size depends on LDS atomics; that
+// changes which workgroup computes a tile, never the tile's result.
+constexpr int kSchedThreads = 1024;
+
+// Key blocks that query tile t of a length-len sequence scans.
+template <int BC, bool CAUSAL>
+__device__ __forceinline__ int tile_blocks(int t, int len) {
+    return t < 0 ? 0 : ((CAUSAL ? min((t + 1) * kBR, len) : len) + BC - 1) / BC;
+}
+
+template <int BC, bool CAUSAL>
+__global__ void __launch_bounds__(kSchedThreads) varlen_schedule_kernel(FwdParams p) {
+    constexpr int PER = kSchedBins / kSchedThreads;
+    static_assert(PER * kSchedThreads == kSchedBins, "bins must split evenly over the threads");
+    __shared__ int cnt[kSchedBins];
+    __shared__ int wtot[kSchedThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    for (int i = tid; i < kSchedBins; i += kSchedThreads) cnt[i] = 0;
+    __syncthreads();
+    const auto bin = [&](int s_lo, int len, int i, int T) {
+        const int t0 = T - 1 - i, t1 = (i == t0) ? -1 : i;
+        const int w = tile_blocks<BC, CAUSAL>(t0, len) + tile_blocks<BC, CAUSAL>(t1, len);
+        return min(w >> p.sched_shift, kSchedBins - 1);
+    };
+    for (int s = tid; s < p.num_seqs; s += kSchedThreads) {
+        const Span sq = seq_bounds(p.cu, s, p.n_q);
+        const int len = sq.hi - sq.lo, T = (len + kBR - 1) / kBR;
+        for (int i = 0; i < (T + 1) / 2; ++i) atomicAdd(&cnt[bin(sq.lo, len, i, T)], 1);
+    }
+    __syncthreads();
+    // Exclusive scan from the top bin down: cnt[b] becomes bin b's first slot.
+    int v[PER], run = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        v[i] = cnt[kSchedBins - 1 - (tid * PER + i)];
+        run += v[i];
+    }
+    int incl = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) wtot[wv] = incl;
+    __syncthreads();
+    int base = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kSchedThreads / 64; ++w) {
+        const int t = wtot[w];
+        base += (w < wv) ? t : 0;
+        total += t;
+    }
+    int ex = base + incl - run;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        cnt[kSchedBins - 1 - (tid * PER + i)] = ex;
+        ex += v[i];
+    }
+    const int count = min(total, p.sched_max);
+    if (tid == 0) p.sched[0] = count;
+    __syncthreads();
+    // Place the items; slots past sched_max (reachable only with malformed
+    // cu_seqlens) are dropped, and unused slots get an empty entry.
+    int4 *items = reinterpret_cast<int4 *>(p.sched + 4);
+    for (int s = tid; s < p.num_seqs; s += kSchedThreads) {
+        const Span sq = seq_bounds(p.cu, s, p.n_q);
+        const int len = sq.hi - sq.lo, T = (len + kBR - 1) / kBR;
+        for (int i = 0; i < (T + 1) / 2; ++i) {
+            const int pos = atomicAdd(&cnt[bin(sq.lo, len, i, T)], 1);
+            const int t0 = T - 1 - i;
+            if (pos < p.sched_max) items[pos] = make_int4(sq.lo, sq.hi, t0, i == t0 ? -1 : i);
+        }
+    }
+    for (int i = count + tid; i < p.sched_max; i += kSchedThreads) items[i] = make_int4(0, 0, -1, -1);
+}
+
 template <typename T, int D, int MASK, int NST>
 __global__ void __launch_bounds__(kT16) fwd16_kernel(FwdParams p) {
     constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
@@ -465,6 +552,18 @@ __global__ void __launch_bounds__(kT16) fwd16_kernel(FwdParams p) {
     }
     const int h = b % p.H;
     int rest = b / p.H;
+    if (varlen && p.sched) {  // item `rest` of the sorted work list
+        const int4 it = reinterpret_cast<const int4 *>(p.sched + 4)[rest];
+#pragma unroll 1
+        for (int k = 0; k < 2; ++k) {
+            const int tile = k == 0 ? it.z : it.w;
+            if (tile < 0) break;
+            const int q_lo = it.x + tile * kBR, q_hi = min(q_lo + kBR, it.y);
+            if (q_lo >= q_hi) break;
+            fwd16_tile<T, D, MASK, NST>(p, smem, h, q_lo, q_hi, it.x, causal ? q_hi : it.y, -1);
+        }
+        return;
+    }
     int seq_lo = 0, seq_hi = p.n_q, ntile = p.n_tiles;
     if (varlen) {
         const Span s = seq_bounds(p.cu, rest % p.num_seqs, p.n_q);
@@ -631,11 +730,26 @@ hipError_t launch_forward(int dtype, int d, int mask, FwdParams p, int max_seqle
                            seqs * ((causal || varlen) ? 1 : p.splits);
     if (grid32 <= 0) return hipSuccess;
     if (grid32 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    int64_t g16 = grid16;
+    if (p.sched && varlen && dtype != 0) {  // sorted varlen work list first
+        const dim3 g1(1), b1(kSchedThreads);
+        if (d == 64) {
+            if (causal) hipLaunchKernelGGL((varlen_schedule_kernel<Fwd16Cfg<64, 2>::BC, true>), g1, b1, 0, st, p);
+            else hipLaunchKernelGGL((varlen_schedule_kernel<Fwd16Cfg<64, 2>::BC, false>), g1, b1, 0, st, p);
+        } else {
+            if (causal) hipLaunchKernelGGL((varlen_schedule_kernel<Fwd16Cfg<128, 2>::BC, true>), g1, b1, 0, st, p);
+            else hipLaunchKernelGGL((varlen_schedule_kernel<Fwd16Cfg<128, 2>::BC, false>), g1, b1, 0, st, p);
+        }
+        g16 = (int64_t)p.sched_max * p.H;
+    } else {
+        p.sched = nullptr;
+    }
+    if (g16 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     switch (mask) {
-        case kDense: launch_fwd_mask<kDense>(dtype, d, p, (int)grid16, (int)grid32, st); break;
-        case kCausal: launch_fwd_mask<kCausal>(dtype, d, p, (int)grid16, (int)grid32, st); break;
-        case kVarlen: launch_fwd_mask<kVarlen>(dtype, d, p, (int)grid16, (int)grid32, st); break;
-        default: launch_fwd_mask<kVarlenCausal>(dtype, d, p, (int)grid16, (int)grid32, st); break;
+        case kDense: launch_fwd_mask<kDense>(dtype, d, p, (int)g16, (int)grid32, st); break;
+        case kCausal: launch_fwd_mask<kCausal>(dtype, d, p, (int)g16, (int)grid32, st); break;
+        case kVarlen: launch_fwd_mask<kVarlen>(dtype, d, p, (int)g16, (int)grid32, st); break;
+        default: launch_fwd_mask<kVarlenCausal>(dtype, d, p, (int)g16, (int)grid32, st); break;
     }
     if (p.splits > 1 && dtype != 0) {  // merge the partial states in a second launch
         const dim3 gr(p.H * ((p.n_q + kCombineRows - 1) / kCombineRows)), bl(256);

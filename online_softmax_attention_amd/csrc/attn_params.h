@@ -13,6 +13,9 @@ enum MaskKind : int {
     kVarlenCausal = 3  // both
 };
 
+// Bins of the varlen work-list sort (sort keys are coarsened to fit).
+constexpr int kSchedBins = 4096;
+
 struct FwdParams {
     const void *q, *k, *v;
     float *o, *m, *l;
@@ -32,6 +35,14 @@ struct FwdParams {
     // launch combines them.  splits == 1: direct output.
     float *part;
     int splits, split_len;
+    // Varlen work list (16-bit kernels).  When non-null, a schedule kernel
+    // first writes sched[0] = number of items and, from sched + 4, sched_max
+    // int4 entries {seq_lo, seq_hi, tile0, tile1} (tile1 = -1: one tile;
+    // tile0 = -1: empty slot), ordered by the number of key blocks the item
+    // scans, largest first.  The grid has sched_max * H workgroups;
+    // sched_shift coarsens the sort key to fit the histogram.
+    int32_t *sched;
+    int sched_max, sched_shift;
 };
 
 struct BwdParams {

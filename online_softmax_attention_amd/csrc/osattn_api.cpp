@@ -102,13 +102,21 @@ int device_cus() {
 // ran 15 us unsplit vs 9 + 8 us split.
 struct FwdPlan {
     int n_tiles, splits, split_len;
-    size_t total;
+    int sched_max, sched_shift;  // varlen work list (0: none)
+    size_t total;                // workspace bytes (0: none used)
 };
 
-size_t round256_(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Varlen (16-bit): a schedule kernel sorts the varlen items (tile pairs
+// (T-1-i, i) of one sequence) by the key blocks they scan, largest first, into
+// the workspace, and the forward takes its items from that list (without a
+// workspace it walks the natural (sequence, pair) grid instead).  A sequence of
+// T_s tiles has ceil(T_s / 2) items, so the list holds at most
+// (sum_s T_s + S) / 2 entries, with sum_s T_s <= (n + 127 S) / 128 and
+// T_s <= ceil(max_seqlen / 128).
 FwdPlan plan_forward(int dtype, int H, int64_t n_q, int64_t n_k, int d, int causal,
-                     const int32_t *cu) {
+                     const int32_t *cu, int num_seqs, int max_seqlen) {
     FwdPlan pl{};
     pl.n_tiles = (int)((n_q + 127) / 128);
     pl.splits = 1;
@@ -127,7 +135,26 @@ FwdPlan plan_forward(int dtype, int H, int64_t n_q, int64_t n_k, int d, int caus
             pl.split_len = (int)(per * 128);
         }
     }
-    if (pl.splits > 1) pl.total = round256_((size_t)pl.splits * H * n_q * (d + 4) * sizeof(float));
+    if (pl.splits > 1) pl.total = round256((size_t)pl.splits * H * n_q * (d + 4) * sizeof(float));
+    // n == S * max_seqlen means every sequence has max_seqlen tokens: the natural
+    // grid is then balanced already and the list would only add a launch.
+    if (dtype != OSATTN_F32 && cu && num_seqs > 0 && max_seqlen > 0 &&
+        n_q != (int64_t)num_seqs * max_seqlen) {
+        const int64_t S = num_seqs, t_max = (max_seqlen + 127) / 128;
+        int64_t tiles = (n_q + 127 * S) / 128;
+        if (S * t_max < tiles) tiles = S * t_max;
+        int64_t bound = (tiles + S) / 2;
+        if (S * ((t_max + 1) / 2) < bound) bound = S * ((t_max + 1) / 2);
+        if (bound > 0 && bound * H <= 0x7fffffffLL) {
+            const int bc = d == 64 ? 256 : 128;  // key block of the 16-bit forward
+            const int64_t max_w = 2 * ((max_seqlen + bc - 1) / bc);
+            int shift = 0;
+            while ((max_w >> shift) >= kSchedBins) ++shift;
+            pl.sched_max = (int)bound;
+            pl.sched_shift = shift;
+            pl.total = round256(16 + 16 * (size_t)bound);
+        }
+    }
     return pl;
 }
 
@@ -141,8 +168,6 @@ struct BwdPlan {
     int q_tiles, k_tiles, q_splits, k_splits, seqs;
     size_t off_delta, off_mlog2, off_linv, off_dq, off_dk, off_dv, total;
 };
-
-size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int clampi(int64_t x, int lo, int hi) { return (int)(x < lo ? lo : (x > hi ? hi : x)); }
 
@@ -208,7 +233,7 @@ size_t osattn_fwd_workspace_bytes(int dtype, int H, int64_t n_q, int64_t n_k, in
                                   const int32_t *cu_seqlens, int num_seqs, int max_seqlen) {
     if (check_common(dtype, H, n_q, n_k, d, 1.f, causal, cu_seqlens, num_seqs, max_seqlen)) return 0;
     if (d != 64 && d != 128) return 0;
-    return plan_forward(dtype, H, n_q, n_k, d, causal, cu_seqlens).total;
+    return plan_forward(dtype, H, n_q, n_k, d, causal, cu_seqlens, num_seqs, max_seqlen).total;
 }
 
 int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q, const void *k,
@@ -244,13 +269,20 @@ int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
     p.scale_log2 = scale * 1.4426950408889634f;
     p.splits = 1;
     p.split_len = (int)n_k;
-    const FwdPlan pl = plan_forward(dtype, H, n_q, n_k, d, causal, cu_seqlens);
-    if (pl.splits > 1 && workspace && workspace_bytes >= pl.total) {
+    const FwdPlan pl = plan_forward(dtype, H, n_q, n_k, d, causal, cu_seqlens, num_seqs, max_seqlen);
+    if (pl.total > 0 && workspace && workspace_bytes >= pl.total) {
         if (reinterpret_cast<uintptr_t>(workspace) & 255u)
             return fail(OSATTN_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
-        p.part = static_cast<float *>(workspace);
-        p.splits = pl.splits;
-        p.split_len = pl.split_len;
+        if (pl.splits > 1) {
+            p.part = static_cast<float *>(workspace);
+            p.splits = pl.splits;
+            p.split_len = pl.split_len;
+        }
+        if (pl.sched_max > 0) {
+            p.sched = static_cast<int32_t *>(workspace);
+            p.sched_max = pl.sched_max;
+            p.sched_shift = pl.sched_shift;
+        }
     }
     const hipError_t e = launch_forward(dtype, d, mask_kind(causal, cu_seqlens), p, max_seqlen,
                                         static_cast<hipStream_t>(stream));

@@ -254,3 +254,41 @@ def test_split_kv_matches_oracle_and_unsplit(osattn, oracle, dtype, D, n_q, n_k,
         assert_fwd_close(host(o), host(m), host(l), ro, rm, rl, dtype, "split-KV %s" % dtype)
     for a, b in zip(runs[0], runs[2]):  # the combine reads splits in a fixed order
         assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------ varlen work list
+@pytest.mark.parametrize("dtype,D,causal", [("f16", 64, True), ("bf16", 128, True),
+                                            ("f16", 128, False), ("bf16", 64, False)])
+def test_varlen_work_list_matches_natural_order(osattn, oracle, dtype, D, causal):
+    """The sorted varlen work list only changes which workgroup computes a
+    tile: results equal the natural-order launch (no workspace) bit for bit
+    and the oracle within tolerance.  The workspace starts as garbage and a
+    second call with fewer sequences reuses it."""
+    lib = osattn.load()
+    lengths = [1300, 0, 5, 256, 129, 2048, 1, 700, 0, 383, 1024, 77]
+    n = sum(lengths)
+    inp = W.make_inputs(small("wl", 2, n, n, D, dtype, causal, 31337, lengths=lengths))
+    q, k, v = (to_dev(x, dtype) for x in (inp.q, inp.k, inp.v))
+    cu = cu_dev(inp.cu_seqlens)
+    code = {"f16": 1, "bf16": 2}[dtype]
+    need = lib.osattn_fwd_workspace_bytes(code, 2, n, n, D, int(causal), cu.data_ptr(),
+                                          len(lengths), max(lengths))
+    assert need > 0
+    ws = torch.full((need,), 0x7f, dtype=torch.uint8, device="cuda")
+    none = torch.empty(0, dtype=torch.uint8, device="cuda")
+    sc = inp.w.softmax_scale
+    for n_seq in (len(lengths), 5):
+        nt = int(inp.cu_seqlens[n_seq])
+        qs, ks, vs = q[:, :nt], k[:, :nt], v[:, :nt]
+        cus = cu[:n_seq + 1].contiguous()
+        a = osattn.fwd(qs, ks, vs, scale=sc, causal=causal, cu_seqlens=cus, workspace=ws)
+        b = osattn.fwd(qs, ks, vs, scale=sc, causal=causal, cu_seqlens=cus, workspace=none)
+        torch.cuda.synchronize()
+        for x, y in zip(a, b):
+            assert torch.equal(x, y), "work-list order changed a result (%d sequences)" % n_seq
+        ro, rm, rl = oracle.attn_fwd(np.ascontiguousarray(inp.q32[:, :nt]),
+                                     np.ascontiguousarray(inp.k32[:, :nt]),
+                                     np.ascontiguousarray(inp.v32[:, :nt]), sc, causal=causal,
+                                     cu_seqlens=inp.cu_seqlens[:n_seq + 1])
+        assert_fwd_close(host(a[0]), host(a[1]), host(a[2]), ro, rm, rl, dtype,
+                         "work list %s D=%d causal=%s seqs=%d" % (dtype, D, causal, n_seq))
