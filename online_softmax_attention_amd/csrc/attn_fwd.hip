@@ -177,15 +177,23 @@ __device__ __forceinline__ void wait_dma_blocks(int blocks) {
     else wait_vmcnt<0>();
 }
 
+// The 8 waves of a workgroup form RG row groups of 32 query rows (a tile of
+// 32 RG rows) times KG = 8 / RG key groups; key group kg takes keys
+// [kg KH, (kg + 1) KH) of every block, and the KG partial states of a row are
+// merged through LDS at the end.  Launches use RG = 4 (128-row tiles) unless
+// such tiles are too few to occupy the device.
 // split < 0: write O, m, l.  split >= 0: write this key range's partial state.
-template <typename T, int D, int MASK, int NST>
+template <typename T, int D, int MASK, int NST, int RG>
 __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h, int q_lo,
                                            int q_hi, int kv_lo, int kv_hi, int split) {
     typedef Fwd16Cfg<D, NST> C;
     typedef typename Half8<T>::vec vec8;
     constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
+    constexpr int KG = 8 / RG, KH = C::BC / KG, NS = KH / 32;  // keys, 32-key chunks per wave
+    static_assert(RG * KG == 8 && NS * 32 == KH && NS >= 1, "wave layout must tile the block");
+    static_assert(8192 + (8 - RG) * (D / 8) * 64 * 16 <= NST * C::STAGE, "merge buffers fit in LDS");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int rg = wave & 3, kg = wave >> 2;
+    const int rg = wave % RG, kg = wave / RG;
     const int c32 = lane & 31, g = lane >> 5;
     constexpr int esz = (int)sizeof(T);
 
@@ -248,7 +256,7 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
         if (j + NST - 1 < nblk) issue(kv_lo + (j + NST - 1) * C::BC, (j + NST - 1) % NST);
 
         const int k0 = kv_lo + j * C::BC;
-        const int kw0 = k0 + kg * C::KH;  // first key of this wave's half
+        const int kw0 = k0 + kg * KH;  // first key of this wave's group
         const char *sk = smem + (j % NST) * C::STAGE;
         const char *sv = sk + C::TILE;
         if (kw0 < kv_hi && (!causal || kw0 <= wrow_hi)) {
@@ -257,7 +265,7 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
             // exponentials so the two overlap in the same scheduling region.
             auto qk = [&](int cc) {  // F2: S^T = K Q^T for one 32-key chunk
                 f32x16 S = zero_vec<f32x16>();
-                const int row = kg * C::KH + 32 * cc + c32;
+                const int row = kg * KH + 32 * cc + c32;
                 const char *krow = sk + row * C::ROW;
 #pragma unroll
                 for (int kk = 0; kk < C::NKK; ++kk) {
@@ -268,7 +276,7 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
             };
             f32x16 S = qk(0);
 #pragma unroll
-            for (int cc = 0; cc < C::NS; ++cc) {
+            for (int cc = 0; cc < NS; ++cc) {
                 const int kc0 = kw0 + 32 * cc;
                 // F3: mask chunks that cross the tail or the diagonal.
                 if (kc0 + 32 > kv_hi || (causal && kc0 + 31 > wrow_lo)) {
@@ -295,7 +303,7 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
                 }
                 const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
                 f32x16 Sn;
-                if (cc + 1 < C::NS) Sn = qk(cc + 1);
+                if (cc + 1 < NS) Sn = qk(cc + 1);
                 float ps[4];
                 vec8 P[2];
 #pragma unroll
@@ -312,7 +320,7 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
                 // holds keys 32 cc + 16 hf + 8 x + 4 g + 0..3 (x = 0, 1).
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
-                    const int r0 = kg * C::KH + 32 * cc + 16 * hf + 4 * g + ((lane & 15) >> 2);
+                    const int r0 = kg * KH + 32 * cc + 16 * hf + 4 * g + ((lane & 15) >> 2);
                     const int cq = lane & 3, hh = (lane >> 4) & 1;
 #pragma unroll
                     for (int dt = 0; dt < C::NDT; ++dt) {
@@ -323,38 +331,57 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
                         U[dt] = Half8<T>::mma(a, P[hf], U[dt]);
                     }
                 }
-                if (cc + 1 < C::NS) S = Sn;
+                if (cc + 1 < NS) S = Sn;
             }
         }
     }
     __syncthreads();  // every wave is done with the last stage
 
-    // F7: merge the two key halves of each row, then O = U / l.
+    // F7: merge the KG key groups of each row, then O = U / l.  Groups 1..KG-1
+    // leave (m_ref, m_true, l) and U in LDS; group 0 rescales all KG states to
+    // the largest reference M and sums them in a fixed order.
     l_run += __shfl_xor(l_run, 32);
-    float *st = reinterpret_cast<float *>(smem);           // 4 x 3 x 64 floats
-    f32x4 *su = reinterpret_cast<f32x4 *>(smem + 4096);    // (rg, D/8, 64) float4
-    if (kg == 1) {
-        st[(rg * 3 + 0) * 64 + lane] = m_ref;
-        st[(rg * 3 + 1) * 64 + lane] = m_true;
-        st[(rg * 3 + 2) * 64 + lane] = l_run;
+    float *st = reinterpret_cast<float *>(smem);           // (8 waves, 3, 64) floats
+    f32x4 *su = reinterpret_cast<f32x4 *>(smem + 8192);    // (8 waves, D/8, 64) float4
+    if (kg != 0) {
+        st[(wave * 3 + 0) * 64 + lane] = m_ref;
+        st[(wave * 3 + 1) * 64 + lane] = m_true;
+        st[(wave * 3 + 2) * 64 + lane] = l_run;
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 f32x4 v = {U[dt][4 * j], U[dt][4 * j + 1], U[dt][4 * j + 2], U[dt][4 * j + 3]};
-                su[(rg * (D / 8) + dt * 4 + j) * 64 + lane] = v;
+                su[((wave - RG) * (D / 8) + dt * 4 + j) * 64 + lane] = v;
             }
     }
     __syncthreads();
     if (kg == 0) {
-        const float m1 = st[(rg * 3 + 0) * 64 + lane];
-        const float t1 = st[(rg * 3 + 1) * 64 + lane];
-        const float l1 = st[(rg * 3 + 2) * 64 + lane];
-        const float M_raw = fmaxf(m_ref, m1);
+        float M_raw = m_ref, mt = m_true;
+#pragma unroll
+        for (int k = 1; k < KG; ++k) {
+            M_raw = fmaxf(M_raw, st[((rg + RG * k) * 3 + 0) * 64 + lane]);
+            mt = fmaxf(mt, st[((rg + RG * k) * 3 + 1) * 64 + lane]);
+        }
         const float M = (M_raw == kNegInf) ? 0.f : M_raw;
-        const float a0 = fast_exp2((m_ref - M) * c), a1 = fast_exp2((m1 - M) * c);
-        const float l = l_run * a0 + l1 * a1;
-        const float mt = fmaxf(m_true, t1);
+        const float a0 = fast_exp2((m_ref - M) * c);
+        float l = l_run * a0;
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) U[dt] *= a0;
+#pragma unroll
+        for (int k = 1; k < KG; ++k) {
+            const int w = rg + RG * k;
+            const float ak = fast_exp2((st[(w * 3 + 0) * 64 + lane] - M) * c);
+            l += st[(w * 3 + 2) * 64 + lane] * ak;
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 u = su[((w - RG) * (D / 8) + dt * 4 + j) * 64 + lane];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) U[dt][4 * j + e] = fmaf(u[e], ak, U[dt][4 * j + e]);
+                }
+        }
         if (split >= 0 && qrow < q_hi) {
             // Partial state of this key range: U and l against reference M_raw.
             float *prow = p.part + (((int64_t)split * p.H + h) * p.n_q + qrow) * (D + 4);
@@ -362,10 +389,7 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
             for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const f32x4 u1 = su[(rg * (D / 8) + dt * 4 + j) * 64 + lane];
-                    f32x4 val;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) val[e] = U[dt][4 * j + e] * a0 + u1[e] * a1;
+                    const f32x4 val = {U[dt][4 * j], U[dt][4 * j + 1], U[dt][4 * j + 2], U[dt][4 * j + 3]};
                     *reinterpret_cast<f32x4 *>(prow + 32 * dt + 8 * j + 4 * g) = val;
                 }
             if (g == 0) {
@@ -374,16 +398,13 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
             }
         } else if (qrow < q_hi) {
             const float inv = 1.f / l;
-            const float f0 = a0 * inv, f1 = a1 * inv;
             float *orow = p.o + (int64_t)h * p.o_sh + (int64_t)qrow * p.o_sn;
 #pragma unroll
             for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const f32x4 u1 = su[(rg * (D / 8) + dt * 4 + j) * 64 + lane];
-                    f32x4 val;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) val[e] = U[dt][4 * j + e] * f0 + u1[e] * f1;
+                    const f32x4 val = {U[dt][4 * j] * inv, U[dt][4 * j + 1] * inv,
+                                       U[dt][4 * j + 2] * inv, U[dt][4 * j + 3] * inv};
                     *reinterpret_cast<f32x4 *>(orow + 32 * dt + 8 * j + 4 * g) = val;
                 }
             if (g == 0) {
@@ -533,10 +554,12 @@ __global__ void __launch_bounds__(kSchedThreads) varlen_schedule_kernel(FwdParam
     for (int i = count + tid; i < p.sched_max; i += kSchedThreads) items[i] = make_int4(0, 0, -1, -1);
 }
 
-template <typename T, int D, int MASK, int NST>
+template <typename T, int D, int MASK, int NST, int RG>
 __global__ void __launch_bounds__(kT16) fwd16_kernel(FwdParams p) {
     constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
     constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
+    constexpr int TR = 32 * RG;  // query rows per tile
+    static_assert(!varlen || TR == kBR, "varlen tiles are kBR rows");
     __shared__ __attribute__((aligned(16))) char smem[NST * Fwd16Cfg<D, NST>::STAGE];
     const int b = blockIdx.x;
     if (!causal && !varlen && p.splits > 1) {
@@ -545,9 +568,9 @@ __global__ void __launch_bounds__(kT16) fwd16_kernel(FwdParams p) {
         const int items = p.H * p.n_tiles;
         const int split = b / items, r = b % items;
         const int h = r % p.H, tile = r / p.H;
-        const int q_lo = tile * kBR, q_hi = min(q_lo + kBR, p.n_q);
+        const int q_lo = tile * TR, q_hi = min(q_lo + TR, p.n_q);
         const int k_lo = split * p.split_len, k_hi = min(k_lo + p.split_len, p.n_k);
-        fwd16_tile<T, D, MASK, NST>(p, smem, h, q_lo, q_hi, k_lo, k_hi, split);
+        fwd16_tile<T, D, MASK, NST, RG>(p, smem, h, q_lo, q_hi, k_lo, k_hi, split);
         return;
     }
     const int h = b % p.H;
@@ -558,9 +581,9 @@ __global__ void __launch_bounds__(kT16) fwd16_kernel(FwdParams p) {
         for (int k = 0; k < 2; ++k) {
             const int tile = k == 0 ? it.z : it.w;
             if (tile < 0) break;
-            const int q_lo = it.x + tile * kBR, q_hi = min(q_lo + kBR, it.y);
+            const int q_lo = it.x + tile * TR, q_hi = min(q_lo + TR, it.y);
             if (q_lo >= q_hi) break;
-            fwd16_tile<T, D, MASK, NST>(p, smem, h, q_lo, q_hi, it.x, causal ? q_hi : it.y, -1);
+            fwd16_tile<T, D, MASK, NST, RG>(p, smem, h, q_lo, q_hi, it.x, causal ? q_hi : it.y, -1);
         }
         return;
     }
@@ -570,11 +593,17 @@ __global__ void __launch_bounds__(kT16) fwd16_kernel(FwdParams p) {
         rest /= p.num_seqs;
         seq_lo = s.lo;
         seq_hi = s.hi;
-        ntile = (seq_hi - seq_lo + kBR - 1) / kBR;
+        ntile = (seq_hi - seq_lo + TR - 1) / TR;
     }
     int t0, t1;
-    if (causal || varlen) {
-        // pair (T-1-i, i); varlen pairs are issued longest sequences first
+    if (causal && !varlen && !p.pair) {
+        // one tile per workgroup, heaviest (last) tiles first: for grids too
+        // small to fill the device, where a pair would double the serial work
+        t0 = p.n_tiles - 1 - rest;
+        t1 = -1;
+    } else if (causal || varlen) {
+        // pair (T-1-i, i): equal work per causal pair; the varlen grid walks
+        // i downwards from the middle tiles of the longest sequence
         const int pairs_max = (p.n_tiles + 1) / 2;
         const int i = varlen ? pairs_max - 1 - rest : rest;
         if (i >= (ntile + 1) / 2) return;
@@ -588,9 +617,9 @@ __global__ void __launch_bounds__(kT16) fwd16_kernel(FwdParams p) {
     for (int k = 0; k < 2; ++k) {
         const int tile = k == 0 ? t0 : t1;
         if (tile < 0) break;
-        const int q_lo = seq_lo + tile * kBR, q_hi = min(q_lo + kBR, seq_hi);
+        const int q_lo = seq_lo + tile * TR, q_hi = min(q_lo + TR, seq_hi);
         const int kv_hi = causal ? q_hi : (varlen ? seq_hi : p.n_k);
-        fwd16_tile<T, D, MASK, NST>(p, smem, h, q_lo, q_hi, seq_lo, kv_hi, -1);
+        fwd16_tile<T, D, MASK, NST, RG>(p, smem, h, q_lo, q_hi, seq_lo, kv_hi, -1);
     }
 }
 
@@ -698,18 +727,33 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) fwd32_kernel(FwdPar
 }
 
 // ------------------------------------------------------------------ launch
+template <typename T, int D, int MASK>
+static void launch_fwd16(const FwdParams &p, int grid, hipStream_t st) {
+    const dim3 g(grid), b(kT16);
+    if constexpr (MASK == kDense || MASK == kCausal) {
+        if (p.tile_rows == 64) {
+            hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 2>), g, b, 0, st, p);
+            return;
+        }
+        if constexpr (D == 64) {
+            if (p.tile_rows == 32) {
+                hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 1>), g, b, 0, st, p);
+                return;
+            }
+        }
+    }
+    hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 4>), g, b, 0, st, p);
+}
+
 template <int MASK>
 static void launch_fwd_mask(int dtype, int d, const FwdParams &p, int grid16, int grid32,
                             hipStream_t st) {
-    const dim3 g16(grid16), b16(kT16);
-    if (dtype == 1 || dtype == 2) {
-        if (dtype == 1) {
-            if (d == 64) hipLaunchKernelGGL((fwd16_kernel<_Float16, 64, MASK, 2>), g16, b16, 0, st, p);
-            else hipLaunchKernelGGL((fwd16_kernel<_Float16, 128, MASK, 2>), g16, b16, 0, st, p);
-        } else {
-            if (d == 64) hipLaunchKernelGGL((fwd16_kernel<__bf16, 64, MASK, 2>), g16, b16, 0, st, p);
-            else hipLaunchKernelGGL((fwd16_kernel<__bf16, 128, MASK, 2>), g16, b16, 0, st, p);
-        }
+    if (dtype == 1) {
+        if (d == 64) launch_fwd16<_Float16, 64, MASK>(p, grid16, st);
+        else launch_fwd16<_Float16, 128, MASK>(p, grid16, st);
+    } else if (dtype == 2) {
+        if (d == 64) launch_fwd16<__bf16, 64, MASK>(p, grid16, st);
+        else launch_fwd16<__bf16, 128, MASK>(p, grid16, st);
     } else {
         if (d == 64) hipLaunchKernelGGL((fwd32_kernel<64, 64, MASK>), dim3(grid32), dim3(kThreads), 0, st, p);
         else hipLaunchKernelGGL((fwd32_kernel<128, 32, MASK>), dim3(grid32), dim3(kThreads), 0, st, p);
@@ -721,13 +765,19 @@ hipError_t launch_forward(int dtype, int d, int mask, FwdParams p, int max_seqle
                           hipStream_t st) {
     const bool varlen = mask >= kVarlen, causal = mask == kCausal || mask == kVarlenCausal;
     const int rows = varlen ? max_seqlen : p.n_q;
-    p.n_tiles = (rows + kBR - 1) / kBR;
+    // 16-bit tiles are p.tile_rows (128, or 64 / 32 for small dense and causal
+    // problems); f32 tiles are kBR.
+    if (dtype == 0 || varlen || (p.tile_rows != 64 && p.tile_rows != 32)) p.tile_rows = kBR;
+    if (d != 64 && p.tile_rows == 32) p.tile_rows = 64;
+    p.n_tiles = (rows + p.tile_rows - 1) / p.tile_rows;
     const int64_t seqs = varlen ? p.num_seqs : 1;
     // f32 kernel: one workgroup per (head, sequence, tile).
     const int64_t grid32 = (int64_t)p.n_tiles * p.H * seqs;
     // 16-bit kernel: tile pairs for causal / varlen, single tiles otherwise.
-    const int64_t grid16 = (int64_t)((causal || varlen) ? (p.n_tiles + 1) / 2 : p.n_tiles) * p.H *
-                           seqs * ((causal || varlen) ? 1 : p.splits);
+    if (!causal || varlen) p.pair = varlen ? 1 : 0;
+    const bool paired = p.pair != 0;
+    const int64_t grid16 = (int64_t)(paired ? (p.n_tiles + 1) / 2 : p.n_tiles) * p.H * seqs *
+                           ((causal || varlen) ? 1 : p.splits);
     if (grid32 <= 0) return hipSuccess;
     if (grid32 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     int64_t g16 = grid16;

@@ -102,6 +102,8 @@ int device_cus() {
 // ran 15 us unsplit vs 9 + 8 us split.
 struct FwdPlan {
     int n_tiles, splits, split_len;
+    int tile_rows;               // query rows per 16-bit tile
+    int pair;                    // causal: two tiles (T-1-i, i) per workgroup
     int sched_max, sched_shift;  // varlen work list (0: none)
     size_t total;                // workspace bytes (0: none used)
 };
@@ -136,6 +138,23 @@ FwdPlan plan_forward(int dtype, int H, int64_t n_q, int64_t n_k, int d, int caus
         }
     }
     if (pl.splits > 1) pl.total = round256((size_t)pl.splits * H * n_q * (d + 4) * sizeof(float));
+    // Small dense / causal problems whose 128-row tiles (pairs, causal) would
+    // not occupy half the device use 64- or 32-row tiles: the workgroup's 8
+    // waves then split each key block 4 or 8 ways instead of 2, so more
+    // workgroups each scan the keys with more waves per row.
+    // Causal tiles are paired (T-1-i, i) so that every workgroup does equal
+    // work, unless the 128-row tiles alone cannot fill the device: then each
+    // workgroup takes one tile, heaviest first, to keep the serial chain short.
+    pl.tile_rows = 128;
+    pl.pair = causal && (int64_t)H * ((n_q + 127) / 128) >= device_cus();
+    if (dtype != OSATTN_F32 && !cu && pl.splits == 1) {
+        const int64_t half = device_cus() / 2;
+        const auto items = [&](int64_t tr) {
+            const int64_t t = (n_q + tr - 1) / tr;
+            return (int64_t)H * (pl.pair ? (t + 1) / 2 : t);
+        };
+        while (pl.tile_rows > (d == 64 ? 32 : 64) && items(pl.tile_rows) < half) pl.tile_rows /= 2;
+    }
     // n == S * max_seqlen means every sequence has max_seqlen tokens: the natural
     // grid is then balanced already and the list would only add a launch.
     if (dtype != OSATTN_F32 && cu && num_seqs > 0 && max_seqlen > 0 &&
@@ -269,6 +288,8 @@ int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
     p.scale_log2 = scale * 1.4426950408889634f;
     p.splits = 1;
     p.split_len = (int)n_k;
+    p.tile_rows = 128;
+    p.pair = 1;
     const FwdPlan pl = plan_forward(dtype, H, n_q, n_k, d, causal, cu_seqlens, num_seqs, max_seqlen);
     if (pl.total > 0 && workspace && workspace_bytes >= pl.total) {
         if (reinterpret_cast<uintptr_t>(workspace) & 255u)
@@ -284,6 +305,8 @@ int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
             p.sched_shift = pl.sched_shift;
         }
     }
+    if (p.splits == 1) p.tile_rows = pl.tile_rows;
+    p.pair = pl.pair;
     const hipError_t e = launch_forward(dtype, d, mask_kind(causal, cu_seqlens), p, max_seqlen,
                                         static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(OSATTN_ERR_HIP, "forward launch: %s", hipGetErrorString(e));

@@ -292,3 +292,26 @@ def test_varlen_work_list_matches_natural_order(osattn, oracle, dtype, D, causal
                                      cu_seqlens=inp.cu_seqlens[:n_seq + 1])
         assert_fwd_close(host(a[0]), host(a[1]), host(a[2]), ro, rm, rl, dtype,
                          "work list %s D=%d causal=%s seqs=%d" % (dtype, D, causal, n_seq))
+
+
+# ------------------------------------------------------------ tile sizes
+# The 16-bit dense / causal forward uses 128-row tiles unless those (causal:
+# tile pairs, when paired) number fewer than half the compute units (128 on
+# MI355X); it then halves the tile to 64 and, for D = 64, to 32 rows.  Causal
+# tiles are paired only when H * ceil(n / 128) fills the device.  These shapes
+# select each variant on a 256-CU device.
+TILE_CASES = [  # (causal, H, n_q, n_k, tile rows selected at D = 64)
+    (False, 16, 1100, 333, 128), (False, 8, 1100, 333, 64), (False, 2, 700, 1500, 32),
+    (True, 32, 1000, 1000, 128),  # paired
+    (True, 16, 1000, 1000, 128), (True, 8, 1000, 1000, 64), (True, 2, 777, 777, 32),
+]
+
+
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128), ("bf16", 64), ("f16", 128)])
+@pytest.mark.parametrize("causal,H,n_q,n_k,rows", TILE_CASES)
+def test_fwd_tile_sizes(osattn, oracle, dtype, D, causal, H, n_q, n_k, rows):
+    inp = W.make_inputs(small("t", H, n_q, n_k, D, dtype, causal, 5000 + H + n_q))
+    o, m, l = run_fwd(osattn, inp, causal)
+    ro, rm, rl = oracle.attn_fwd(inp.q32, inp.k32, inp.v32, inp.w.softmax_scale, causal=causal)
+    assert_fwd_close(o, m, l, ro, rm, rl, dtype,
+                     "%s D=%d causal=%s H=%d %dx%d (%d-row tiles)" % (dtype, D, causal, H, n_q, n_k, rows))
