@@ -232,8 +232,8 @@ def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True):
     # duration, from HIP events around replays of a graph of back-to-back
     # forward launches on the launch stream.
     kern = "fwd16_kernel" if w.dtype != "f32" else "fwd32_kernel"
-    if fws_bytes:
-        kern += "+fwd_combine_kernel"
+    if fws_bytes:  # varlen work list before, or split-KV combine after, the forward
+        kern = ("varlen_schedule_kernel+" + kern) if w.lengths else (kern + "+fwd_combine_kernel")
     n_per, reps = 50, 10
     g_fwd = capture(fwd, n_per, torch, stream)
     with torch.cuda.stream(stream):
