@@ -1,5 +1,5 @@
-// Forward attention kernels for gfx950: one fused pass per 128-row query tile
-// that scans key/value blocks with the online-softmax recurrence.
+// Forward attention kernels for gfx950: one fused pass per query tile that
+// scans key/value blocks with the online-softmax recurrence.
 //
 // Method: OCANNL "Module Ir.Online_softmax", fourth rewrite bullet (the block
 // fold): per key block the score tile (contraction, scale, mask), the new row
@@ -9,17 +9,19 @@
 // tail whose scores are -inf.  Relations: TIGA-lang "Attention and dense
 // relations" (dense, causal j <= i, varlen block-diagonal with cu_seqlens).
 //
-// Work decomposition (MI355X): a workgroup of 4 waves owns 128 query rows of
-// one head (32 per wave).  Each wave computes the transposed score tile
-// S^T = K Q^T on MFMA so that every lane owns ONE query row: the row maximum
-// and row sum are in-lane reductions plus a single exchange between the two
-// lane halves, and the rescale of U by alpha is a per-lane multiply.  Q lives
-// in registers for the whole scan; K and V blocks are staged through LDS
-// (V transposed, for the 16-bit types) with coalesced 16-byte global loads that
-// are prefetched into registers one block ahead.  Workgroup index order puts
-// the head index fastest, so the round-robin dispatch over the 8 XCDs keeps
-// each head's K/V on one XCD's L2 when H is a multiple of 8, and causal tiles
-// are issued heaviest first.
+// Work decomposition (MI355X).  fp16/bf16: a workgroup of 8 waves owns a tile
+// of 32 RG query rows of one head (RG row groups x 8/RG key groups, 128 rows by
+// default).  Each wave computes the transposed score tile S^T = K Q^T on MFMA so
+// that every lane owns ONE query row: the row maximum and row sum are in-lane
+// reductions plus one exchange between the two lane halves, and the rescale of U
+// is a per-lane multiply.  Q lives in registers for the whole scan; K and V
+// blocks go HBM/L2 -> LDS by buffer-load DMA, two stages deep, and V reaches the
+// MFMA through the transposing LDS read.  The key groups of a row merge through
+// LDS at the end.  f32: 4 waves own 128 rows with the 32x32x2 f32 MFMA and
+// register-staged K/V.  Workgroup index order puts the head index fastest, so the
+// round-robin dispatch over the 8 XCDs keeps each head's K/V on one XCD's L2 when
+// H is a multiple of 8; causal tiles are paired (T-1-i, i) for equal work, and
+// varlen tiles can follow a sorted work list (see the schedule kernel).
 #include "attn_device.h"
 
 namespace osattn {
@@ -128,11 +130,12 @@ __device__ __forceinline__ void fwd_epilogue(const FwdParams &p, const FwdWork &
 // v_mfma_f32_32x32x16_{f16,bf16}, f32 accumulation; P is rounded to T (RNE) as
 // the operand of the P.V product while the row sum takes the f32 P.
 //
-// A workgroup of 8 waves owns one 128-row query tile at a time: wave w serves
-// rows 32 (w & 3) .. +32 and key half w >> 2 of every key block, so two waves
-// per SIMD overlap one's exponentials with the other's MFMAs.  The two halves
-// keep separate running states (m, l, U) that are merged through LDS once per
-// tile with the same combine rule the recurrence uses between blocks.
+// A workgroup of 8 waves owns one query tile at a time (128 rows by default):
+// with RG row groups, wave w serves rows 32 (w % RG) .. +32 and key group w / RG
+// of every key block, so two waves per SIMD overlap one's exponentials with the
+// other's MFMAs.  The key groups keep separate running states (m, l, U) that
+// are merged through LDS once per tile with the same combine rule the
+// recurrence uses between blocks.
 //
 // K and V blocks travel HBM/L2 -> LDS by buffer_load ... lds (no staging
 // registers), double-buffered with one barrier per block; the buffer range
