@@ -30,6 +30,7 @@ import argparse
 import glob
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -58,12 +59,23 @@ def bwd_flops(w) -> float:
     return 2.5 * fwd_flops(w)
 
 
+_COMMENT_OR_STRING = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'', re.S)
+
+
+def _code_only(text: str) -> str:
+    """C/C++/HIP source with comments removed and whitespace collapsed."""
+    text = _COMMENT_OR_STRING.sub(lambda m: " " if m.group(0).startswith("/") else m.group(0), text)
+    return " ".join(text.split())
+
+
 def kernel_source_sha() -> str:
+    """Hash of the kernel sources' code (comments and layout ignored): recorded
+    counters are reported only while the code they were taken on is unchanged."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "online_softmax_attention_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
+        with open(p, encoding="utf-8") as f:
             h.update(os.path.basename(p).encode())
-            h.update(f.read())
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
