@@ -53,6 +53,25 @@ __device__ __forceinline__ f32x16 mma_f32(float a, float b, f32x16 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max(a, b) as v_maximum*_f32 (NaN-propagating): unlike fmaxf it needs no
+// quieting of its inputs, and three-input chains fuse into v_maximum3_f32.
+// The kernels' scores are finite or -inf, where the two agree.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// The value of lane l ^ 32 combined with lane l's own, through gfx950's
+// v_permlane32_swap (no LDS round trip).  After swapping the upper half of
+// one copy of x with the lower half of another, each lane holds x[l] in one
+// result and x[l ^ 32] in the other, in an order that depends on the half;
+// max and sum are symmetric in the pair.
+__device__ __forceinline__ float xor32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <typename V> __device__ __forceinline__ V zero_vec() {
     V z;
     for (int i = 0; i < (int)(sizeof(V) / sizeof(z[0])); ++i) z[i] = 0;

@@ -291,13 +291,13 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
                 float t[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    t[i] = fmaxf(fmaxf(S[4 * i], S[4 * i + 1]), fmaxf(S[4 * i + 2], S[4 * i + 3]));
-                float mx = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                m_true = fmaxf(m_true, mx);
+                    t[i] = vmax(vmax(S[4 * i], S[4 * i + 1]), vmax(S[4 * i + 2], S[4 * i + 3]));
+                float mx = vmax(vmax(t[0], t[1]), vmax(t[2], t[3]));
+                mx = xor32_max(mx);
+                m_true = vmax(m_true, mx);
                 // F5 (lazy): move the exponent reference only on a large increase.
                 if (__any((mx - m_ref) * c > kLazyLog2)) {
-                    const float m_new = fmaxf(m_ref, mx);
+                    const float m_new = vmax(m_ref, mx);
                     const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_ref - m_new) * c);
 #pragma unroll
                     for (int dt = 0; dt < C::NDT; ++dt) U[dt] *= alpha;
@@ -343,7 +343,7 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
     // F7: merge the KG key groups of each row, then O = U / l.  Groups 1..KG-1
     // leave (m_ref, m_true, l) and U in LDS; group 0 rescales all KG states to
     // the largest reference M and sums them in a fixed order.
-    l_run += __shfl_xor(l_run, 32);
+    l_run = xor32_sum(l_run);
     float *st = reinterpret_cast<float *>(smem);           // (8 waves, 3, 64) floats
     f32x4 *su = reinterpret_cast<f32x4 *>(smem + 8192);    // (8 waves, D/8, 64) float4
     if (kg != 0) {
@@ -363,8 +363,8 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
         float M_raw = m_ref, mt = m_true;
 #pragma unroll
         for (int k = 1; k < KG; ++k) {
-            M_raw = fmaxf(M_raw, st[((rg + RG * k) * 3 + 0) * 64 + lane]);
-            mt = fmaxf(mt, st[((rg + RG * k) * 3 + 1) * 64 + lane]);
+            M_raw = vmax(M_raw, st[((rg + RG * k) * 3 + 0) * 64 + lane]);
+            mt = vmax(mt, st[((rg + RG * k) * 3 + 1) * 64 + lane]);
         }
         const float M = (M_raw == kNegInf) ? 0.f : M_raw;
         const float a0 = fast_exp2((m_ref - M) * c);
