@@ -43,8 +43,8 @@
  *  - Row strides: stride_n * element size must be <= 4 MiB for q and k/v
  *    (OSATTN_ERR_UNSUPPORTED otherwise).
  *  - Supported feature widths: d = 64 or 128 for the forward (any dtype);
- *    d = 64 with dtype f32 for the backward.  Other combinations return
- *    OSATTN_ERR_UNSUPPORTED.
+ *    for the backward d = 64 or 128 with fp16/bf16 and d = 64 with f32.
+ *    Other combinations return OSATTN_ERR_UNSUPPORTED.
  *  - scale must be finite and > 0 (OSATTN_ERR_UNSUPPORTED otherwise).
  *  - causal != 0 selects j <= i; without cu_seqlens it needs n_q == n_k.
  *  - Varlen: cu_seqlens != NULL selects block-diagonal attention over
@@ -150,7 +150,9 @@ size_t osattn_bwd_workspace_bytes(int dtype, int H, int64_t n_q, int64_t n_k, in
  *   dS_ij = P_ij (<dO_i, v_j> - D_i)
  *   dQ_i = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i
  * o, m, l are the forward's outputs for the same q, k, v, scale and mask.
- * dq uses the q strides, dk and dv the k/v strides; all are written in full.
+ * dq uses the q strides, dk and dv the k/v strides; all are written in full,
+ * in the input dtype (fp16/bf16 gradients are f32 sums rounded to nearest
+ * even once at the end).
  * workspace (device, 256-byte aligned) must hold at least
  * osattn_bwd_workspace_bytes(...) bytes; its contents on entry are ignored.
  * No atomics are used: repeated calls give bit-identical gradients.

@@ -1,0 +1,594 @@
+// Backward attention kernels for gfx950, fp16/bf16 inputs, feature width 64 or
+// 128 (v_mfma_f32_32x32x16_{f16,bf16}, f32 accumulation).
+//
+// Method: OCANNL "Module Ir.Online_softmax", third rewrite bullet (the fused
+// backward): a per-row D = sum(dO * O), then nests that recompute each pair's
+// p, dp and ds = p * (dp - D) from the forward's row state -- one over the
+// query rows accumulating dQ, one over the keys accumulating dK and dV -- each
+// owning what it writes.  The mask and the scale act on ds only.  No
+// (N_q, N_k) buffer exists at any point.
+//
+// Row state.  The pre-pass folds m and l into one base-2 offset per row,
+// beta = m log2(e) + log2(l), so that p = 2^(s c - beta) with c = scale log2(e)
+// (one exponential, no division), next to D.
+//
+// Kernels (one stream):
+//   bwd16_pre  : D_i, beta_i                                             (B0)
+//   bwd16_dkdv : a workgroup owns 128 keys, resident in LDS; its 8 waves are
+//                4 key groups of 32 keys x 2 query halves, and scan blocks of
+//                queries whose Q, dO, beta and D arrive by LDS DMA, two stages
+//                deep.  Per 32-query chunk: S = Q K^T, dP = dO V^T (row
+//                operands, ds_read_b128), P, dS, then dV^T += dO^T P and
+//                dK^T += Q^T dS with the transposed operands read by
+//                ds_read_b64_tr_b16; every lane owns one key column.  The two
+//                query halves merge through LDS at the end.              (B1)
+//   bwd16_dq   : a workgroup owns 128 queries (4 row groups x 2 key halves,
+//                one query column per lane) and scans key blocks whose K and V
+//                arrive by LDS DMA: S^T = K Q^T, dP^T = V dO^T, P^T, dS^T,
+//                dQ^T += K^T dS^T with K^T read transposed.              (B2)
+//   reduce     : sums the f32 partials of a split reduction in a fixed order
+//                and rounds to the gradient dtype (no atomics).
+// Tiles read both as MFMA rows and transposed use the swz_rt swizzle; tiles
+// read only as rows use swz_k.
+#include "attn_device.h"
+
+namespace osattn {
+
+constexpr int kB16T = 512;  // threads per workgroup (8 waves)
+
+template <int D>
+struct Bwd16Cfg {
+    static constexpr int ROW = D * 2;   // bytes per 16-bit row
+    static constexpr int NKK = D / 16;  // 16-feature slices of the contraction
+    static constexpr int NDT = D / 32;  // 32-feature accumulator tiles
+    // dQ pass: key blocks of BC keys, K and V double-buffered.
+    static constexpr int BC = D == 64 ? 256 : 128;
+    static constexpr int KH = BC / 2, NSQ = KH / 32;
+    static constexpr int KTILE = BC * ROW;
+    static constexpr int KSTAGE = 2 * KTILE;
+    static constexpr int NDMA_Q = KTILE / (kB16T * 16);
+    // dK/dV pass: BK resident keys, query blocks of BQ double-buffered.
+    static constexpr int BK = 128;
+    static constexpr int BQ = D == 64 ? 128 : 64;
+    static constexpr int QH = BQ / 2, NSK = QH / 32;
+    static constexpr int QTILE = BQ * ROW;
+    static constexpr int QSTAGE = 2 * QTILE + 2 * BQ * 4;  // Q, dO, beta, D
+    static constexpr int KVRES = 2 * BK * ROW;             // resident K, V
+    static constexpr int NDMA_K = QTILE / (kB16T * 16);
+    static constexpr int NDMA_KV = BK * ROW / (kB16T * 16);
+    static constexpr int LDS_DQ = 2 * KSTAGE;
+    static constexpr int LDS_DKDV_LOOP = KVRES + 2 * QSTAGE;
+    static constexpr int LDS_DKDV_MERGE = 4 * 2 * NDT * 16 * 64 * 4;
+    static constexpr int LDS_DKDV = LDS_DKDV_LOOP > LDS_DKDV_MERGE ? LDS_DKDV_LOOP : LDS_DKDV_MERGE;
+    static_assert(NDMA_Q * kB16T * 16 == KTILE && NDMA_K * kB16T * 16 == QTILE &&
+                      NDMA_KV * kB16T * 16 == BK * ROW,
+                  "tiles must split evenly over the DMA lanes");
+    static_assert(BQ % 64 == 0, "statistics DMA moves 64 floats per instruction");
+};
+
+// ---------------------------------------------------------------- B0
+template <typename T, int D>
+__global__ void __launch_bounds__(256) bwd16_pre_kernel(BwdParams p) {
+    constexpr int PER = D / 16;  // features per thread; 16 threads per row
+    const int64_t total = (int64_t)p.H * p.n_q;
+    const int64_t row = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
+    const int sub = threadIdx.x % 16;
+    float acc = 0.f;
+    if (row < total) {
+        const int h = (int)(row / p.n_q), i = (int)(row % p.n_q);
+        const T *dorow = static_cast<const T *>(p.d_o) + (int64_t)h * p.q_sh + (int64_t)i * p.q_sn;
+        const float *orow = p.o + (int64_t)h * p.o_sh + (int64_t)i * p.o_sn;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc += (float)dorow[sub * PER + e] * orow[sub * PER + e];
+    }
+    acc += __shfl_xor(acc, 8);
+    acc += __shfl_xor(acc, 4);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 1);
+    if (sub == 0 && row < total) {
+        p.stat_delta[row] = acc;
+        p.stat_mlog2[row] = p.m[row] * kLog2e + __log2f(p.l[row]);  // beta
+    }
+}
+
+struct Range16 {
+    int lo, hi;
+};
+
+template <bool VARLEN>
+__device__ __forceinline__ Range16 axis16(const BwdParams &p, int seq, int n) {
+    if (!VARLEN) return {0, n};
+    const Span s = seq_bounds(p.cu, seq, n);
+    return {s.lo, s.hi};
+}
+
+// Part `split` of [lo, hi) cut into `splits` pieces aligned to `blk`.
+__device__ __forceinline__ Range16 split16(int lo, int hi, int split, int splits, int blk) {
+    const int len = hi > lo ? hi - lo : 0;
+    int chunk = (len + splits - 1) / splits;
+    chunk = (chunk + blk - 1) / blk * blk;
+    const int a = lo + split * chunk;
+    const int b = min(a + chunk, hi);
+    return {a, b > a ? b : a};
+}
+
+// Store a lane's transposed accumulator tiles (feature rows, one position
+// column) as one row of `out`, scaled and rounded to T (or f32 partials).
+template <typename T, int NDT>
+__device__ __forceinline__ void store_row16(T *rowp, const f32x16 (&acc)[NDT], int g, float scale) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            typedef T t4 __attribute__((ext_vector_type(4)));
+            f32x4 v = {acc[dt][4 * j] * scale, acc[dt][4 * j + 1] * scale, acc[dt][4 * j + 2] * scale,
+                       acc[dt][4 * j + 3] * scale};
+            *reinterpret_cast<t4 *>(rowp + 32 * dt + 8 * j + 4 * g) = __builtin_convertvector(v, t4);
+        }
+}
+template <int NDT>
+__device__ __forceinline__ void store_row_part(float *rowp, const f32x16 (&acc)[NDT], int g, float scale) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f32x4 v = {acc[dt][4 * j] * scale, acc[dt][4 * j + 1] * scale, acc[dt][4 * j + 2] * scale,
+                       acc[dt][4 * j + 3] * scale};
+            *reinterpret_cast<f32x4 *>(rowp + 32 * dt + 8 * j + 4 * g) = v;
+        }
+}
+
+// A operand of a transposed product: rows [r0, r0 + 4) and [r0 + 8, r0 + 12)
+// of a row-major 16-bit tile (swz_rt), feature chunk ch, as 8 values per lane.
+template <typename T, int ROW>
+__device__ __forceinline__ typename Half8<T>::vec tr_operand(const char *tile, int r0, int ch, int cq) {
+    const i16x4 lo = lds_read_tr16(tile + r0 * ROW + swz_rt<ROW>(r0, ch) * 16 + 8 * (cq & 1));
+    const i16x4 hi = lds_read_tr16(tile + (r0 + 8) * ROW + swz_rt<ROW>(r0 + 8, ch) * 16 + 8 * (cq & 1));
+    return __builtin_bit_cast(typename Half8<T>::vec, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// ---------------------------------------------------------------- B1
+template <typename T, int D, int MASK>
+__global__ void __launch_bounds__(kB16T) bwd16_dkdv_kernel(BwdParams p) {
+    typedef Bwd16Cfg<D> C;
+    typedef typename Half8<T>::vec vec8;
+    constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
+    constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
+    constexpr int esz = (int)sizeof(T);
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS_DKDV];
+
+    const int b = blockIdx.x;
+    const int h = b % p.H;
+    int rest = b / p.H;
+    const int split = rest % p.k_splits;
+    rest /= p.k_splits;
+    int seq = 0;
+    if (varlen) {
+        seq = rest % p.num_seqs;
+        rest /= p.num_seqs;
+    }
+    // Causal key tiles are issued heaviest (earliest keys: most queries) first.
+    const int ktile = rest;
+    const Range16 ks = axis16<varlen>(p, seq, p.n_k);
+    const Range16 qs_all = axis16<varlen>(p, seq, p.n_q);
+    const int k_lo = ks.lo + ktile * C::BK;
+    if (k_lo >= ks.hi) return;
+    const int k_hi = min(k_lo + C::BK, ks.hi);
+    const int qa = causal ? max(qs_all.lo, k_lo) : qs_all.lo;
+    const Range16 qr = split16(qa, qs_all.hi, split, p.k_splits, C::BQ);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int kq = wave & 3, qg = wave >> 2;  // key group, query half
+    const int c32 = lane & 31, g = lane >> 5;
+    const int key = k_lo + 32 * kq + c32;      // this lane's key column
+    const int kv_sn = (int)p.kv_sn, q_sn = (int)p.q_sn;
+
+    // Resident K and V of the tile (rows past k_hi arrive as zeros).
+    char *sK = smem, *sV = smem + C::BK * C::ROW;
+    {
+        const T *kb = static_cast<const T *>(p.k) + (int64_t)h * p.kv_sh + (int64_t)k_lo * p.kv_sn;
+        const T *vb = static_cast<const T *>(p.v) + (int64_t)h * p.kv_sh + (int64_t)k_lo * p.kv_sn;
+        const int64_t bytes = (int64_t)(k_hi - k_lo) * p.kv_sn * esz;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, bytes), rv = make_rsrc(vb, bytes);
+#pragma unroll
+        for (int i = 0; i < C::NDMA_KV; ++i) {
+            const int byte = (8 * i + wave) * 1024 + 16 * lane;
+            const int row = byte / C::ROW, pch = (byte % C::ROW) / 16;
+            const int off = row * kv_sn * esz + swz_k<C::ROW>(row, pch) * 16;
+            dma16(rk, sK + (8 * i + wave) * 1024, off);
+            dma16(rv, sV + (8 * i + wave) * 1024, off);
+        }
+    }
+
+    // Query block DMA into stage `buf`: Q and dO rows (swz_rt), beta and D.
+    const T *qh = static_cast<const T *>(p.q) + (int64_t)h * p.q_sh;
+    const T *doh = static_cast<const T *>(p.d_o) + (int64_t)h * p.q_sh;
+    const float *bh = p.stat_mlog2 + (int64_t)h * p.n_q;
+    const float *dh = p.stat_delta + (int64_t)h * p.n_q;
+    char *stage0 = smem + C::KVRES;
+    auto issue = [&](int q0, int buf) {
+        char *sq = stage0 + buf * C::QSTAGE;
+        char *sdo = sq + C::QTILE;
+        float *sb = reinterpret_cast<float *>(sdo + C::QTILE);
+        float *sd = sb + C::BQ;
+        const int64_t bytes = (int64_t)(qr.hi - q0) * p.q_sn * esz;
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(qh + (int64_t)q0 * p.q_sn, bytes);
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(doh + (int64_t)q0 * p.q_sn, bytes);
+#pragma unroll
+        for (int i = 0; i < C::NDMA_K; ++i) {
+            const int byte = (8 * i + wave) * 1024 + 16 * lane;
+            const int row = byte / C::ROW, pch = (byte % C::ROW) / 16;
+            const int off = row * q_sn * esz + swz_rt<C::ROW>(row, pch) * 16;
+            dma16(rq, sq + (8 * i + wave) * 1024, off);
+            dma16(rd, sdo + (8 * i + wave) * 1024, off);
+        }
+        // beta and D: waves 0 .. BQ/64 - 1 move 64 floats each per array.
+        if (wave < C::BQ / 64) {
+            const int64_t sbytes = (int64_t)(qr.hi - q0) * 4;
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(bh + q0, sbytes), rdl = make_rsrc(dh + q0, sbytes);
+            dma4(rb, sb + 64 * wave, 4 * (64 * wave + lane));
+            dma4(rdl, sd + 64 * wave, 4 * (64 * wave + lane));
+        }
+    };
+
+    f32x16 dK[C::NDT], dV[C::NDT];
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) {
+        dK[dt] = zero_vec<f32x16>();
+        dV[dt] = zero_vec<f32x16>();
+    }
+    const float c = p.scale_log2;
+    const int nblk = (qr.hi - qr.lo + C::BQ - 1) / C::BQ;
+    const int krow = 32 * kq + c32;  // this lane's row of the resident tiles
+
+    if (nblk > 0) issue(qr.lo, 0);
+    for (int j = 0; j < nblk; ++j) {
+        // Block j (and, for j = 0, the resident K/V) has landed for this
+        // thread, and after the barrier for all; block j-1's stage is free.
+        wait_vmcnt<0>();
+        bare_barrier();
+        if (j + 1 < nblk) issue(qr.lo + (j + 1) * C::BQ, (j + 1) & 1);
+
+        const int q0 = qr.lo + j * C::BQ;
+        const char *sq = stage0 + (j & 1) * C::QSTAGE;
+        const char *sdo = sq + C::QTILE;
+        const float *sb = reinterpret_cast<const float *>(sdo + C::QTILE);
+        const float *sd = sb + C::BQ;
+#pragma unroll
+        for (int cc = 0; cc < C::NSK; ++cc) {
+            const int ql0 = qg * C::QH + 32 * cc;  // chunk's first row in the block
+            const int qc0 = q0 + ql0;
+            if (qc0 >= qr.hi) break;
+            if (causal && k_lo + 32 * kq > qc0 + 31) continue;  // every pair masked
+            // S = Q K^T and dP = dO V^T: rows = the chunk's queries, column =
+            // this lane's key.
+            f32x16 S = zero_vec<f32x16>(), dP = zero_vec<f32x16>();
+            const int qrow = ql0 + c32;
+#pragma unroll
+            for (int kk = 0; kk < C::NKK; ++kk) {
+                const vec8 qa8 = *reinterpret_cast<const vec8 *>(sq + qrow * C::ROW + swz_rt<C::ROW>(qrow, 2 * kk + g) * 16);
+                const vec8 kb8 = *reinterpret_cast<const vec8 *>(sK + krow * C::ROW + swz_k<C::ROW>(krow, 2 * kk + g) * 16);
+                S = Half8<T>::mma(qa8, kb8, S);
+            }
+#pragma unroll
+            for (int kk = 0; kk < C::NKK; ++kk) {
+                const vec8 da8 = *reinterpret_cast<const vec8 *>(sdo + qrow * C::ROW + swz_rt<C::ROW>(qrow, 2 * kk + g) * 16);
+                const vec8 vb8 = *reinterpret_cast<const vec8 *>(sV + krow * C::ROW + swz_k<C::ROW>(krow, 2 * kk + g) * 16);
+                dP = Half8<T>::mma(da8, vb8, dP);
+            }
+            // P = 2^(s c - beta), zero where key > query; dS = P (dP - D).
+            const bool diag = causal && k_lo + 32 * kq + 31 > qc0;
+            f32x16 P, dS;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 bv = *reinterpret_cast<const f32x4 *>(sb + ql0 + 8 * i + 4 * g);
+                const f32x4 dv = *reinterpret_cast<const f32x4 *>(sd + ql0 + 8 * i + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * i + e;
+                    float pv = fast_exp2(fmaf(S[r], c, -bv[e]));
+                    if (diag && key > qc0 + acc_row(r, g)) pv = 0.f;
+                    P[r] = pv;
+                    dS[r] = pv * (dP[r] - dv[e]);
+                }
+            }
+            // dV^T += dO^T P and dK^T += Q^T dS over the chunk's two 16-query
+            // slices; slice hf holds rows 16 hf + 8 x + 4 g + 0..3 (x = 0, 1).
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                f32x8 pp, ss;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    pp[e] = P[8 * hf + e];
+                    ss[e] = dS[8 * hf + e];
+                }
+                const vec8 pb = __builtin_convertvector(pp, vec8);
+                const vec8 sbv = __builtin_convertvector(ss, vec8);
+                const int r0 = ql0 + 16 * hf + 4 * g + ((lane & 15) >> 2);
+                const int cq = lane & 3, hh = (lane >> 4) & 1;
+#pragma unroll
+                for (int dt = 0; dt < C::NDT; ++dt) {
+                    const int ch = 4 * dt + 2 * hh + (cq >> 1);
+                    dV[dt] = Half8<T>::mma(tr_operand<T, C::ROW>(sdo, r0, ch, cq), pb, dV[dt]);
+                    dK[dt] = Half8<T>::mma(tr_operand<T, C::ROW>(sq, r0, ch, cq), sbv, dK[dt]);
+                }
+            }
+        }
+    }
+    __syncthreads();  // every wave is done with the stages and the resident tiles
+
+    // Merge the two query halves: half 1 leaves dK^T, dV^T in LDS.
+    f32x4 *sm = reinterpret_cast<f32x4 *>(smem);  // (4 key groups, 2, D/8, 64) float4
+    if (qg == 1) {
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                f32x4 a = {dK[dt][4 * jj], dK[dt][4 * jj + 1], dK[dt][4 * jj + 2], dK[dt][4 * jj + 3]};
+                f32x4 v = {dV[dt][4 * jj], dV[dt][4 * jj + 1], dV[dt][4 * jj + 2], dV[dt][4 * jj + 3]};
+                sm[((kq * 2 + 0) * (D / 8) + dt * 4 + jj) * 64 + lane] = a;
+                sm[((kq * 2 + 1) * (D / 8) + dt * 4 + jj) * 64 + lane] = v;
+            }
+    }
+    __syncthreads();
+    if (qg != 0 || key >= k_hi) return;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const f32x4 a = sm[((kq * 2 + 0) * (D / 8) + dt * 4 + jj) * 64 + lane];
+            const f32x4 v = sm[((kq * 2 + 1) * (D / 8) + dt * 4 + jj) * 64 + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dK[dt][4 * jj + e] += a[e];
+                dV[dt][4 * jj + e] += v[e];
+            }
+        }
+    if (p.k_splits == 1) {
+        store_row16<T, C::NDT>(static_cast<T *>(p.dk) + (int64_t)h * p.kv_sh + (int64_t)key * p.kv_sn, dK, g, p.scale);
+        store_row16<T, C::NDT>(static_cast<T *>(p.dv) + (int64_t)h * p.kv_sh + (int64_t)key * p.kv_sn, dV, g, 1.f);
+    } else {
+        const int64_t off = (((int64_t)split * p.H + h) * p.n_k + key) * D;
+        store_row_part<C::NDT>(p.dk_part + off, dK, g, p.scale);
+        store_row_part<C::NDT>(p.dv_part + off, dV, g, 1.f);
+    }
+}
+
+// ---------------------------------------------------------------- B2
+template <typename T, int D, int MASK>
+__global__ void __launch_bounds__(kB16T) bwd16_dq_kernel(BwdParams p) {
+    typedef Bwd16Cfg<D> C;
+    typedef typename Half8<T>::vec vec8;
+    constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
+    constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
+    constexpr int esz = (int)sizeof(T);
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS_DQ];
+
+    const int b = blockIdx.x;
+    const int h = b % p.H;
+    int rest = b / p.H;
+    const int split = rest % p.q_splits;
+    rest /= p.q_splits;
+    int seq = 0;
+    if (varlen) {
+        seq = rest % p.num_seqs;
+        rest /= p.num_seqs;
+    }
+    const int qtile = causal ? (p.q_tiles - 1 - rest) : rest;  // causal: heaviest first
+    const Range16 qs_all = axis16<varlen>(p, seq, p.n_q);
+    const Range16 ks_all = axis16<varlen>(p, seq, p.n_k);
+    const int q_lo = qs_all.lo + qtile * 128;
+    if (qtile < 0 || q_lo >= qs_all.hi) return;
+    const int q_hi = min(q_lo + 128, qs_all.hi);
+    const int kv_end = causal ? q_hi : ks_all.hi;
+    const Range16 kr = split16(ks_all.lo, kv_end, split, p.q_splits, C::BC);
+    const int kv_lo = kr.lo, kv_hi = kr.hi;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rg = wave & 3, kg = wave >> 2;
+    const int c32 = lane & 31, g = lane >> 5;
+    const int qrow = q_lo + 32 * rg + c32;
+    const bool qok = qrow < q_hi;
+
+    // This lane's query row of Q and dO as B operands, and its row state.
+    const T *qb = static_cast<const T *>(p.q) + (int64_t)h * p.q_sh + (int64_t)q_lo * p.q_sn;
+    const T *db = static_cast<const T *>(p.d_o) + (int64_t)h * p.q_sh + (int64_t)q_lo * p.q_sn;
+    const int64_t qbytes = (int64_t)(q_hi - q_lo) * p.q_sn * esz;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, qbytes), rdo = make_rsrc(db, qbytes);
+    vec8 qreg[C::NKK], doreg[C::NKK];
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk) {
+        const int off = ((32 * rg + c32) * (int)p.q_sn + 16 * kk + 8 * g) * esz;
+        qreg[kk] = __builtin_bit_cast(vec8, bload16(rq, off));
+        doreg[kk] = __builtin_bit_cast(vec8, bload16(rdo, off));
+    }
+    const int64_t srow = (int64_t)h * p.n_q + qrow;
+    const float beta = qok ? p.stat_mlog2[srow] : 0.f;
+    const float dl = qok ? p.stat_delta[srow] : 0.f;
+
+    const T *kh = static_cast<const T *>(p.k) + (int64_t)h * p.kv_sh;
+    const T *vh = static_cast<const T *>(p.v) + (int64_t)h * p.kv_sh;
+    const int kv_sn = (int)p.kv_sn;
+    auto issue = [&](int k0, int buf) {
+        const int64_t bytes = (int64_t)(kv_hi - k0) * kv_sn * esz;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh + (int64_t)k0 * kv_sn, bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh + (int64_t)k0 * kv_sn, bytes);
+        char *sk = smem + buf * C::KSTAGE;
+        char *sv = sk + C::KTILE;
+#pragma unroll
+        for (int i = 0; i < C::NDMA_Q; ++i) {
+            const int byte = (8 * i + wave) * 1024 + 16 * lane;
+            const int row = byte / C::ROW, pch = (byte % C::ROW) / 16;
+            dma16(rk, sk + (8 * i + wave) * 1024, row * kv_sn * esz + swz_rt<C::ROW>(row, pch) * 16);
+            dma16(rv, sv + (8 * i + wave) * 1024, row * kv_sn * esz + swz_k<C::ROW>(row, pch) * 16);
+        }
+    };
+
+    f32x16 dQ[C::NDT];
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) dQ[dt] = zero_vec<f32x16>();
+    const float c = p.scale_log2;
+    const int nblk = (kv_hi - kv_lo + C::BC - 1) / C::BC;
+    const int wrow_lo = q_lo + 32 * rg, wrow_hi = wrow_lo + 31;
+
+    if (nblk > 0) issue(kv_lo, 0);
+    for (int j = 0; j < nblk; ++j) {
+        wait_vmcnt<0>();
+        bare_barrier();
+        if (j + 1 < nblk) issue(kv_lo + (j + 1) * C::BC, (j + 1) & 1);
+
+        const int k0 = kv_lo + j * C::BC;
+        const int kw0 = k0 + kg * C::KH;
+        const char *sk = smem + (j & 1) * C::KSTAGE;
+        const char *sv = sk + C::KTILE;
+        if (kw0 < kv_hi && (!causal || kw0 <= wrow_hi)) {
+#pragma unroll
+            for (int cc = 0; cc < C::NSQ; ++cc) {
+                const int kc0 = kw0 + 32 * cc;
+                if (kc0 >= kv_hi || (causal && kc0 > wrow_hi)) break;
+                const int row = kg * C::KH + 32 * cc + c32;
+                // S^T = K Q^T and dP^T = V dO^T: rows = the chunk's keys,
+                // column = this lane's query.
+                f32x16 S = zero_vec<f32x16>(), dP = zero_vec<f32x16>();
+#pragma unroll
+                for (int kk = 0; kk < C::NKK; ++kk) {
+                    const vec8 ka = *reinterpret_cast<const vec8 *>(sk + row * C::ROW + swz_rt<C::ROW>(row, 2 * kk + g) * 16);
+                    S = Half8<T>::mma(ka, qreg[kk], S);
+                }
+#pragma unroll
+                for (int kk = 0; kk < C::NKK; ++kk) {
+                    const vec8 va = *reinterpret_cast<const vec8 *>(sv + row * C::ROW + swz_k<C::ROW>(row, 2 * kk + g) * 16);
+                    dP = Half8<T>::mma(va, doreg[kk], dP);
+                }
+                if (kc0 + 32 > kv_hi || (causal && kc0 + 31 > wrow_lo)) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {  // tail keys and keys past the diagonal
+                        const int kk2 = kc0 + acc_row(r, g);
+                        if (kk2 >= kv_hi || (causal && kk2 > qrow)) S[r] = kNegInf;
+                    }
+                }
+                // dS^T = P^T (dP^T - D), P^T = 2^(s c - beta).
+                vec8 dsv[2];
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    f32x8 x;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float pv = fast_exp2(fmaf(S[8 * hf + e], c, -beta));
+                        x[e] = pv * (dP[8 * hf + e] - dl);
+                    }
+                    dsv[hf] = __builtin_convertvector(x, vec8);
+                }
+                // dQ^T += K^T dS^T over the chunk's two 16-key slices.
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int r0 = kg * C::KH + 32 * cc + 16 * hf + 4 * g + ((lane & 15) >> 2);
+                    const int cq = lane & 3, hh = (lane >> 4) & 1;
+#pragma unroll
+                    for (int dt = 0; dt < C::NDT; ++dt) {
+                        const int ch = 4 * dt + 2 * hh + (cq >> 1);
+                        dQ[dt] = Half8<T>::mma(tr_operand<T, C::ROW>(sk, r0, ch, cq), dsv[hf], dQ[dt]);
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // Merge the two key halves: half 1 leaves dQ^T in LDS.
+    f32x4 *sm = reinterpret_cast<f32x4 *>(smem);  // (4 row groups, D/8, 64) float4
+    if (kg == 1) {
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                f32x4 a = {dQ[dt][4 * jj], dQ[dt][4 * jj + 1], dQ[dt][4 * jj + 2], dQ[dt][4 * jj + 3]};
+                sm[(rg * (D / 8) + dt * 4 + jj) * 64 + lane] = a;
+            }
+    }
+    __syncthreads();
+    if (kg != 0 || !qok) return;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const f32x4 a = sm[(rg * (D / 8) + dt * 4 + jj) * 64 + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dQ[dt][4 * jj + e] += a[e];
+        }
+    if (p.q_splits == 1) {
+        store_row16<T, C::NDT>(static_cast<T *>(p.dq) + (int64_t)h * p.q_sh + (int64_t)qrow * p.q_sn, dQ, g, p.scale);
+    } else {
+        const int64_t off = (((int64_t)split * p.H + h) * p.n_q + qrow) * D;
+        store_row_part<C::NDT>(p.dq_part + off, dQ, g, p.scale);
+    }
+}
+
+// ---------------------------------------------------------------- reduce
+template <typename T, int D>
+__global__ void __launch_bounds__(256) bwd16_reduce_kernel(ReduceParams r) {
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    const int64_t total4 = (int64_t)r.H * r.n * D / 4;
+    const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i4 >= total4) return;
+    const int64_t e = i4 * 4;
+    const int64_t plane = (int64_t)r.n * D;
+    const int h = (int)(e / plane);
+    const int64_t rem = e % plane;
+    const int i = (int)(rem / D), d = (int)(rem % D);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int64_t stride = (int64_t)r.H * plane;
+    for (int s = 0; s < r.splits; ++s) acc += *reinterpret_cast<const f32x4 *>(r.part + s * stride + e);
+    *reinterpret_cast<t4 *>(static_cast<T *>(r.out) + (int64_t)h * r.out_sh + (int64_t)i * r.out_sn + d) =
+        __builtin_convertvector(acc, t4);
+}
+
+// ------------------------------------------------------------------ launch
+template <typename T, int D, int MASK>
+static void launch_bwd16_mask(const BwdParams &p, int grid_k, int grid_q, hipStream_t st) {
+    if (grid_k > 0)
+        hipLaunchKernelGGL((bwd16_dkdv_kernel<T, D, MASK>), dim3(grid_k), dim3(kB16T), 0, st, p);
+    if (grid_q > 0)
+        hipLaunchKernelGGL((bwd16_dq_kernel<T, D, MASK>), dim3(grid_q), dim3(kB16T), 0, st, p);
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd16_typed(int mask, const BwdParams &p, int seqs, hipStream_t st) {
+    const int64_t rows = (int64_t)p.H * p.n_q;
+    hipLaunchKernelGGL((bwd16_pre_kernel<T, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t grid_k = (int64_t)p.H * p.k_splits * seqs * p.k_tiles;
+    const int64_t grid_q = (int64_t)p.H * p.q_splits * seqs * p.q_tiles;
+    if (grid_k > 0x7fffffffLL || grid_q > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    switch (mask) {
+        case kDense: launch_bwd16_mask<T, D, kDense>(p, (int)grid_k, (int)grid_q, st); break;
+        case kCausal: launch_bwd16_mask<T, D, kCausal>(p, (int)grid_k, (int)grid_q, st); break;
+        case kVarlen: launch_bwd16_mask<T, D, kVarlen>(p, (int)grid_k, (int)grid_q, st); break;
+        default: launch_bwd16_mask<T, D, kVarlenCausal>(p, (int)grid_k, (int)grid_q, st); break;
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    auto reduce = [&](const float *part, void *out, int64_t sh, int64_t sn, int n, int splits) {
+        ReduceParams r{part, out, sh, sn, p.H, n, splits};
+        const int64_t grid = ((int64_t)p.H * n * D / 4 + 255) / 256;
+        if (grid > 0) hipLaunchKernelGGL((bwd16_reduce_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, st, r);
+    };
+    if (p.k_splits > 1) {
+        reduce(p.dk_part, p.dk, p.kv_sh, p.kv_sn, p.n_k, p.k_splits);
+        reduce(p.dv_part, p.dv, p.kv_sh, p.kv_sn, p.n_k, p.k_splits);
+    }
+    if (p.q_splits > 1) reduce(p.dq_part, p.dq, p.q_sh, p.q_sn, p.n_q, p.q_splits);
+    return hipGetLastError();
+}
+
+// Host entry for fp16/bf16 (dtype 1 / 2), d = 64 or 128 (validated by the ABI).
+hipError_t launch_backward16(int dtype, int d, int mask, BwdParams p, int seqs, hipStream_t st) {
+    if (dtype == 1)
+        return d == 64 ? launch_bwd16_typed<_Float16, 64>(mask, p, seqs, st)
+                       : launch_bwd16_typed<_Float16, 128>(mask, p, seqs, st);
+    return d == 64 ? launch_bwd16_typed<__bf16, 64>(mask, p, seqs, st)
+                   : launch_bwd16_typed<__bf16, 128>(mask, p, seqs, st);
+}
+
+}  // namespace osattn

@@ -119,6 +119,20 @@ __device__ __forceinline__ int swz_vt(int row, int chunk) {
     return ROW_BYTES >= 256 ? (chunk ^ ((row & 3) << 2)) : (chunk ^ (((row >> 1) & 1) << 2));
 }
 
+// Swizzle of a 16-bit tile that is read both ways: as MFMA rows with
+// ds_read_b128 (16 consecutive rows at one logical chunk) and transposed with
+// ds_read_b64_tr_b16 (4 consecutive rows x 2 chunks per 16 lanes).  The XOR
+// mask mixes the low row bits into different chunk bits so that both patterns
+// touch distinct bank groups (checked exhaustively with a 64-bank model):
+// 256-byte rows use ((row & 3) << 2) | ((row >> 2) & 3); 128-byte rows, whose
+// neighbours share the bank half, use bits 1, 2, 3 of the row.
+template <int ROW_BYTES>
+__device__ __forceinline__ int swz_rt(int row, int chunk) {
+    return ROW_BYTES >= 256
+               ? (chunk ^ (((row & 3) << 2) | ((row >> 2) & 3)))
+               : (chunk ^ ((((row >> 1) & 1) << 1) | ((row >> 2) & 1) | (((row >> 3) & 1) << 2)));
+}
+
 #define OSATTN_LDS __attribute__((address_space(3)))
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -135,6 +149,10 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const void *lds_addr) {
 // Past-the-end chunks arrive as zeros.  Completion is counted by vmcnt.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *lds_base, int byte_off) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (OSATTN_LDS void *)(lds_base), 16, byte_off, 0, 0, 0);
+}
+// The same with 4 bytes per lane: lane L writes [lds_base + 4 L, + 4).
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void *lds_base, int byte_off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (OSATTN_LDS void *)(lds_base), 4, byte_off, 0, 0, 0);
 }
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits

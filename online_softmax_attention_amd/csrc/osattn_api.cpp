@@ -13,6 +13,7 @@
 namespace osattn {
 hipError_t launch_forward(int dtype, int d, int mask, FwdParams p, int max_seqlen, hipStream_t st);
 hipError_t launch_backward(int mask, BwdParams p, int seqs, hipStream_t st);
+hipError_t launch_backward16(int dtype, int d, int mask, BwdParams p, int seqs, hipStream_t st);
 }  // namespace osattn
 
 using namespace osattn;
@@ -222,9 +223,11 @@ BwdPlan plan_backward(int H, int64_t n_q, int64_t n_k, int d, const int32_t *cu,
 }
 
 int check_bwd_supported(int dtype, int d) {
-    if (dtype != OSATTN_F32 || d != 64)
+    const bool ok = dtype == OSATTN_F32 ? d == 64 : (d == 64 || d == 128);
+    if (!ok)
         return fail(OSATTN_ERR_UNSUPPORTED,
-                    "backward supports dtype OSATTN_F32 with d = 64 (got dtype %d, d %d)", dtype, d);
+                    "backward supports f32 with d = 64 and fp16/bf16 with d = 64 or 128 "
+                    "(got dtype %d, d %d)", dtype, d);
     return OSATTN_OK;
 }
 
@@ -367,8 +370,10 @@ int osattn_bwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
     p.dv_part = reinterpret_cast<float *>(ws + pl.off_dv);
     p.q_tiles = pl.q_tiles; p.k_tiles = pl.k_tiles;
     p.q_splits = pl.q_splits; p.k_splits = pl.k_splits;
-    const hipError_t e = launch_backward(mask_kind(causal, cu_seqlens), p, pl.seqs,
-                                         static_cast<hipStream_t>(stream));
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int mk = mask_kind(causal, cu_seqlens);
+    const hipError_t e = dtype == OSATTN_F32 ? launch_backward(mk, p, pl.seqs, hs)
+                                             : launch_backward16(dtype, d, mk, p, pl.seqs, hs);
     if (e != hipSuccess) return fail(OSATTN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
     return ok();
 }

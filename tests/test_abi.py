@@ -111,9 +111,11 @@ def bwd(lib, dtype=F32, H=1, n_q=256, n_k=128, d=64, ptrs=None, ws=None, ws_byte
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dtype=F16), osa.ERR_UNSUPPORTED),
-    (dict(d=128), osa.ERR_UNSUPPORTED),
+    (dict(dtype=F16, d=96), osa.ERR_UNSUPPORTED),
+    (dict(d=128), osa.ERR_UNSUPPORTED),  # f32 backward: d = 64 only
     (dict(ws=None), osa.ERR_WORKSPACE),
+    (dict(dtype=F16, ws=None), osa.ERR_WORKSPACE),  # fp16 d = 64 passes the dtype checks
+    (dict(dtype=BF16, d=128, ws=None), osa.ERR_WORKSPACE),
     (dict(ws=A, ws_bytes=16), osa.ERR_WORKSPACE),
     (dict(ws=A + 16), osa.ERR_ALIGNMENT),
     (dict(ptrs={"do": None}), osa.ERR_INVALID_ARG),
@@ -158,7 +160,9 @@ def test_fwd_workspace_bytes_varlen_work_list(lib):
 def test_bwd_workspace_bytes(lib):
     n = lib.osattn_bwd_workspace_bytes(F32, 1, 8192, 2048, 64, 0, None, 0, 0)
     assert n >= 3 * 8192 * 4 and n % 256 == 0
-    assert lib.osattn_bwd_workspace_bytes(F16, 1, 8192, 2048, 64, 0, None, 0, 0) == 0
+    assert lib.osattn_bwd_workspace_bytes(F16, 1, 8192, 2048, 64, 0, None, 0, 0) >= 3 * 8192 * 4
+    assert lib.osattn_bwd_workspace_bytes(BF16, 1, 8192, 2048, 128, 0, None, 0, 0) >= 3 * 8192 * 4
+    assert lib.osattn_bwd_workspace_bytes(F16, 1, 8192, 2048, 96, 0, None, 0, 0) == 0
     assert lib.osattn_bwd_workspace_bytes(F32, 1, 8192, 2048, 128, 0, None, 0, 0) == 0
     assert lib.osattn_bwd_workspace_bytes(F32, 0, 8192, 2048, 64, 0, None, 0, 0) == 0
 

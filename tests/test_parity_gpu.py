@@ -235,6 +235,41 @@ def test_bwd_parity_f32(osattn, oracle, causal, n_q, n_k, H, lengths):
         assert torch.equal(a, b)
 
 
+BWD16_CASES = [
+    # (causal, n_q, n_k, H, lengths): ragged tails, several query and key tiles,
+    # split reductions (n_q = 1024 with 256 keys splits dK/dV over queries;
+    # 200 queries against 1024 keys split dQ over keys), varlen with empty and
+    # one-token sequences
+    (False, 300, 200, 2, None), (True, 300, 300, 2, None), (True, 700, 700, 1, None),
+    (False, 1024, 256, 1, None), (False, 200, 1024, 1, None), (False, 1, 1, 1, None),
+    (True, 0, 0, 2, [384, 1, 96, 640, 57]), (False, 0, 0, 1, [130, 0, 7, 300]),
+]
+
+
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128), ("bf16", 64), ("f16", 128)])
+@pytest.mark.parametrize("causal,n_q,n_k,H,lengths", BWD16_CASES)
+def test_bwd_parity_16bit(osattn, oracle, dtype, D, causal, n_q, n_k, H, lengths):
+    if lengths is not None:
+        n_q = n_k = sum(lengths)
+    w = small("b16", H, n_q, n_k, D, dtype, causal, 7000 + n_q + D, lengths=lengths, backward=True)
+    inp = W.make_inputs(w)
+    q, k, v, do = (to_dev(x, dtype) for x in (inp.q, inp.k, inp.v, inp.do))
+    cu = cu_dev(inp.cu_seqlens)
+    o, m, l = osattn.fwd(q, k, v, scale=w.softmax_scale, causal=causal, cu_seqlens=cu)
+    dq, dk, dv = osattn.bwd(q, k, v, o, do, m, l, scale=w.softmax_scale, causal=causal,
+                            cu_seqlens=cu)
+    dq2, dk2, dv2 = osattn.bwd(q, k, v, o, do, m, l, scale=w.softmax_scale, causal=causal,
+                               cu_seqlens=cu)
+    torch.cuda.synchronize()
+    assert dq.dtype == q.dtype and dk.dtype == q.dtype and dv.dtype == q.dtype
+    rdq, rdk, rdv, *_ = oracle.attn_bwd(inp.q32, inp.k32, inp.v32, inp.do32, w.softmax_scale,
+                                        causal=causal, cu_seqlens=inp.cu_seqlens)
+    for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        assert_grad_close(host(g), r, dtype, "%s %s D=%d causal=%s" % (name, dtype, D, causal))
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):  # no atomics: bit-identical reruns
+        assert torch.equal(a, b)
+
+
 # ------------------------------------------------------------ split-KV forward
 @pytest.mark.parametrize("dtype,D,n_q,n_k,H", [("f16", 64, 128, 16384, 4), ("bf16", 128, 300, 2100, 2),
                                                ("f16", 128, 129, 4097, 1), ("bf16", 64, 1, 8191, 3)])
