@@ -27,6 +27,7 @@ sequence for varlen; backward 2.5x the forward).  Rank 0 prints ONE JSON line
 Only one GPU is used; --gpus above 1 exits with a message.
 """
 import argparse
+import dataclasses
 import glob
 import hashlib
 import json
@@ -160,8 +161,10 @@ def capture(fn, n, torch, stream):
     return g
 
 
-def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True):
+def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True, backward=False):
     w = W.WORKLOADS[name]
+    if backward and not w.backward:  # same q, k, v draws; dO drawn after them
+        w = dataclasses.replace(w, backward=True)
     inp = W.make_inputs(w)
     q, k, v, do, cu = upload(inp, torch, np)
     max_seqlen = max(w.lengths) if w.lengths else None
@@ -263,6 +266,23 @@ def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True):
                 "frac": achieved / peak, "traffic": recorded_traffic(name, kern),
                 "kernel": kern, "launch_us_avg": avg_ms * 1e3, "launches": n_per * reps,
                 "flops_per_launch": fwd_flops(w)}
+    bwd_rec = None
+    if bw is not None:
+        # Backward alone: same protocol as the forward roofline above.
+        g_bwd = capture(bw, n_per, torch, stream)
+        with torch.cuda.stream(stream):
+            g_bwd.replay()
+            b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            b0.record()
+            for _ in range(reps):
+                g_bwd.replay()
+            b1.record()
+        torch.cuda.synchronize()
+        bwd_ms = b0.elapsed_time(b1) / (n_per * reps)
+        bwd_ach = bwd_flops(w) / (bwd_ms * 1e-3) / 1e12
+        bwd_rec = {"launch_us_avg": bwd_ms * 1e3, "achieved": bwd_ach, "peak": peak,
+                   "unit": "TFLOP/s", "frac": bwd_ach / peak, "flops_per_launch": bwd_flops(w),
+                   "kernels": "bwd_pre+dkdv+dq(+reduce)"}
     out = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
            "warmup": warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
@@ -276,6 +296,8 @@ def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True):
            "pct_of_peak": 100.0 * value / peak,
            "event_ms_per_step": e0.elapsed_time(e1) / steps,
            "roofline": roofline, "parity": parity_rec}
+    if bwd_rec is not None:
+        out["backward"] = bwd_rec
     if with_cpu:
         out["cpu_baseline"] = cpu_baseline(w, inp, oracle, np)
     return out
@@ -289,6 +311,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--all", action="store_true", help="one JSON line per workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    ap.add_argument("--backward", action="store_true",
+                    help="time forward + backward for the workload (its step becomes both passes)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run 10 plain device copies of BYTES bytes (calibrates the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters against a known size)")
@@ -320,7 +344,7 @@ def main():
     names = W.ORDER if args.all else [args.workload]
     for name in names:
         res = run_workload(name, args.steps, args.warmup, torch, np, osa, W, oracle,
-                           with_cpu=not args.no_cpu)
+                           with_cpu=not args.no_cpu, backward=args.backward)
         print(json.dumps(res), flush=True)
 
 

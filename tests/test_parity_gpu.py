@@ -6,6 +6,8 @@ element within the stated tolerances (tests/gpu_util.py).  Sizes span several
 128-row query tiles and ragged tails; the full-size workloads compare sampled
 rows, which the oracle computes one by one.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -268,6 +270,38 @@ def test_bwd_parity_16bit(osattn, oracle, dtype, D, causal, n_q, n_k, H, lengths
         assert_grad_close(host(g), r, dtype, "%s %s D=%d causal=%s" % (name, dtype, D, causal))
     for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):  # no atomics: bit-identical reruns
         assert torch.equal(a, b)
+
+
+# Full-size backward at the fp16/bf16 workloads' shapes.  The oracle runs on the
+# sampled heads only, and on varlen one packed sequence at a time (sequences
+# are independent: the oracle pins check varlen against per-sequence runs).
+BWD_FULL = [("dense_n1024_h4_d64_f16", None), ("causal_n4096_h16_d128_bf16", [5, 12]),
+            ("varlen_causal_16k_h8_d64_f16", [3])]
+
+
+@pytest.mark.parametrize("name,heads", BWD_FULL)
+def test_workload_bwd_full_size(osattn, oracle, name, heads):
+    w = dataclasses.replace(W.WORKLOADS[name], backward=True)
+    inp = W.make_inputs(w)
+    q, k, v, do = (to_dev(x, w.dtype) for x in (inp.q, inp.k, inp.v, inp.do))
+    cu = cu_dev(inp.cu_seqlens)
+    o, m, l = osattn.fwd(q, k, v, scale=w.softmax_scale, causal=w.causal, cu_seqlens=cu)
+    dq, dk, dv = osattn.bwd(q, k, v, o, do, m, l, scale=w.softmax_scale, causal=w.causal,
+                            cu_seqlens=cu)
+    torch.cuda.synchronize()
+    got = [host(t) for t in (dq, dk, dv)]
+    spans = ([(0, w.n_q)] if inp.cu_seqlens is None else
+             [(int(a), int(b)) for a, b in zip(inp.cu_seqlens[:-1], inp.cu_seqlens[1:]) if b > a])
+    for h in (range(w.H) if heads is None else heads):
+        ref = [np.zeros((w.n_q, w.D)), np.zeros((w.n_k, w.D)), np.zeros((w.n_k, w.D))]
+        for a, b in spans:
+            sl = lambda x: np.ascontiguousarray(x[h:h + 1, a:b])
+            r = oracle.attn_bwd(sl(inp.q32), sl(inp.k32), sl(inp.v32), sl(inp.do32), w.softmax_scale,
+                                causal=w.causal)
+            for i in range(3):
+                ref[i][a:b] = r[i][0]
+        for i, nm in enumerate(("dq", "dk", "dv")):
+            assert_grad_close(got[i][h], ref[i], w.dtype, "%s %s head %d" % (name, nm, h))
 
 
 # ------------------------------------------------------------ split-KV forward
