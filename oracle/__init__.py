@@ -10,7 +10,9 @@ Definitions followed (cited per function in the C file):
   * forward: TIGA-lang "Attention and dense relations", the equations of the
     full, causal and varlen causal sections;
   * backward: OCANNL "Module Ir.Online_softmax", the composed-backward bullet,
-    in Jacobian form (no D = rowsum(dO * O) shortcut).
+    in Jacobian form (no D = rowsum(dO * O) shortcut);
+  * tile-pruned forward: TIGA-lang "Tile-pruned sparse attention", the
+    admission rule on (query block, key tile) pairs.
 
 Inputs are float arrays laid out (H, N, D); they are upcast exactly to f64.
 bf16 inputs must be passed already widened to f32 (exact).
@@ -58,6 +60,10 @@ def _load():
             ctypes.c_int, i64, i64, ctypes.c_int, dp, dp, dp, dp, ctypes.c_double,
             ctypes.c_int, ip, ctypes.c_int, dp, dp, dp, dp, dp, dp]
         lib.oracle_attn_bwd.restype = ctypes.c_int
+        lib.oracle_attn_fwd_pruned.argtypes = [
+            ctypes.c_int, i64, i64, ctypes.c_int, dp, dp, dp, ctypes.c_double, ctypes.c_double,
+            ctypes.c_int, ctypes.c_int, dp, dp, dp, ctypes.POINTER(ctypes.c_uint8), dp]
+        lib.oracle_attn_fwd_pruned.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -139,3 +145,30 @@ def attn_bwd(q, k, v, dout, scale, causal=False, cu_seqlens=None):
     if st != 0:
         raise ValueError("oracle_attn_bwd failed with status %d" % st)
     return dq, dk, dv, m, l, delta
+
+
+def attn_fwd_pruned(q, k, v, scale, rho, br=128, bc=128):
+    """Tile-pruned dense forward (an approximation; see the C source).
+
+    Query blocks of ``br`` rows, key tiles of ``bc`` keys, admission
+    m_tile >= m_run + ln(rho) per (head, query block).  Returns
+    (o, m, l, admit, min_margin): o (H, n_q, D), m and l (H, n_q) in f64,
+    admit (H, ceil(n_q / br), ceil(n_k / bc)) uint8, and the smallest distance
+    of a tile maximum from its threshold over the decisions taken against a
+    finite running maximum.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    H, n_q, D = q.shape
+    n_k = k.shape[1]
+    assert k.shape == (H, n_k, D) and v.shape == (H, n_k, D)
+    o = np.empty((H, n_q, D))
+    m = np.empty((H, n_q))
+    l = np.empty((H, n_q))
+    admit = np.zeros((H, (n_q + br - 1) // br, (n_k + bc - 1) // bc), dtype=np.uint8)
+    margin = ctypes.c_double(0.0)
+    st = _load().oracle_attn_fwd_pruned(
+        H, n_q, n_k, D, _ptr(q), _ptr(k), _ptr(v), float(scale), float(rho), int(br), int(bc),
+        _ptr(o), _ptr(m), _ptr(l), _ptr(admit, ctypes.c_uint8), ctypes.byref(margin))
+    if st != 0:
+        raise ValueError("oracle_attn_fwd_pruned failed with status %d" % st)
+    return o, m, l, admit, margin.value

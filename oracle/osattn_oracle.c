@@ -42,6 +42,9 @@
  *       dQ_i    = scale * sum_j dS_ij k_j
  *       dK_j    = scale * sum_i dS_ij q_i
  *
+ *   Tile-pruned forward (an approximation, defined on query blocks and key
+ *   tiles) -- see oracle_attn_fwd_pruned below.
+ *
  * Layout: every array is (H, N, D) row-major and contiguous, in double.
  * Parallelism: OpenMP over independent (head, row) pairs only; every output
  * element is produced by one thread with a fixed serial summation order, so
@@ -259,6 +262,106 @@ int oracle_attn_bwd(int H, int64_t n_q, int64_t n_k, int D,
 }
 
 /* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
+/*
+ * Tile-pruned dense forward -- TIGA-lang "基于 tile 剪枝的稀疏注意力"
+ * (tile-pruned sparse attention), section "具体规则与边界" (rules and
+ * boundaries) and its admission inequality.  An approximation of the dense
+ * attention above, defined on tiles: query block b = rows [b br, (b+1) br),
+ * key tile t = keys [t bc, (t+1) bc) (both cut at the tensor ends).  For each
+ * (head, query block) the key tiles are visited in increasing key order,
+ * with a block-level running maximum m_run that starts at -inf:
+ *     m_tile = max over rows i of the block and keys j of the tile of s_ij
+ *     the tile is admitted  iff  m_tile >= m_run + ln(rho)      (0 < rho <= 1)
+ *     if admitted: m_run = max(m_run, m_tile)
+ * A pruned tile contributes nothing: each row's output is the exact two-pass
+ * softmax attention over the keys of its block's admitted tiles, and m, l are
+ * that softmax's row maximum and normaliser.  (rho -> 0 admits every tile:
+ * the exact dense result.)
+ * Extra outputs, each optional (NULL): admit[(h * nqb + b) * nkt + t] = 1 or 0
+ * with nqb = ceil(n_q / br), nkt = ceil(n_k / bc); *min_margin = the smallest
+ * |m_tile - (m_run + ln rho)| over the decisions taken against a finite
+ * m_run (+inf if there are none), so a caller can tell whether rounding of
+ * the scores could flip a decision.
+ */
+int oracle_attn_fwd_pruned(int H, int64_t n_q, int64_t n_k, int D,
+                           const double *q, const double *k, const double *v,
+                           double scale, double rho, int br, int bc,
+                           double *o, double *m, double *l,
+                           unsigned char *admit, double *min_margin)
+{
+    if (!q || !k || !v || !o || !m || !l) return -1;
+    if (check_args(H, n_q, n_k, D, 0, NULL, 0)) return -1;
+    if (!(rho > 0.0 && rho <= 1.0) || br <= 0 || bc <= 0) return -1;
+    const int64_t nqb = (n_q + br - 1) / br, nkt = (n_k + bc - 1) / bc;
+    const double log_rho = log(rho);
+    int status = 0;
+    double margin = INFINITY;
+
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)br * (size_t)n_k);
+        unsigned char *adm = (unsigned char *)malloc((size_t)nkt);
+        double my_margin = INFINITY;
+        if (!s || !adm) {
+#pragma omp atomic write
+            status = -2;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t hb = 0; hb < (int64_t)H * nqb; ++hb) {
+            if (!s || !adm) continue;
+            const int64_t h = hb / nqb, b = hb % nqb;
+            const int64_t i0 = b * br, i1 = (i0 + br < n_q) ? i0 + br : n_q;
+            const double *kh = k + h * n_k * D;
+            const double *vh = v + h * n_k * D;
+            /* every score of the block */
+            for (int64_t i = i0; i < i1; ++i)
+                for (int64_t j = 0; j < n_k; ++j)
+                    s[(i - i0) * n_k + j] = dot(kh + j * D, q + (h * n_q + i) * D, D) * scale;
+            /* the admission scan over the key tiles */
+            double m_run = -INFINITY;
+            for (int64_t t = 0; t < nkt; ++t) {
+                const int64_t j0 = t * bc, j1 = (j0 + bc < n_k) ? j0 + bc : n_k;
+                double m_tile = -INFINITY;
+                for (int64_t i = i0; i < i1; ++i)
+                    for (int64_t j = j0; j < j1; ++j)
+                        if (s[(i - i0) * n_k + j] > m_tile) m_tile = s[(i - i0) * n_k + j];
+                const double thr = m_run + log_rho;
+                adm[t] = (unsigned char)(m_tile >= thr);
+                if (isfinite(m_run) && fabs(m_tile - thr) < my_margin) my_margin = fabs(m_tile - thr);
+                if (adm[t] && m_tile > m_run) m_run = m_tile;
+                if (admit) admit[hb * nkt + t] = adm[t];
+            }
+            /* each row: two-pass softmax over the admitted tiles' keys */
+            for (int64_t i = i0; i < i1; ++i) {
+                const double *si = s + (i - i0) * n_k;
+                double *oi = o + (h * n_q + i) * D;
+                double mx = -INFINITY;
+                for (int64_t j = 0; j < n_k; ++j)
+                    if (adm[j / bc] && si[j] > mx) mx = si[j];
+                double sum = 0.0;
+                for (int64_t j = 0; j < n_k; ++j)
+                    if (adm[j / bc]) sum += exp(si[j] - mx);
+                for (int d = 0; d < D; ++d) oi[d] = 0.0;
+                for (int64_t j = 0; j < n_k; ++j) {
+                    if (!adm[j / bc]) continue;
+                    const double p = exp(si[j] - mx) / sum;
+                    for (int d = 0; d < D; ++d) oi[d] += p * vh[j * D + d];
+                }
+                m[h * n_q + i] = mx;
+                l[h * n_q + i] = sum;
+            }
+        }
+#pragma omp critical
+        {
+            if (my_margin < margin) margin = my_margin;
+        }
+        free(s);
+        free(adm);
+    }
+    if (min_margin) *min_margin = margin;
+    return status;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -34,6 +34,17 @@ MUTATIONS = {
     "dv_uses_dS": ("dvj[d] += p * doh[i * D + d];", "dvj[d] += ds * doh[i * D + d];"),
     "dk_uses_do": ("dkj[d] += ds * qh[i * D + d];", "dkj[d] += ds * doh[i * D + d];"),
     "dq_uses_v": ("acc += dSi[j] * kh[j * D + d];", "acc += dSi[j] * vh[j * D + d];"),
+    # tile pruning
+    "prune_strict_comparison": ("adm[t] = (unsigned char)(m_tile >= thr);",
+                                "adm[t] = (unsigned char)(m_tile > thr);"),
+    "prune_log_base_2": ("const double log_rho = log(rho);", "const double log_rho = log2(rho);"),
+    "prune_threshold_sign": ("const double thr = m_run + log_rho;", "const double thr = m_run - log_rho;"),
+    "prune_tile_max_first_row_only": (
+        "for (int64_t i = i0; i < i1; ++i)\n                    for (int64_t j = j0; j < j1; ++j)",
+        "for (int64_t i = i0; i < i0 + 1; ++i)\n                    for (int64_t j = j0; j < j1; ++j)"),
+    "prune_running_max_never_moves": ("if (adm[t] && m_tile > m_run) m_run = m_tile;", ""),
+    "prune_tile_overlaps_next": ("const int64_t j0 = t * bc, j1 = (j0 + bc < n_k) ? j0 + bc : n_k;",
+                                 "const int64_t j0 = t * bc, j1 = (j0 + bc + 1 < n_k) ? j0 + bc + 1 : n_k;"),
 }
 
 PIN_CALLS = [
@@ -48,6 +59,8 @@ PIN_CALLS = [
     lambda o: pins.test_backward_autograd_sdpa(o, False),
     lambda o: pins.test_backward_autograd_sdpa(o, True),
     lambda o: pins.test_backward_identities(o, True, [0, 10, 11, 40]),
+    lambda o: [pins.test_pruning_golden(o, c) for c in pins.load_pruning()["cases"]],
+    lambda o: pins.test_pruning_tiny_rho_is_exact(o, 300, 200, 128, 128),
 ]
 
 

@@ -407,3 +407,48 @@ def test_thread_count_does_not_change_results(oracle):
         env = dict(os.environ, OMP_NUM_THREADS=t)
         outs.append(subprocess.check_output([sys.executable, "-c", code], env=env))
     assert outs[0] == outs[1]
+
+
+# ------------------------------------------------------------------- tile pruning
+PRUNE_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "tile_pruning_cases.json")
+
+
+def load_pruning():
+    with open(PRUNE_GOLDEN) as f:
+        return json.load(f)
+
+
+def test_pruning_page_ratio():
+    # The page prints exp(1 - 10) as about 0.00012.
+    r = load_pruning()["page_ratio"]
+    assert abs(math.exp(1 - 10) - r["printed"]) < 5e-6 and r["value"] == math.exp(-9)
+
+
+@pytest.mark.parametrize("case", load_pruning()["cases"], ids=lambda c: c["name"])
+def test_pruning_golden(oracle, case):
+    q, k, v = (np.array(case[x], dtype=np.float64) for x in "qkv")
+    o, m, l, admit, _ = oracle.attn_fwd_pruned(q, k, v, case["scale"], case["rho"], case["br"],
+                                               case["bc"])
+    assert admit.tolist() == case["admit"]
+    np.testing.assert_allclose(o, np.array(case["o"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(m, np.array(case["m"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, np.array(case["l"]), rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("n_q,n_k,br,bc", [(300, 200, 128, 128), (130, 257, 64, 32)])
+def test_pruning_tiny_rho_is_exact(oracle, n_q, n_k, br, bc):
+    # rho -> 0 admits every tile: the exact dense attention.
+    q, k, v = rand((2, n_q, 16), 1), rand((2, n_k, 16), 2), rand((2, n_k, 16), 3)
+    o, m, l, admit, _ = oracle.attn_fwd_pruned(q, k, v, 0.25, 1e-300, br, bc)
+    ro, rm, rl = oracle.attn_fwd(q, k, v, 0.25)
+    assert admit.all()
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(m, rm, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, rl, rtol=1e-12, atol=0)
+
+
+def test_pruning_rejects_bad_rho(oracle):
+    q = rand((1, 4, 8), 1)
+    for rho in (0.0, -0.5, 1.5, float("nan")):
+        with pytest.raises(ValueError):
+            oracle.attn_fwd_pruned(q, q, q, 0.5, rho, 2, 2)
