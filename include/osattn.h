@@ -133,6 +133,33 @@ int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d,
                void *stream);
 
 /*
+ * Tile-pruned forward: an approximation of the dense forward (TIGA-lang
+ * "tile-pruned sparse attention", the admission rule of its rules section).
+ * Queries are cut into blocks of 128 rows and keys into tiles of 128 keys.
+ * For each (head, query block) the key tiles are visited in key order with a
+ * block running maximum m_run (starting at -inf): a tile whose largest
+ * scaled score over all the block's rows and the tile's keys is below
+ * m_run + ln(rho) is pruned -- it adds nothing to the softmax; otherwise it
+ * is admitted and m_run = max(m_run, that score).  o, m, l are the exact
+ * softmax results over each block's admitted keys.  The tile scores are
+ * always computed; a pruned tile skips the exponentials and the P.V product.
+ * Larger rho prunes more; rho = 1 keeps only tiles that reach the running
+ * maximum.  There is no error bound: validate accuracy per workload.
+ *
+ * Dense relation only (no causal or varlen form), fp16/bf16, d = 64 or 128.
+ * rho must satisfy 0 < rho <= 1 (OSATTN_ERR_INVALID_ARG otherwise; for the
+ * exact result call osattn_fwd).  f32 returns OSATTN_ERR_UNSUPPORTED.
+ * Arguments, layouts and errors otherwise as osattn_fwd; no workspace.
+ */
+int osattn_fwd_pruned(int dtype, int H, int64_t n_q, int64_t n_k, int d,
+                      const void *q, const void *k, const void *v,
+                      int64_t q_stride_h, int64_t q_stride_n,
+                      int64_t kv_stride_h, int64_t kv_stride_n,
+                      float *o, int64_t o_stride_h, int64_t o_stride_n,
+                      float *m, float *l, float scale, float rho,
+                      void *stream);
+
+/*
  * Bytes of device workspace osattn_bwd needs for this problem (the per-row
  * D vector and statistics, plus partial gradient sums when the launch splits
  * a reduction across workgroups).  Returns 0 for unsupported or invalid

@@ -7,6 +7,7 @@ computation runs in the library's HIP kernels; there is no fallback of any
 kind -- if the library is missing, every call raises.
 
     o, m, l = fwd(q, k, v, scale=None, causal=False, cu_seqlens=None, max_seqlen=None)
+    o, m, l = fwd_pruned(q, k, v, rho, scale=None)     # tile-pruned approximation
     dq, dk, dv = bwd(q, k, v, o, do, m, l, scale=None, causal=False, ...)
 
 Tensors are (H, N, D) by default (``layout="hnd"``) or (N, H, D)
@@ -27,8 +28,9 @@ LIB_PATH = os.path.join(_HERE, "libosattn.so")
 
 F32, F16, BF16 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_HIP, ERR_WORKSPACE = range(6)
-EXPORTS = ("osattn_fwd", "osattn_fwd_workspace_bytes", "osattn_bwd", "osattn_bwd_workspace_bytes",
-           "osattn_status_string", "osattn_last_error", "osattn_version")
+EXPORTS = ("osattn_fwd", "osattn_fwd_workspace_bytes", "osattn_fwd_pruned", "osattn_bwd",
+           "osattn_bwd_workspace_bytes", "osattn_status_string", "osattn_last_error",
+           "osattn_version")
 
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 _lib = None
@@ -53,6 +55,9 @@ def load(path: Optional[str] = None):
     lib.osattn_fwd.argtypes = [i32, i32, i64, i64, i32, vp, vp, vp, i64, i64, i64, i64,
                                vp, i64, i64, vp, vp, f32, i32, vp, i32, i32, vp, ctypes.c_size_t, vp]
     lib.osattn_fwd.restype = i32
+    lib.osattn_fwd_pruned.argtypes = [i32, i32, i64, i64, i32, vp, vp, vp, i64, i64, i64, i64,
+                                      vp, i64, i64, vp, vp, f32, f32, vp]
+    lib.osattn_fwd_pruned.restype = i32
     lib.osattn_fwd_workspace_bytes.argtypes = [i32, i32, i64, i64, i32, i32, vp, i32, i32]
     lib.osattn_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.osattn_bwd_workspace_bytes.argtypes = [i32, i32, i64, i64, i32, i32, vp, i32, i32]
@@ -179,6 +184,34 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float
                         l.data_ptr(), scale, int(bool(causal)), cu_ptr, num_seqs, max_seqlen,
                         ws_ptr, ws_bytes, _stream())
     _check(st, "osattn_fwd")
+    return o, m, l
+
+
+def fwd_pruned(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: float,
+               scale: Optional[float] = None, layout: str = "hnd",
+               out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """Tile-pruned dense forward (an approximation; see osattn_fwd_pruned); returns (o, m, l)."""
+    lib = load()
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype of float16/bfloat16")
+    H, n_q, D, q_sh, q_sn = _hn(q, layout)
+    Hk, n_k, Dk, kv_sh, kv_sn = _hn(k, layout)
+    Hv, n_v, Dv, v_sh, v_sn = _hn(v, layout)
+    if (Hk, Dk) != (H, D) or (Hv, n_v, Dv) != (H, n_k, D) or (v_sh, v_sn) != (kv_sh, kv_sn):
+        raise ValueError("k and v must have the same shape and strides, matching q's H and D")
+    scale = D ** -0.5 if scale is None else float(scale)
+    if out is None:
+        shape = (H, n_q, D) if layout == "hnd" else (n_q, H, D)
+        o = torch.empty(shape, dtype=torch.float32, device=q.device)
+        m = torch.empty((H, n_q), dtype=torch.float32, device=q.device)
+        l = torch.empty((H, n_q), dtype=torch.float32, device=q.device)
+    else:
+        o, m, l = out
+    _, _, _, o_sh, o_sn = _hn(o, layout)
+    st = lib.osattn_fwd_pruned(_DT[q.dtype], H, n_q, n_k, D, q.data_ptr(), k.data_ptr(),
+                               v.data_ptr(), q_sh, q_sn, kv_sh, kv_sn, o.data_ptr(), o_sh, o_sn,
+                               m.data_ptr(), l.data_ptr(), scale, float(rho), _stream())
+    _check(st, "osattn_fwd_pruned")
     return o, m, l
 
 

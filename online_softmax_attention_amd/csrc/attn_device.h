@@ -162,6 +162,11 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// s_waitcnt on the LDS/scalar counter only (vmcnt and expcnt at their maxima).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
 // Workgroup barrier without the memory fence __syncthreads() carries (that
 // fence would wait for every outstanding LDS DMA, defeating the prefetch).
 // Callers order their own LDS traffic with explicit vmcnt / lgkmcnt waits;

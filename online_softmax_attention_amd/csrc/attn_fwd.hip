@@ -186,7 +186,9 @@ __device__ __forceinline__ void wait_dma_blocks(int blocks) {
 // merged through LDS at the end.  Launches use RG = 4 (128-row tiles) unless
 // such tiles are too few to occupy the device.
 // split < 0: write O, m, l.  split >= 0: write this key range's partial state.
-template <typename T, int D, int MASK, int NST, int RG>
+// PRUNE: tile-pruned dense forward (each block is one 128 x BC tile); smem then
+// carries 8 extra floats past the stages for the tile-maximum exchange.
+template <typename T, int D, int MASK, int NST, int RG, bool PRUNE = false>
 __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h, int q_lo,
                                            int q_hi, int kv_lo, int kv_hi, int split) {
     typedef Fwd16Cfg<D, NST> C;
@@ -247,6 +249,7 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
     const float c = p.scale_log2;
     const int nblk = (kv_hi - kv_lo + C::BC - 1) / C::BC;
     const int wrow_lo = q_lo + 32 * rg, wrow_hi = wrow_lo + 31;
+    float m_blk = kNegInf;  // PRUNE: running maximum of the query block (raw score units)
 
     // Prefetch distance NST - 1 blocks.
     for (int j = 0; j < NST - 1 && j < nblk; ++j) issue(kv_lo + j * C::BC, j);
@@ -262,6 +265,98 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
         const int kw0 = k0 + kg * KH;  // first key of this wave's group
         const char *sk = smem + (j % NST) * C::STAGE;
         const char *sv = sk + C::TILE;
+        if constexpr (PRUNE) {
+            // Tile pruning (TIGA-lang "tile-pruned sparse attention", the
+            // admission rule): the block is one (128-row, BC-key) tile.  Every
+            // wave scores its keys for its rows, the 8 waves' maxima meet in
+            // LDS, and the tile is admitted iff its maximum reaches the
+            // block's running maximum plus ln(rho) (p.prune_thr = ln(rho) /
+            // scale in raw score units).  A pruned tile skips the
+            // exponentials and the P.V product; its V block was prefetched.
+            const bool act = kw0 < kv_hi;
+            f32x16 S[NS];
+            float mxc[NS];
+            float wmax = kNegInf;
+            if (act) {
+#pragma unroll
+                for (int cc = 0; cc < NS; ++cc) {
+                    const int row = kg * KH + 32 * cc + c32;
+                    const char *krow = sk + row * C::ROW;
+                    S[cc] = zero_vec<f32x16>();
+#pragma unroll
+                    for (int kk = 0; kk < C::NKK; ++kk) {
+                        const vec8 a = *reinterpret_cast<const vec8 *>(krow + swz_k<C::ROW>(row, 2 * kk + g) * 16);
+                        S[cc] = Half8<T>::mma(a, qreg[kk], S[cc]);
+                    }
+                    const int kc0 = kw0 + 32 * cc;
+                    if (kc0 + 32 > kv_hi) {
+                        f32x16 Sm[1] = {S[cc]};
+                        mask_block<1, false>(Sm, kc0, g, kv_hi, qrow);
+                        S[cc] = Sm[0];
+                    }
+                    float t[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        t[i] = vmax(vmax(S[cc][4 * i], S[cc][4 * i + 1]), vmax(S[cc][4 * i + 2], S[cc][4 * i + 3]));
+                    mxc[cc] = xor32_max(vmax(vmax(t[0], t[1]), vmax(t[2], t[3])));
+                    wmax = vmax(wmax, mxc[cc]);
+                }
+                if (qrow >= q_hi) wmax = kNegInf;  // rows past the tile end do not count
+            }
+#pragma unroll
+            for (int off = 16; off >= 1; off >>= 1) wmax = vmax(wmax, __shfl_xor(wmax, off));
+            float *slot = reinterpret_cast<float *>(smem + NST * C::STAGE);
+            if (lane == 0) slot[wave] = wmax;
+            wait_lgkmcnt0();
+            bare_barrier();
+            float m_tile = slot[0];
+#pragma unroll
+            for (int w = 1; w < 8; ++w) m_tile = vmax(m_tile, slot[w]);
+            if (m_tile >= m_blk + p.prune_thr) {
+                m_blk = vmax(m_blk, m_tile);
+                if (act) {
+#pragma unroll
+                    for (int cc = 0; cc < NS; ++cc) {
+                        const float mx = mxc[cc];
+                        m_true = vmax(m_true, mx);
+                        if (__any((mx - m_ref) * c > kLazyLog2)) {
+                            const float m_new = vmax(m_ref, mx);
+                            const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_ref - m_new) * c);
+#pragma unroll
+                            for (int dt = 0; dt < C::NDT; ++dt) U[dt] *= alpha;
+                            l_run *= alpha;
+                            m_ref = m_new;
+                        }
+                        const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
+                        vec8 P[2];
+                        float ps = 0.f;
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf) {
+                            f32x8 x;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) x[e] = fast_exp2(fmaf(S[cc][8 * hf + e], c, -mc));
+                            ps += ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+                            P[hf] = __builtin_convertvector(x, vec8);
+                        }
+                        l_run += ps;
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf) {
+                            const int r0 = kg * KH + 32 * cc + 16 * hf + 4 * g + ((lane & 15) >> 2);
+                            const int cq = lane & 3, hh = (lane >> 4) & 1;
+#pragma unroll
+                            for (int dt = 0; dt < C::NDT; ++dt) {
+                                const int ch = 4 * dt + 2 * hh + (cq >> 1);
+                                const i16x4 lo = lds_read_tr16(sv + r0 * C::ROW + swz_vt<C::ROW>(r0, ch) * 16 + 8 * (cq & 1));
+                                const i16x4 hi = lds_read_tr16(sv + (r0 + 8) * C::ROW + swz_vt<C::ROW>(r0 + 8, ch) * 16 + 8 * (cq & 1));
+                                const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                                U[dt] = Half8<T>::mma(a, P[hf], U[dt]);
+                            }
+                        }
+                    }
+                }
+            }
+            continue;
+        }
         if (kw0 < kv_hi && (!causal || kw0 <= wrow_hi)) {
             // The wave's KH keys are processed as 32-key chunks, software
             // pipelined: chunk cc+1's S^T MFMAs are issued before chunk cc's
@@ -624,6 +719,35 @@ __global__ void __launch_bounds__(kT16) fwd16_kernel(FwdParams p) {
         const int kv_hi = causal ? q_hi : (varlen ? seq_hi : p.n_k);
         fwd16_tile<T, D, MASK, NST, RG>(p, smem, h, q_lo, q_hi, seq_lo, kv_hi, -1);
     }
+}
+
+// Tile-pruned dense forward: one 128-row tile per workgroup, key blocks of 128
+// (D = 64 uses four stages of 128 keys so that both widths prune 128 x 128
+// tiles).
+template <typename T, int D>
+__global__ void __launch_bounds__(kT16) fwd16_pruned_kernel(FwdParams p) {
+    constexpr int NST = D == 64 ? 4 : 2;
+    static_assert(Fwd16Cfg<D, NST>::BC == 128, "pruning tiles are 128 keys");
+    __shared__ __attribute__((aligned(16))) char smem[NST * Fwd16Cfg<D, NST>::STAGE + 256];
+    const int h = blockIdx.x % p.H, tile = blockIdx.x / p.H;
+    const int q_lo = tile * kBR, q_hi = min(q_lo + kBR, p.n_q);
+    fwd16_tile<T, D, kDense, NST, 4, true>(p, smem, h, q_lo, q_hi, 0, p.n_k, -1);
+}
+
+hipError_t launch_forward_pruned(int dtype, int d, FwdParams p, hipStream_t st) {
+    p.n_tiles = (p.n_q + kBR - 1) / kBR;
+    const int64_t grid = (int64_t)p.n_tiles * p.H;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const dim3 g((unsigned)grid), b(kT16);
+    if (dtype == 1) {
+        if (d == 64) hipLaunchKernelGGL((fwd16_pruned_kernel<_Float16, 64>), g, b, 0, st, p);
+        else hipLaunchKernelGGL((fwd16_pruned_kernel<_Float16, 128>), g, b, 0, st, p);
+    } else {
+        if (d == 64) hipLaunchKernelGGL((fwd16_pruned_kernel<__bf16, 64>), g, b, 0, st, p);
+        else hipLaunchKernelGGL((fwd16_pruned_kernel<__bf16, 128>), g, b, 0, st, p);
+    }
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------- f32

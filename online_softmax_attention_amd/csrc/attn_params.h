@@ -45,6 +45,7 @@ struct FwdParams {
     // sched_shift coarsens the sort key to fit the histogram.
     int32_t *sched;
     int sched_max, sched_shift;
+    float prune_thr;       // tile pruning: ln(rho) / scale (raw score units)
 };
 
 struct BwdParams {

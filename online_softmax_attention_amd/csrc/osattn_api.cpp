@@ -14,6 +14,7 @@ namespace osattn {
 hipError_t launch_forward(int dtype, int d, int mask, FwdParams p, int max_seqlen, hipStream_t st);
 hipError_t launch_backward(int mask, BwdParams p, int seqs, hipStream_t st);
 hipError_t launch_backward16(int dtype, int d, int mask, BwdParams p, int seqs, hipStream_t st);
+hipError_t launch_forward_pruned(int dtype, int d, FwdParams p, hipStream_t st);
 }  // namespace osattn
 
 using namespace osattn;
@@ -313,6 +314,48 @@ int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
     const hipError_t e = launch_forward(dtype, d, mask_kind(causal, cu_seqlens), p, max_seqlen,
                                         static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(OSATTN_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int osattn_fwd_pruned(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
+                      const void *k, const void *v, int64_t q_stride_h, int64_t q_stride_n,
+                      int64_t kv_stride_h, int64_t kv_stride_n, float *o, int64_t o_stride_h,
+                      int64_t o_stride_n, float *m, float *l, float scale, float rho,
+                      void *stream) {
+    int st = check_common(dtype, H, n_q, n_k, d, scale, 0, nullptr, 0, 0);
+    if (st) return st;
+    if (dtype == OSATTN_F32)
+        return fail(OSATTN_ERR_UNSUPPORTED, "tile pruning supports fp16/bf16 only");
+    if (d != 64 && d != 128) return fail(OSATTN_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", d);
+    if (!(rho > 0.f && rho <= 1.f))
+        return fail(OSATTN_ERR_INVALID_ARG, "rho must be in (0, 1] (got %g); omit pruning for the "
+                    "exact result", (double)rho);
+    const size_t es = elem_size(dtype);
+    if ((st = check_tensor("q", q, q_stride_h, q_stride_n, es))) return st;
+    if ((st = check_tensor("k", k, kv_stride_h, kv_stride_n, es))) return st;
+    if ((st = check_tensor("v", v, kv_stride_h, kv_stride_n, es))) return st;
+    if ((st = check_tensor("o", o, o_stride_h, o_stride_n, 4))) return st;
+    if (q_stride_n * (int64_t)es > kMaxRowBytes || kv_stride_n * (int64_t)es > kMaxRowBytes)
+        return fail(OSATTN_ERR_UNSUPPORTED, "row strides above %lld bytes are not supported",
+                    (long long)kMaxRowBytes);
+    if (!m || !l) return fail(OSATTN_ERR_INVALID_ARG, "m and l must not be NULL");
+    FwdParams p{};
+    p.q = q; p.k = k; p.v = v;
+    p.o = o; p.m = m; p.l = l;
+    p.q_sh = q_stride_h; p.q_sn = q_stride_n;
+    p.kv_sh = kv_stride_h; p.kv_sn = kv_stride_n;
+    p.o_sh = o_stride_h; p.o_sn = o_stride_n;
+    p.H = H; p.n_q = (int)n_q; p.n_k = (int)n_k;
+    p.num_seqs = 1;
+    p.scale = scale;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.splits = 1;
+    p.split_len = (int)n_k;
+    p.tile_rows = 128;
+    p.pair = 0;
+    p.prune_thr = logf(rho) / scale;
+    const hipError_t e = launch_forward_pruned(dtype, d, p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(OSATTN_ERR_HIP, "pruned forward launch: %s", hipGetErrorString(e));
     return ok();
 }
 

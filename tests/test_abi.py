@@ -171,3 +171,24 @@ def test_fwd_rejects_huge_row_stride(lib):
     big = (1 << 22) // 2 + 8  # f16 elements: just above 4 MiB per row
     assert fwd(lib, qs=(big * 128, big)) == osa.ERR_UNSUPPORTED
     assert fwd(lib, kvs=(big * 128, big)) == osa.ERR_UNSUPPORTED
+
+
+# Tile-pruned forward: every case fails a host check before any launch.
+def fwd_pruned(lib, dtype=F16, H=1, n_q=256, n_k=128, d=64, rho=0.5, m=None, scale=0.125):
+    return lib.osattn_fwd_pruned(dtype, H, n_q, n_k, d, A, B, C, n_q * d, d, n_k * d, d,
+                                 O, n_q * d, d, m, L, scale, rho, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rho=0.0), osa.ERR_INVALID_ARG),
+    (dict(rho=-0.5), osa.ERR_INVALID_ARG),
+    (dict(rho=1.5), osa.ERR_INVALID_ARG),
+    (dict(rho=float("nan")), osa.ERR_INVALID_ARG),
+    (dict(dtype=F32), osa.ERR_UNSUPPORTED),
+    (dict(d=96), osa.ERR_UNSUPPORTED),
+    (dict(scale=0.0), osa.ERR_UNSUPPORTED),
+    (dict(n_q=0), osa.ERR_INVALID_ARG),
+    (dict(), osa.ERR_INVALID_ARG),  # m is NULL: the last check
+])
+def test_fwd_pruned_rejects_on_host(lib, kw, status):
+    assert fwd_pruned(lib, **kw) == status

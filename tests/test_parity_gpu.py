@@ -384,3 +384,37 @@ def test_fwd_tile_sizes(osattn, oracle, dtype, D, causal, H, n_q, n_k, rows):
     ro, rm, rl = oracle.attn_fwd(inp.q32, inp.k32, inp.v32, inp.w.softmax_scale, causal=causal)
     assert_fwd_close(o, m, l, ro, rm, rl, dtype,
                      "%s D=%d causal=%s H=%d %dx%d (%d-row tiles)" % (dtype, D, causal, H, n_q, n_k, rows))
+
+
+# ------------------------------------------------------------ tile pruning
+# The oracle's admission decisions must be unique at f32 resolution (every
+# tile maximum at least 1e-4 from its threshold), and the case must prune.
+PRUNE_CASES = [  # (dtype, D, rho, n_q, n_k, H); seed 9000
+    ("f16", 64, 1.0, 300, 700, 2), ("bf16", 128, 1.0, 257, 1000, 2),
+    ("f16", 128, 0.7, 1000, 2000, 1), ("bf16", 64, 0.7, 129, 600, 3),
+    ("f16", 64, 0.9, 1024, 1024, 4),
+]
+
+
+@pytest.mark.parametrize("dtype,D,rho,n_q,n_k,H", PRUNE_CASES)
+def test_pruned_fwd_parity(osattn, oracle, dtype, D, rho, n_q, n_k, H):
+    inp = W.make_inputs(small("p", H, n_q, n_k, D, dtype, False, 9000))
+    sc = inp.w.softmax_scale
+    ro, rm, rl, admit, margin = oracle.attn_fwd_pruned(inp.q32, inp.k32, inp.v32, sc, rho, 128, 128)
+    assert margin > 1e-4, "ambiguous admission in the oracle (margin %.2e)" % margin
+    assert (admit == 0).any() and admit.any()
+    q, k, v = (to_dev(x, dtype) for x in (inp.q, inp.k, inp.v))
+    o, m, l = osattn.fwd_pruned(q, k, v, rho, scale=sc)
+    torch.cuda.synchronize()
+    assert_fwd_close(host(o), host(m), host(l), ro, rm, rl, dtype,
+                     "pruned %s D=%d rho=%g (%d%% of tiles pruned)" % (dtype, D, rho, 100 * (1 - admit.mean())))
+
+
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128)])
+def test_pruned_tiny_rho_is_exact(osattn, oracle, dtype, D):
+    inp = W.make_inputs(small("p0", 2, 333, 555, D, dtype, False, 9100))
+    q, k, v = (to_dev(x, dtype) for x in (inp.q, inp.k, inp.v))
+    o, m, l = osattn.fwd_pruned(q, k, v, 1e-30, scale=inp.w.softmax_scale)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attn_fwd(inp.q32, inp.k32, inp.v32, inp.w.softmax_scale)
+    assert_fwd_close(host(o), host(m), host(l), ro, rm, rl, dtype, "pruned, rho -> 0")
