@@ -303,6 +303,75 @@ def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True, 
     return out
 
 
+def run_pruned(name, rho, steps, warmup, torch, np, osa, W, oracle):
+    """Tile-pruned dense forward against the exact forward at one workload's shape."""
+    w = W.WORKLOADS[name]
+    if w.causal or w.lengths or w.dtype == "f32":
+        raise SystemExit("--prune needs a dense fp16/bf16 workload (got %s)" % name)
+    inp = W.make_inputs(w)
+    q, k, v, _, _ = upload(inp, torch, np)
+    H, D = w.H, w.D
+    o = torch.empty((H, w.n_q, D), dtype=torch.float32, device="cuda")
+    m = torch.empty((H, w.n_q), dtype=torch.float32, device="cuda")
+    l = torch.empty_like(m)
+    o2, m2, l2 = torch.empty_like(o), torch.empty_like(m), torch.empty_like(m)
+    ws = torch.empty(0, dtype=torch.uint8, device="cuda")
+
+    def pruned():
+        osa.fwd_pruned(q, k, v, rho, scale=w.softmax_scale, out=(o, m, l))
+
+    def exact():
+        osa.fwd(q, k, v, scale=w.softmax_scale, check=False, out=(o2, m2, l2), workspace=ws)
+
+    hs = min(H, 2)  # the pruned oracle on the first heads only (it scores every tile)
+    ro, rm, rl, admit, margin = oracle.attn_fwd_pruned(inp.q32[:hs], inp.k32[:hs], inp.v32[:hs],
+                                                       w.softmax_scale, rho, 128, 128)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(max(warmup, 1)):
+            pruned()
+            exact()
+    torch.cuda.synchronize()
+    err = float(np.max(np.abs(o[:hs].cpu().numpy() - ro)))
+    n_per = 20
+    reps = max(1, steps // n_per) if steps > 0 else 10
+    times = {}
+    for tag, fn in (("pruned", pruned), ("exact", exact)):
+        g = capture(fn, n_per, torch, stream)
+        with torch.cuda.stream(stream):
+            g.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        times[tag] = e0.elapsed_time(e1) / (n_per * reps)
+    pruned_frac = float(1.0 - admit.mean())
+    flops_exact = fwd_flops(w)
+    # executed: every tile's scores, the P.V product of admitted tiles only
+    flops_exec = flops_exact / 2 * (1.0 + float(admit.mean()))
+    peak = PEAK_TFLOPS[w.dtype]
+    value = flops_exec / (times["pruned"] * 1e-3) / 1e12
+    return {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": n_per * reps, "warmup": warmup, "ms_per_step": times["pruned"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+            "data": "synthetic: seeded N(0,1) q,k,v (numpy default_rng seed %d) rounded to %s"
+                    % (w.seed, w.dtype),
+            "config": {"workload": name, "H": H, "n_q": w.n_q, "n_k": w.n_k, "D": D,
+                       "pass": "fwd_pruned", "rho": rho, "tile": "128 queries x 128 keys",
+                       "flops": "executed: all tile scores + P.V of admitted tiles"},
+            "pct_of_peak": 100.0 * value / peak,
+            "pruning": {"rho": rho, "tiles_pruned_frac": pruned_frac, "oracle_heads": hs,
+                        "min_decision_margin": margin, "pruned_ms": times["pruned"],
+                        "exact_ms": times["exact"], "speedup": times["exact"] / times["pruned"],
+                        "exact_tflops": flops_exact / (times["exact"] * 1e-3) / 1e12},
+            "parity": {"max_abs_err_o_vs_pruned_oracle": err, "tol": TOL[w.dtype],
+                       "ok": bool(err <= TOL[w.dtype]),
+                       # a decision within 1e-4 of its threshold may round either way
+                       "decisions_unambiguous": bool(margin > 1e-4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -311,6 +380,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--all", action="store_true", help="one JSON line per workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    ap.add_argument("--prune", type=float, default=None, metavar="RHO",
+                    help="time the tile-pruned dense forward (threshold RHO) against the exact one")
     ap.add_argument("--backward", action="store_true",
                     help="time forward + backward for the workload (its step becomes both passes)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -341,6 +412,11 @@ def main():
         print(json.dumps({"copy_probe_bytes": n * 4, "copies": 10}), flush=True)
         return
     osa.load()
+    if args.prune is not None:
+        res = run_pruned(args.workload, args.prune, args.steps, args.warmup, torch, np, osa, W,
+                         oracle)
+        print(json.dumps(res), flush=True)
+        return
     names = W.ORDER if args.all else [args.workload]
     for name in names:
         res = run_workload(name, args.steps, args.warmup, torch, np, osa, W, oracle,

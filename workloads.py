@@ -170,3 +170,13 @@ WORKLOADS = {
 
 # The order the workloads are listed in (index 0 is the small correctness case).
 ORDER = list(WORKLOADS)
+
+# Extra measurement shape (not one of the five above): the dense relation at the
+# causal workload's size, where tile pruning (a dense-only approximation) has
+# enough tiles per query block to act.
+EXTRA = {
+    "dense_n4096_h16_d128_bf16": Workload(
+        "dense_n4096_h16_d128_bf16", 16, 4096, 4096, 128, "bf16", False, 7,
+        description="dense forward, N=4096, H=16, D=128, bf16 (tile-pruning measurement)"),
+}
+WORKLOADS.update(EXTRA)
