@@ -12,7 +12,9 @@ Definitions followed (cited per function in the C file):
   * backward: OCANNL "Module Ir.Online_softmax", the composed-backward bullet,
     in Jacobian form (no D = rowsum(dO * O) shortcut);
   * tile-pruned forward: TIGA-lang "Tile-pruned sparse attention", the
-    admission rule on (query block, key tile) pairs.
+    admission rule on (query block, key tile) pairs;
+  * CSR segment softmax over given edge scores: the relation view of the
+    TIGA-lang attention pages (each destination row's softmax over its edges).
 
 Inputs are float arrays laid out (H, N, D); they are upcast exactly to f64.
 bf16 inputs must be passed already widened to f32 (exact).
@@ -64,6 +66,9 @@ def _load():
             ctypes.c_int, i64, i64, ctypes.c_int, dp, dp, dp, ctypes.c_double, ctypes.c_double,
             ctypes.c_int, ctypes.c_int, dp, dp, dp, ctypes.POINTER(ctypes.c_uint8), dp]
         lib.oracle_attn_fwd_pruned.restype = ctypes.c_int
+        lib.oracle_csr_softmax.argtypes = [ctypes.c_int, i64, i64, ctypes.c_int, ip, ip, dp, dp,
+                                           dp, dp, dp]
+        lib.oracle_csr_softmax.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -172,3 +177,27 @@ def attn_fwd_pruned(q, k, v, scale, rho, br=128, bc=128):
     if st != 0:
         raise ValueError("oracle_attn_fwd_pruned failed with status %d" % st)
     return o, m, l, admit, margin.value
+
+
+def csr_softmax(row_ptr, col_idx, scores, v):
+    """Segment softmax over CSR rows with given edge scores.
+
+    row_ptr (n_dst + 1,) and col_idx (nnz,) int; scores (H, nnz); v (H, n_src, D).
+    Returns (o, m, l) in f64: o (H, n_dst, D), m and l (H, n_dst); empty rows
+    give o = 0, m = -inf, l = 0.
+    """
+    rp = np.ascontiguousarray(np.asarray(row_ptr, dtype=np.int32))
+    ci = np.ascontiguousarray(np.asarray(col_idx, dtype=np.int32))
+    scores, v = _f64(scores), _f64(v)
+    H, n_src, D = v.shape
+    n_dst = len(rp) - 1
+    assert scores.shape == (H, int(rp[-1]))
+    o = np.empty((H, n_dst, D))
+    m = np.empty((H, n_dst))
+    l = np.empty((H, n_dst))
+    ci_p = _ptr(ci, ctypes.c_int32) if len(ci) else ctypes.POINTER(ctypes.c_int32)()
+    st = _load().oracle_csr_softmax(H, n_dst, n_src, D, _ptr(rp, ctypes.c_int32), ci_p,
+                                    _ptr(scores), _ptr(v), _ptr(o), _ptr(m), _ptr(l))
+    if st != 0:
+        raise ValueError("oracle_csr_softmax failed with status %d" % st)
+    return o, m, l

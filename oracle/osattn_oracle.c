@@ -45,6 +45,8 @@
  *   Tile-pruned forward (an approximation, defined on query blocks and key
  *   tiles) -- see oracle_attn_fwd_pruned below.
  *
+ *   CSR segment softmax with given edge scores -- see oracle_csr_softmax.
+ *
  * Layout: every array is (H, N, D) row-major and contiguous, in double.
  * Parallelism: OpenMP over independent (head, row) pairs only; every output
  * element is produced by one thread with a fixed serial summation order, so
@@ -360,6 +362,58 @@ int oracle_attn_fwd_pruned(int H, int64_t n_q, int64_t n_k, int D,
     }
     if (min_margin) *min_margin = margin;
     return status;
+}
+
+/*
+ * CSR segment softmax with field scores -- TIGA-lang "用图组合表达 varlen 因果注意力"
+ * (varlen causal attention by graph composition), its remark that compiled
+ * streaming covers CSR segment softmax over field scores, and the relation
+ * view of "Attention and dense relations": a relation is a set of edges
+ * (j -> i), and each destination row i takes the softmax of its edges'
+ * scores against the source values.  Here the scores are given per edge (a
+ * field), not computed from q and k:
+ *     edges of row i:  e = row_ptr[i] .. row_ptr[i+1]-1, source col_idx[e]
+ *     m_hi = max_e s_he,   l_hi = sum_e exp(s_he - m_hi)
+ *     out_hi = sum_e exp(s_he - m_hi) / l_hi * v_h,col_idx[e]
+ * A row with no edges has out = 0, m = -inf, l = 0 (an empty relation row).
+ * scores is (H, nnz) with nnz = row_ptr[n_dst]; v is (H, n_src, D); o is
+ * (H, n_dst, D); m, l are (H, n_dst).  Returns -1 on malformed CSR
+ * (row_ptr not starting at 0 or decreasing, a column outside [0, n_src)).
+ */
+int oracle_csr_softmax(int H, int64_t n_dst, int64_t n_src, int D,
+                       const int32_t *row_ptr, const int32_t *col_idx,
+                       const double *scores, const double *v,
+                       double *o, double *m, double *l)
+{
+    if (!row_ptr || !scores || !v || !o || !m || !l) return -1;
+    if (H <= 0 || n_dst <= 0 || n_src <= 0 || D <= 0 || row_ptr[0] != 0) return -1;
+    for (int64_t i = 0; i < n_dst; ++i)
+        if (row_ptr[i + 1] < row_ptr[i]) return -1;
+    const int64_t nnz = row_ptr[n_dst];
+    if (nnz > 0 && !col_idx) return -1;
+    for (int64_t e = 0; e < nnz; ++e)
+        if (col_idx[e] < 0 || col_idx[e] >= n_src) return -1;
+
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < (int64_t)H * n_dst; ++r) {
+        const int64_t h = r / n_dst, i = r % n_dst;
+        const double *sh = scores + h * nnz;
+        const double *vh = v + h * n_src * D;
+        double *oi = o + r * D;
+        double mx = -INFINITY;
+        for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e)
+            if (sh[e] > mx) mx = sh[e];
+        double sum = 0.0;
+        for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) sum += exp(sh[e] - mx);
+        for (int d = 0; d < D; ++d) oi[d] = 0.0;
+        for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+            const double p = exp(sh[e] - mx) / sum;
+            for (int d = 0; d < D; ++d) oi[d] += p * vh[(int64_t)col_idx[e] * D + d];
+        }
+        m[r] = mx;
+        l[r] = sum;
+    }
+    return 0;
 }
 
 int oracle_num_threads(void)

@@ -43,6 +43,12 @@ MUTATIONS = {
         "for (int64_t i = i0; i < i1; ++i)\n                    for (int64_t j = j0; j < j1; ++j)",
         "for (int64_t i = i0; i < i0 + 1; ++i)\n                    for (int64_t j = j0; j < j1; ++j)"),
     "prune_running_max_never_moves": ("if (adm[t] && m_tile > m_run) m_run = m_tile;", ""),
+    # CSR segment softmax
+    "csr_segment_end_inclusive": ("for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) sum += exp(sh[e] - mx);",
+                                  "for (int64_t e = row_ptr[i]; e <= row_ptr[i + 1]; ++e) sum += exp(sh[e] - mx);"),
+    "csr_gathers_destination_row": ("oi[d] += p * vh[(int64_t)col_idx[e] * D + d];",
+                                    "oi[d] += p * vh[i * D + d];"),
+    "csr_head_offset_dropped": ("const double *sh = scores + h * nnz;", "const double *sh = scores;"),
     "prune_tile_overlaps_next": ("const int64_t j0 = t * bc, j1 = (j0 + bc < n_k) ? j0 + bc : n_k;",
                                  "const int64_t j0 = t * bc, j1 = (j0 + bc + 1 < n_k) ? j0 + bc + 1 : n_k;"),
 }
@@ -61,6 +67,8 @@ PIN_CALLS = [
     lambda o: pins.test_backward_identities(o, True, [0, 10, 11, 40]),
     lambda o: [pins.test_pruning_golden(o, c) for c in pins.load_pruning()["cases"]],
     lambda o: pins.test_pruning_tiny_rho_is_exact(o, 300, 200, 128, 128),
+    lambda o: pins.test_csr_relation_equals_attention(o, True, [0, 5, 6, 19, 40]),
+    lambda o: pins.test_csr_empty_rows_and_duplicate_edges(o),
 ]
 
 

@@ -452,3 +452,97 @@ def test_pruning_rejects_bad_rho(oracle):
     for rho in (0.0, -0.5, 1.5, float("nan")):
         with pytest.raises(ValueError):
             oracle.attn_fwd_pruned(q, q, q, 0.5, rho, 2, 2)
+
+
+# ------------------------------------------------------------ CSR segment softmax
+def relation_csr(n_q, n_k, causal=False, cu=None):
+    """CSR (row_ptr, col_idx) of the dense / causal / varlen relations."""
+    rows = []
+    for i in range(n_q):
+        lo, hi = 0, n_k
+        if cu is not None:
+            for a, b in zip(cu[:-1], cu[1:]):
+                if a <= i < b:
+                    lo, hi = a, b
+        if causal:
+            hi = min(hi, i + 1)
+        rows.append(list(range(lo, hi)))
+    row_ptr = np.cumsum([0] + [len(r) for r in rows])
+    col_idx = np.array([j for r in rows for j in r], dtype=np.int64)
+    return row_ptr, col_idx
+
+
+def edge_scores(q, k, scale, row_ptr, col_idx):
+    """Scores of every edge, s_e = scale <q_i, k_col(e)>, as a (H, nnz) field."""
+    rows = np.repeat(np.arange(len(row_ptr) - 1), np.diff(row_ptr))
+    return np.einsum("hed,hed->he", q[:, rows], k[:, col_idx]) * scale
+
+
+@pytest.mark.parametrize("causal,cu", [(False, None), (True, None), (True, [0, 5, 6, 19, 40]),
+                                       (False, [0, 7, 7, 30, 40])])
+def test_csr_relation_equals_attention(oracle, causal, cu):
+    # The dense, causal and varlen relations written as CSR with q.k scores
+    # give exactly the attention definition.
+    n = 40
+    q, k, v = rand((2, n, 8), 11), rand((2, n, 8), 12), rand((2, n, 8), 13)
+    row_ptr, col_idx = relation_csr(n, n, causal, cu)
+    o, m, l = oracle.csr_softmax(row_ptr, col_idx, edge_scores(q, k, 0.4, row_ptr, col_idx), v)
+    ro, rm, rl = oracle.attn_fwd(q, k, v, 0.4, causal=causal, cu_seqlens=cu)
+    empty = np.diff(row_ptr) == 0
+    np.testing.assert_allclose(o[:, ~empty], ro[:, ~empty], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(m[:, ~empty], rm[:, ~empty], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l[:, ~empty], rl[:, ~empty], rtol=1e-12, atol=0)
+
+
+def test_csr_rectangular_dense_equals_attention(oracle):
+    q, k, v = rand((1, 9, 4), 21), rand((1, 30, 4), 22), rand((1, 30, 4), 23)
+    row_ptr, col_idx = relation_csr(9, 30)
+    o, m, l = oracle.csr_softmax(row_ptr, col_idx, edge_scores(q, k, 0.5, row_ptr, col_idx), v)
+    ro, rm, rl = oracle.attn_fwd(q, k, v, 0.5)
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", load_golden()["forward"], ids=lambda c: c["name"])
+def test_csr_golden(oracle, case):
+    # The hand-derived forward cases, with their scores given as an edge field.
+    q, k, v = (np.array(case[x], dtype=np.float64) for x in "qkv")
+    rel = case["relation"]
+    n_q, n_k = q.shape[1], k.shape[1]
+    row_ptr, col_idx = relation_csr(n_q, n_k, causal=rel != "dense", cu=case.get("cu_seqlens"))
+    o, m, l = oracle.csr_softmax(row_ptr, col_idx, edge_scores(q, k, case["scale"], row_ptr, col_idx), v)
+    np.testing.assert_allclose(o, np.array(case["o"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(m, np.array(case["m"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, np.array(case["l"]), rtol=1e-12, atol=0)
+
+
+def test_csr_empty_rows_and_duplicate_edges(oracle):
+    # Row 0 has no edges: o = 0, m = -inf, l = 0.  Row 1 lists source 2 twice
+    # with score 0 and source 0 once with score ln 2: weights 1 : 1 : 2, which
+    # is the same as one edge to source 2 with score ln 2 (1 : 1 of mass 2).
+    v = np.array([[[8.0], [100.0], [2.0]]])
+    o, m, l = oracle.csr_softmax([0, 0, 3], [2, 2, 0], np.array([[0.0, 0.0, math.log(2)]]), v)
+    assert o[0, 0, 0] == 0.0 and m[0, 0] == -math.inf and l[0, 0] == 0.0
+    assert abs(o[0, 1, 0] - (2 + 2 + 2 * 8) / 4) < 1e-12
+    assert abs(m[0, 1] - math.log(2)) < 1e-15 and abs(l[0, 1] - 2.0) < 1e-12
+
+
+def test_csr_edge_order_is_free(oracle):
+    rng = np.random.default_rng(5)
+    deg = rng.integers(0, 9, size=50)
+    row_ptr = np.concatenate([[0], np.cumsum(deg)])
+    col_idx = rng.integers(0, 30, size=row_ptr[-1])
+    s = rng.standard_normal((2, row_ptr[-1]))
+    v = rng.standard_normal((2, 30, 5))
+    perm = np.concatenate([rng.permutation(np.arange(a, b)) for a, b in zip(row_ptr[:-1], row_ptr[1:])]
+                          ).astype(np.int64)
+    a = oracle.csr_softmax(row_ptr, col_idx, s, v)
+    b = oracle.csr_softmax(row_ptr, col_idx[perm], s[:, perm], v)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-14)
+
+
+def test_csr_rejects_malformed(oracle):
+    v = np.zeros((1, 3, 2))
+    for rp, ci in (([1, 2], [0]), ([0, 2, 1], [0, 1]), ([0, 1], [3]), ([0, 1], [-1])):
+        with pytest.raises(ValueError):
+            oracle.csr_softmax(rp, ci, np.zeros((1, max(rp[-1], 0))), v)
