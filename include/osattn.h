@@ -160,6 +160,34 @@ int osattn_fwd_pruned(int dtype, int H, int64_t n_q, int64_t n_k, int d,
                       void *stream);
 
 /*
+ * CSR segment softmax with given edge scores: for every head h and
+ * destination row i with edges e = row_ptr[i] .. row_ptr[i+1]-1 to sources
+ * col_idx[e],
+ *     m_hi = max_e s_he,  l_hi = sum_e exp(s_he - m_hi),
+ *     o_hi = sum_e exp(s_he - m_hi) / l_hi * v_h,col_idx[e]
+ * (the relation view of TIGA-lang's attention pages -- each row's softmax
+ * over its edges -- with the scores supplied as an edge field, the CSR case
+ * the varlen-by-graph-composition section names for compiled streaming).
+ * Dense, causal and varlen attention are special relations of this form.
+ *
+ * row_ptr: n_dst + 1 int32 (device), non-decreasing from 0 to nnz; col_idx:
+ * nnz int32 (device) in [0, n_src); scores: f32 (H, nnz) with head stride
+ * scores_stride_h (elements), finite; v: (H, n_src, d) of dtype with element
+ * strides v_stride_h, v_stride_n (16-byte aligned rows); o: f32 (H, n_dst, d)
+ * with its own strides; m, l: f32 (H, n_dst).  d = 64 or 128; dtype any.
+ * A row with no edges gets o = 0, m = -inf, l = 0.  The CSR arrays live on
+ * the device and are not checked: the kernel clamps them into range, so a
+ * malformed CSR gives wrong results but no out-of-bounds access.  No
+ * workspace, no atomics; asynchronous on `stream`.
+ */
+int osattn_csr_softmax(int dtype, int H, int64_t n_dst, int64_t n_src, int d,
+                       const int32_t *row_ptr, const int32_t *col_idx, int64_t nnz,
+                       const float *scores, int64_t scores_stride_h,
+                       const void *v, int64_t v_stride_h, int64_t v_stride_n,
+                       float *o, int64_t o_stride_h, int64_t o_stride_n,
+                       float *m, float *l, void *stream);
+
+/*
  * Bytes of device workspace osattn_bwd needs for this problem (the per-row
  * D vector and statistics, plus partial gradient sums when the launch splits
  * a reduction across workgroups).  Returns 0 for unsupported or invalid

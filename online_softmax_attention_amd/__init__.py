@@ -29,8 +29,8 @@ LIB_PATH = os.path.join(_HERE, "libosattn.so")
 F32, F16, BF16 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_HIP, ERR_WORKSPACE = range(6)
 EXPORTS = ("osattn_fwd", "osattn_fwd_workspace_bytes", "osattn_fwd_pruned", "osattn_bwd",
-           "osattn_bwd_workspace_bytes", "osattn_status_string", "osattn_last_error",
-           "osattn_version")
+           "osattn_bwd_workspace_bytes", "osattn_csr_softmax", "osattn_status_string",
+           "osattn_last_error", "osattn_version")
 
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 _lib = None
@@ -58,6 +58,9 @@ def load(path: Optional[str] = None):
     lib.osattn_fwd_pruned.argtypes = [i32, i32, i64, i64, i32, vp, vp, vp, i64, i64, i64, i64,
                                       vp, i64, i64, vp, vp, f32, f32, vp]
     lib.osattn_fwd_pruned.restype = i32
+    lib.osattn_csr_softmax.argtypes = [i32, i32, i64, i64, i32, vp, vp, i64, vp, i64, vp, i64, i64,
+                                       vp, i64, i64, vp, vp, vp]
+    lib.osattn_csr_softmax.restype = i32
     lib.osattn_fwd_workspace_bytes.argtypes = [i32, i32, i64, i64, i32, i32, vp, i32, i32]
     lib.osattn_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.osattn_bwd_workspace_bytes.argtypes = [i32, i32, i64, i64, i32, i32, vp, i32, i32]
@@ -212,6 +215,39 @@ def fwd_pruned(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: float,
                                v.data_ptr(), q_sh, q_sn, kv_sh, kv_sn, o.data_ptr(), o_sh, o_sn,
                                m.data_ptr(), l.data_ptr(), scale, float(rho), _stream())
     _check(st, "osattn_fwd_pruned")
+    return o, m, l
+
+
+def csr_softmax(row_ptr: torch.Tensor, col_idx: torch.Tensor, scores: torch.Tensor,
+                v: torch.Tensor, out=None):
+    """CSR segment softmax with given edge scores; returns (o, m, l).
+
+    row_ptr (n_dst + 1,), col_idx (nnz,) int32 device tensors; scores (H, nnz)
+    float32 with a contiguous last dimension; v (H, n_src, D)."""
+    lib = load()
+    if v.dtype not in _DT:
+        raise ValueError("v must be float32, float16 or bfloat16")
+    for t, name in ((row_ptr, "row_ptr"), (col_idx, "col_idx")):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous 1-D int32 device tensor" % name)
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores must be a float32 (H, nnz) tensor with a contiguous last dimension")
+    H, n_src, D, v_sh, v_sn = _hn(v, "hnd")
+    n_dst, nnz = row_ptr.numel() - 1, col_idx.numel()
+    if scores.shape != (H, nnz):
+        raise ValueError("scores must be (H, nnz) = (%d, %d)" % (H, nnz))
+    if out is None:
+        o = torch.empty((H, n_dst, D), dtype=torch.float32, device=v.device)
+        m = torch.empty((H, n_dst), dtype=torch.float32, device=v.device)
+        l = torch.empty((H, n_dst), dtype=torch.float32, device=v.device)
+    else:
+        o, m, l = out
+    st = lib.osattn_csr_softmax(_DT[v.dtype], H, n_dst, n_src, D, row_ptr.data_ptr(),
+                                col_idx.data_ptr() if nnz else None, nnz,
+                                scores.data_ptr() if nnz else None, scores.stride(0), v.data_ptr(),
+                                v_sh, v_sn, o.data_ptr(), o.stride(0), o.stride(1), m.data_ptr(),
+                                l.data_ptr(), _stream())
+    _check(st, "osattn_csr_softmax")
     return o, m, l
 
 

@@ -72,6 +72,19 @@ struct BwdParams {
     int k_splits;          // query-range splits of the dK/dV reduction
 };
 
+// CSR segment softmax over given edge scores.
+struct CsrParams {
+    const int32_t *row_ptr, *col_idx;  // device CSR (clamped, never trusted)
+    const float *scores;               // (H, nnz) f32, head stride s_sh
+    int64_t s_sh;
+    const void *v;                     // (H, n_src, D) with strides v_sh, v_sn
+    int64_t v_sh, v_sn;
+    float *o;                          // (H, n_dst, D) f32
+    int64_t o_sh, o_sn;
+    float *m, *l;                      // (H, n_dst)
+    int H, n_dst, n_src, nnz;
+};
+
 struct ReduceParams {
     const float *part;     // (splits, H, n, D) contiguous
     void *out;             // (H, n, D) with strides out_sh, out_sn

@@ -15,6 +15,7 @@ hipError_t launch_forward(int dtype, int d, int mask, FwdParams p, int max_seqle
 hipError_t launch_backward(int mask, BwdParams p, int seqs, hipStream_t st);
 hipError_t launch_backward16(int dtype, int d, int mask, BwdParams p, int seqs, hipStream_t st);
 hipError_t launch_forward_pruned(int dtype, int d, FwdParams p, hipStream_t st);
+hipError_t launch_csr_softmax(int dtype, int d, const CsrParams &p, hipStream_t st);
 }  // namespace osattn
 
 using namespace osattn;
@@ -356,6 +357,39 @@ int osattn_fwd_pruned(int dtype, int H, int64_t n_q, int64_t n_k, int d, const v
     p.prune_thr = logf(rho) / scale;
     const hipError_t e = launch_forward_pruned(dtype, d, p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(OSATTN_ERR_HIP, "pruned forward launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int osattn_csr_softmax(int dtype, int H, int64_t n_dst, int64_t n_src, int d,
+                       const int32_t *row_ptr, const int32_t *col_idx, int64_t nnz,
+                       const float *scores, int64_t scores_stride_h, const void *v,
+                       int64_t v_stride_h, int64_t v_stride_n, float *o, int64_t o_stride_h,
+                       int64_t o_stride_n, float *m, float *l, void *stream) {
+    if (dtype != OSATTN_F32 && dtype != OSATTN_F16 && dtype != OSATTN_BF16)
+        return fail(OSATTN_ERR_INVALID_ARG, "dtype %d is not OSATTN_F32/F16/BF16", dtype);
+    if (H <= 0 || n_dst <= 0 || n_src <= 0 || nnz < 0)
+        return fail(OSATTN_ERR_INVALID_ARG, "H, n_dst, n_src must be positive and nnz >= 0");
+    if (n_dst > kMaxLen || n_src > kMaxLen || nnz > 0x7fffffffLL)
+        return fail(OSATTN_ERR_UNSUPPORTED, "n_dst, n_src must be <= 2^30 and nnz < 2^31");
+    if (d != 64 && d != 128) return fail(OSATTN_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", d);
+    if (!row_ptr) return fail(OSATTN_ERR_INVALID_ARG, "row_ptr is NULL");
+    if (nnz > 0 && (!col_idx || !scores))
+        return fail(OSATTN_ERR_INVALID_ARG, "col_idx and scores must not be NULL when nnz > 0");
+    if (scores_stride_h < 0) return fail(OSATTN_ERR_INVALID_ARG, "scores_stride_h is negative");
+    int st;
+    const size_t es = elem_size(dtype);
+    if ((st = check_tensor("v", v, v_stride_h, v_stride_n, es))) return st;
+    if ((st = check_tensor("o", o, o_stride_h, o_stride_n, 4))) return st;
+    if (!m || !l) return fail(OSATTN_ERR_INVALID_ARG, "m and l must not be NULL");
+    CsrParams p{};
+    p.row_ptr = row_ptr; p.col_idx = col_idx;
+    p.scores = scores; p.s_sh = scores_stride_h;
+    p.v = v; p.v_sh = v_stride_h; p.v_sn = v_stride_n;
+    p.o = o; p.o_sh = o_stride_h; p.o_sn = o_stride_n;
+    p.m = m; p.l = l;
+    p.H = H; p.n_dst = (int)n_dst; p.n_src = (int)n_src; p.nnz = (int)nnz;
+    const hipError_t e = launch_csr_softmax(dtype, d, p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(OSATTN_ERR_HIP, "csr softmax launch: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -192,3 +192,27 @@ def fwd_pruned(lib, dtype=F16, H=1, n_q=256, n_k=128, d=64, rho=0.5, m=None, sca
 ])
 def test_fwd_pruned_rejects_on_host(lib, kw, status):
     assert fwd_pruned(lib, **kw) == status
+
+
+# CSR segment softmax: every case fails a host check before any launch.
+def csr(lib, dtype=F16, H=1, n_dst=16, n_src=16, d=64, nnz=32, rp=A + 0x100000, ci=A + 0x200000,
+        sc=A + 0x300000, v=B, o=O, m=None, l=L):
+    return lib.osattn_csr_softmax(dtype, H, n_dst, n_src, d, rp, ci, nnz, sc, nnz, v, n_src * d, d,
+                                  o, n_dst * d, d, m, l, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), osa.ERR_INVALID_ARG),
+    (dict(n_dst=0), osa.ERR_INVALID_ARG),
+    (dict(nnz=-1), osa.ERR_INVALID_ARG),
+    (dict(nnz=1 << 31), osa.ERR_UNSUPPORTED),
+    (dict(d=96), osa.ERR_UNSUPPORTED),
+    (dict(rp=None), osa.ERR_INVALID_ARG),
+    (dict(ci=None), osa.ERR_INVALID_ARG),
+    (dict(sc=None), osa.ERR_INVALID_ARG),
+    (dict(v=B + 4), osa.ERR_ALIGNMENT),
+    (dict(o=O + 8), osa.ERR_ALIGNMENT),
+    (dict(), osa.ERR_INVALID_ARG),  # m is NULL: the last check
+])
+def test_csr_rejects_on_host(lib, kw, status):
+    assert csr(lib, **kw) == status

@@ -418,3 +418,41 @@ def test_pruned_tiny_rho_is_exact(osattn, oracle, dtype, D):
     torch.cuda.synchronize()
     ro, rm, rl = oracle.attn_fwd(inp.q32, inp.k32, inp.v32, inp.w.softmax_scale)
     assert_fwd_close(host(o), host(m), host(l), ro, rm, rl, dtype, "pruned, rho -> 0")
+
+
+# ------------------------------------------------------------ CSR segment softmax
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("f16", 64), ("bf16", 128), ("f16", 128), ("f32", 128)])
+def test_csr_softmax_parity(osattn, oracle, dtype, D):
+    # Heavy-tailed degrees (up to 300, several 64-edge passes), empty rows,
+    # repeated sources.
+    row_ptr, col_idx = W.csr_graph(77, 500, 700, 24, 300, empty_frac=0.05)
+    assert (np.diff(row_ptr) == 0).any() and np.diff(row_ptr).max() > 64
+    H = 2
+    scores, v, vw = W.csr_inputs(78, H, 700, len(col_idx), D, dtype)
+    o, m, l = osattn.csr_softmax(torch.tensor(row_ptr, device="cuda"), torch.tensor(col_idx, device="cuda"),
+                                 torch.tensor(scores, device="cuda"), to_dev(v, dtype))
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.csr_softmax(row_ptr, col_idx, scores, vw)
+    empty = np.diff(row_ptr) == 0
+    o, m, l = host(o), host(m), host(l)
+    assert np.all(o[:, empty] == 0) and np.all(l[:, empty] == 0) and np.all(np.isneginf(m[:, empty]))
+    assert_fwd_close(o[:, ~empty], m[:, ~empty], l[:, ~empty], ro[:, ~empty], rm[:, ~empty],
+                     rl[:, ~empty], dtype, "csr %s D=%d" % (dtype, D))
+
+
+def test_csr_softmax_causal_relation_matches_attention(osattn, oracle):
+    # The causal relation as CSR with q.k scores gives causal attention.
+    n, H, D = 200, 2, 64
+    inp = W.make_inputs(small("csr", H, n, n, D, "f16", True, 79))
+    rows = [list(range(i + 1)) for i in range(n)]
+    row_ptr = np.cumsum([0] + [len(r) for r in rows]).astype(np.int32)
+    col_idx = np.array([j for r in rows for j in r], dtype=np.int32)
+    dst = np.repeat(np.arange(n), np.diff(row_ptr))
+    scores = np.ascontiguousarray((np.einsum("hed,hed->he", inp.q32[:, dst].astype(np.float64),
+                                             inp.k32[:, col_idx].astype(np.float64))
+                                   * inp.w.softmax_scale).astype(np.float32))
+    o, m, l = osattn.csr_softmax(torch.tensor(row_ptr, device="cuda"), torch.tensor(col_idx, device="cuda"),
+                                 torch.tensor(scores, device="cuda"), to_dev(inp.v, "f16"))
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attn_fwd(inp.q32, inp.k32, inp.v32, inp.w.softmax_scale, causal=True)
+    assert_fwd_close(host(o), host(m), host(l), ro, rm, rl, "f16", "csr causal relation")

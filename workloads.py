@@ -180,3 +180,36 @@ EXTRA = {
         description="dense forward, N=4096, H=16, D=128, bf16 (tile-pruning measurement)"),
 }
 WORKLOADS.update(EXTRA)
+
+
+# ------------------------------------------------------------------ CSR graphs
+def csr_graph(seed: int, n_dst: int, n_src: int, mean_degree: float, max_degree: int,
+              empty_frac: float = 0.02):
+    """A seeded random CSR relation: heavy-tailed row degrees (Pareto, shape 2,
+    scaled to `mean_degree`, clipped to `max_degree`), `empty_frac` of the rows
+    with no edges, and sources drawn uniformly.  Returns int32 arrays
+    (row_ptr (n_dst + 1,), col_idx (nnz,))."""
+    rng = np.random.default_rng(seed)
+    deg = np.floor((rng.pareto(2.0, size=n_dst) + 1.0) * (mean_degree / 2.0)).astype(np.int64)
+    deg = np.clip(deg, 1, max_degree)
+    deg[rng.random(n_dst) < empty_frac] = 0
+    row_ptr = np.zeros(n_dst + 1, dtype=np.int64)
+    np.cumsum(deg, out=row_ptr[1:])
+    col_idx = rng.integers(0, n_src, size=int(row_ptr[-1]))
+    return row_ptr.astype(np.int32), col_idx.astype(np.int32)
+
+
+def csr_inputs(seed: int, H: int, n_src: int, nnz: int, D: int, dtype: str):
+    """Edge scores (H, nnz) f32 ~ N(0, 1) and values (H, n_src, D) ~ N(0, 1)
+    rounded to dtype; returns (scores, v_stored, v_widened_f32)."""
+    rng = np.random.default_rng(seed + 1)
+    scores = rng.standard_normal((H, nnz), dtype=np.float32)
+    v32 = rng.standard_normal((H, n_src, D), dtype=np.float32)
+    v, vw = round_to_dtype(v32, dtype)
+    return scores, v, vw
+
+
+# The CSR measurement workload: 65536 rows over 65536 sources, mean degree 32.
+CSR_WORKLOAD = {"name": "csr_n65536_deg32_h4_d64_f16", "seed": 4242, "n_dst": 65536,
+                "n_src": 65536, "mean_degree": 32, "max_degree": 2048, "H": 4, "D": 64,
+                "dtype": "f16"}
