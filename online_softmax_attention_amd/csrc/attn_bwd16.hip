@@ -148,31 +148,15 @@ __device__ __forceinline__ typename Half8<T>::vec tr_operand(const char *tile, i
 }
 
 // ---------------------------------------------------------------- B1
+// One 128-key tile: keys [k_lo, min(k_lo + 128, ks.hi)) against the queries
+// of qs_all (from k_lo on when causal), part `split` of k_splits.
 template <typename T, int D, int MASK>
-__global__ void __launch_bounds__(kB16T) bwd16_dkdv_kernel(BwdParams p) {
+__device__ __forceinline__ void dkdv16_tile(const BwdParams &p, char *smem, int h, int split,
+                                            Range16 ks, Range16 qs_all, int k_lo) {
     typedef Bwd16Cfg<D> C;
     typedef typename Half8<T>::vec vec8;
     constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
-    constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
     constexpr int esz = (int)sizeof(T);
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS_DKDV];
-
-    const int b = blockIdx.x;
-    const int h = b % p.H;
-    int rest = b / p.H;
-    const int split = rest % p.k_splits;
-    rest /= p.k_splits;
-    int seq = 0;
-    if (varlen) {
-        seq = rest % p.num_seqs;
-        rest /= p.num_seqs;
-    }
-    // Causal key tiles are issued heaviest (earliest keys: most queries) first.
-    const int ktile = rest;
-    const Range16 ks = axis16<varlen>(p, seq, p.n_k);
-    const Range16 qs_all = axis16<varlen>(p, seq, p.n_q);
-    const int k_lo = ks.lo + ktile * C::BK;
-    if (k_lo >= ks.hi) return;
     const int k_hi = min(k_lo + C::BK, ks.hi);
     const int qa = causal ? max(qs_all.lo, k_lo) : qs_all.lo;
     const Range16 qr = split16(qa, qs_all.hi, split, p.k_splits, C::BQ);
@@ -331,54 +315,82 @@ __global__ void __launch_bounds__(kB16T) bwd16_dkdv_kernel(BwdParams p) {
             }
     }
     __syncthreads();
-    if (qg != 0 || key >= k_hi) return;
+    if (qg == 0 && key < k_hi) {
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
+        for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const f32x4 a = sm[((kq * 2 + 0) * (D / 8) + dt * 4 + jj) * 64 + lane];
-            const f32x4 v = sm[((kq * 2 + 1) * (D / 8) + dt * 4 + jj) * 64 + lane];
+            for (int jj = 0; jj < 4; ++jj) {
+                const f32x4 a = sm[((kq * 2 + 0) * (D / 8) + dt * 4 + jj) * 64 + lane];
+                const f32x4 v = sm[((kq * 2 + 1) * (D / 8) + dt * 4 + jj) * 64 + lane];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                dK[dt][4 * jj + e] += a[e];
-                dV[dt][4 * jj + e] += v[e];
+                for (int e = 0; e < 4; ++e) {
+                    dK[dt][4 * jj + e] += a[e];
+                    dV[dt][4 * jj + e] += v[e];
+                }
             }
+        if (p.k_splits == 1) {
+            store_row16<T, C::NDT>(static_cast<T *>(p.dk) + (int64_t)h * p.kv_sh + (int64_t)key * p.kv_sn, dK, g, p.scale);
+            store_row16<T, C::NDT>(static_cast<T *>(p.dv) + (int64_t)h * p.kv_sh + (int64_t)key * p.kv_sn, dV, g, 1.f);
+        } else {
+            const int64_t off = (((int64_t)split * p.H + h) * p.n_k + key) * D;
+            store_row_part<C::NDT>(p.dk_part + off, dK, g, p.scale);
+            store_row_part<C::NDT>(p.dv_part + off, dV, g, 1.f);
         }
-    if (p.k_splits == 1) {
-        store_row16<T, C::NDT>(static_cast<T *>(p.dk) + (int64_t)h * p.kv_sh + (int64_t)key * p.kv_sn, dK, g, p.scale);
-        store_row16<T, C::NDT>(static_cast<T *>(p.dv) + (int64_t)h * p.kv_sh + (int64_t)key * p.kv_sn, dV, g, 1.f);
+    }
+    __syncthreads();  // the next tile reuses this LDS
+}
+
+// SCHED: varlen items from the sorted work list (one or two tiles each);
+// otherwise one tile of the natural grid.
+template <typename T, int D, int MASK, bool SCHED>
+__global__ void __launch_bounds__(kB16T) bwd16_dkdv_kernel(BwdParams p) {
+    constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
+    __shared__ __attribute__((aligned(16))) char smem[Bwd16Cfg<D>::LDS_DKDV];
+    const int b = blockIdx.x;
+    const int h = b % p.H;
+    int rest = b / p.H;
+    // The item: a key range [lo, hi) with up to two 128-key tiles of it, and
+    // the query range [qlo, qhi) those keys meet.
+    int split = 0, lo, hi, qlo, qhi, t0, t1 = -1;
+    if constexpr (SCHED) {  // tiles (T-1-i, i) of one sequence, largest pairs first
+        const int4 it = reinterpret_cast<const int4 *>(p.sched + 4)[rest];
+        lo = qlo = it.x; hi = qhi = it.y; t0 = it.z; t1 = it.w;
     } else {
-        const int64_t off = (((int64_t)split * p.H + h) * p.n_k + key) * D;
-        store_row_part<C::NDT>(p.dk_part + off, dK, g, p.scale);
-        store_row_part<C::NDT>(p.dv_part + off, dV, g, 1.f);
+        split = rest % p.k_splits;
+        rest /= p.k_splits;
+        int seq = 0;
+        if (varlen) {
+            seq = rest % p.num_seqs;
+            rest /= p.num_seqs;
+        }
+        const Range16 ks = axis16<varlen>(p, seq, p.n_k), qs = axis16<varlen>(p, seq, p.n_q);
+        lo = ks.lo; hi = ks.hi; qlo = qs.lo; qhi = qs.hi;
+        t0 = rest;  // causal: key tile 0 (the most queries) first
+    }
+    if constexpr (SCHED) {
+#pragma unroll 1
+        for (int k = 0; k < 2; ++k) {
+            const int t = k == 0 ? t0 : t1;
+            if (t < 0 || lo + t * 128 >= hi) break;
+            dkdv16_tile<T, D, MASK>(p, smem, h, split, {lo, hi}, {qlo, qhi}, lo + t * 128);
+        }
+    } else {
+        (void)t1;
+        if (t0 < 0 || lo + t0 * 128 >= hi) return;
+        dkdv16_tile<T, D, MASK>(p, smem, h, split, {lo, hi}, {qlo, qhi}, lo + t0 * 128);
     }
 }
 
 // ---------------------------------------------------------------- B2
+// One 128-query tile: rows [q_lo, min(q_lo + 128, qs_all.hi)) against the keys
+// of ks_all (up to the tile end when causal), part `split` of q_splits.
 template <typename T, int D, int MASK>
-__global__ void __launch_bounds__(kB16T) bwd16_dq_kernel(BwdParams p) {
+__device__ __forceinline__ void dq16_tile(const BwdParams &p, char *smem, int h, int split,
+                                          Range16 qs_all, Range16 ks_all, int q_lo) {
     typedef Bwd16Cfg<D> C;
     typedef typename Half8<T>::vec vec8;
     constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
-    constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
     constexpr int esz = (int)sizeof(T);
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS_DQ];
-
-    const int b = blockIdx.x;
-    const int h = b % p.H;
-    int rest = b / p.H;
-    const int split = rest % p.q_splits;
-    rest /= p.q_splits;
-    int seq = 0;
-    if (varlen) {
-        seq = rest % p.num_seqs;
-        rest /= p.num_seqs;
-    }
-    const int qtile = causal ? (p.q_tiles - 1 - rest) : rest;  // causal: heaviest first
-    const Range16 qs_all = axis16<varlen>(p, seq, p.n_q);
-    const Range16 ks_all = axis16<varlen>(p, seq, p.n_k);
-    const int q_lo = qs_all.lo + qtile * 128;
-    if (qtile < 0 || q_lo >= qs_all.hi) return;
     const int q_hi = min(q_lo + 128, qs_all.hi);
     const int kv_end = causal ? q_hi : ks_all.hi;
     const Range16 kr = split16(ks_all.lo, kv_end, split, p.q_splits, C::BC);
@@ -507,20 +519,64 @@ __global__ void __launch_bounds__(kB16T) bwd16_dq_kernel(BwdParams p) {
             }
     }
     __syncthreads();
-    if (kg != 0 || !qok) return;
+    if (kg == 0 && qok) {
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
+        for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const f32x4 a = sm[(rg * (D / 8) + dt * 4 + jj) * 64 + lane];
+            for (int jj = 0; jj < 4; ++jj) {
+                const f32x4 a = sm[(rg * (D / 8) + dt * 4 + jj) * 64 + lane];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dQ[dt][4 * jj + e] += a[e];
+                for (int e = 0; e < 4; ++e) dQ[dt][4 * jj + e] += a[e];
+            }
+        if (p.q_splits == 1) {
+            store_row16<T, C::NDT>(static_cast<T *>(p.dq) + (int64_t)h * p.q_sh + (int64_t)qrow * p.q_sn, dQ, g, p.scale);
+        } else {
+            const int64_t off = (((int64_t)split * p.H + h) * p.n_q + qrow) * D;
+            store_row_part<C::NDT>(p.dq_part + off, dQ, g, p.scale);
         }
-    if (p.q_splits == 1) {
-        store_row16<T, C::NDT>(static_cast<T *>(p.dq) + (int64_t)h * p.q_sh + (int64_t)qrow * p.q_sn, dQ, g, p.scale);
+    }
+    __syncthreads();  // the next tile reuses this LDS
+}
+
+// SCHED: varlen items from the sorted work list (one or two tiles each);
+// otherwise one tile of the natural grid.
+template <typename T, int D, int MASK, bool SCHED>
+__global__ void __launch_bounds__(kB16T) bwd16_dq_kernel(BwdParams p) {
+    constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
+    constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
+    __shared__ __attribute__((aligned(16))) char smem[Bwd16Cfg<D>::LDS_DQ];
+    const int b = blockIdx.x;
+    const int h = b % p.H;
+    int rest = b / p.H;
+    // The item: a query range [lo, hi) with up to two 128-query tiles of it,
+    // and the key range [klo, khi) those queries meet.
+    int split = 0, lo, hi, klo, khi, t0, t1 = -1;
+    if constexpr (SCHED) {  // tiles (T-1-i, i) of one sequence, largest pairs first
+        const int4 it = reinterpret_cast<const int4 *>(p.sched + 4)[rest];
+        lo = klo = it.x; hi = khi = it.y; t0 = it.z; t1 = it.w;
     } else {
-        const int64_t off = (((int64_t)split * p.H + h) * p.n_q + qrow) * D;
-        store_row_part<C::NDT>(p.dq_part + off, dQ, g, p.scale);
+        split = rest % p.q_splits;
+        rest /= p.q_splits;
+        int seq = 0;
+        if (varlen) {
+            seq = rest % p.num_seqs;
+            rest /= p.num_seqs;
+        }
+        const Range16 qs = axis16<varlen>(p, seq, p.n_q), ks = axis16<varlen>(p, seq, p.n_k);
+        lo = qs.lo; hi = qs.hi; klo = ks.lo; khi = ks.hi;
+        t0 = causal ? (p.q_tiles - 1 - rest) : rest;  // causal: heaviest first
+    }
+    if constexpr (SCHED) {
+#pragma unroll 1
+        for (int k = 0; k < 2; ++k) {
+            const int t = k == 0 ? t0 : t1;
+            if (t < 0 || lo + t * 128 >= hi) break;
+            dq16_tile<T, D, MASK>(p, smem, h, split, {lo, hi}, {klo, khi}, lo + t * 128);
+        }
+    } else {
+        (void)t1;
+        if (t0 < 0 || lo + t0 * 128 >= hi) return;
+        dq16_tile<T, D, MASK>(p, smem, h, split, {lo, hi}, {klo, khi}, lo + t0 * 128);
     }
 }
 
@@ -546,11 +602,22 @@ __global__ void __launch_bounds__(256) bwd16_reduce_kernel(ReduceParams r) {
 // ------------------------------------------------------------------ launch
 template <typename T, int D, int MASK>
 static void launch_bwd16_mask(const BwdParams &p, int grid_k, int grid_q, hipStream_t st) {
+    constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
+    if (varlen && p.sched) {
+        if (grid_k > 0)
+            hipLaunchKernelGGL((bwd16_dkdv_kernel<T, D, MASK, varlen>), dim3(grid_k), dim3(kB16T), 0, st, p);
+        if (grid_q > 0)
+            hipLaunchKernelGGL((bwd16_dq_kernel<T, D, MASK, varlen>), dim3(grid_q), dim3(kB16T), 0, st, p);
+        return;
+    }
     if (grid_k > 0)
-        hipLaunchKernelGGL((bwd16_dkdv_kernel<T, D, MASK>), dim3(grid_k), dim3(kB16T), 0, st, p);
+        hipLaunchKernelGGL((bwd16_dkdv_kernel<T, D, MASK, false>), dim3(grid_k), dim3(kB16T), 0, st, p);
     if (grid_q > 0)
-        hipLaunchKernelGGL((bwd16_dq_kernel<T, D, MASK>), dim3(grid_q), dim3(kB16T), 0, st, p);
+        hipLaunchKernelGGL((bwd16_dq_kernel<T, D, MASK, false>), dim3(grid_q), dim3(kB16T), 0, st, p);
 }
+
+hipError_t launch_varlen_schedule(int d, int causal, const int32_t *cu, int num_seqs, int n,
+                                  int32_t *sched, int sched_max, int sched_shift, hipStream_t st);
 
 template <typename T, int D>
 static hipError_t launch_bwd16_typed(int mask, const BwdParams &p, int seqs, hipStream_t st) {
@@ -558,8 +625,9 @@ static hipError_t launch_bwd16_typed(int mask, const BwdParams &p, int seqs, hip
     hipLaunchKernelGGL((bwd16_pre_kernel<T, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t grid_k = (int64_t)p.H * p.k_splits * seqs * p.k_tiles;
-    const int64_t grid_q = (int64_t)p.H * p.q_splits * seqs * p.q_tiles;
+    int64_t grid_k = (int64_t)p.H * p.k_splits * seqs * p.k_tiles;
+    int64_t grid_q = (int64_t)p.H * p.q_splits * seqs * p.q_tiles;
+    if (p.sched) grid_k = grid_q = (int64_t)p.H * p.sched_max;  // one workgroup per listed pair
     if (grid_k > 0x7fffffffLL || grid_q > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     switch (mask) {
         case kDense: launch_bwd16_mask<T, D, kDense>(p, (int)grid_k, (int)grid_q, st); break;
@@ -583,7 +651,15 @@ static hipError_t launch_bwd16_typed(int mask, const BwdParams &p, int seqs, hip
 }
 
 // Host entry for fp16/bf16 (dtype 1 / 2), d = 64 or 128 (validated by the ABI).
-hipError_t launch_backward16(int dtype, int d, int mask, BwdParams p, int seqs, hipStream_t st) {
+// With p.sched set (varlen), the work list is written first.
+hipError_t launch_backward16(int dtype, int d, int mask, BwdParams p, int seqs, int sched_shift,
+                             hipStream_t st) {
+    if (p.sched) {
+        const hipError_t e = launch_varlen_schedule(d, mask == kVarlenCausal, p.cu, p.num_seqs, p.n_q,
+                                                    const_cast<int32_t *>(p.sched), p.sched_max,
+                                                    sched_shift, st);
+        if (e != hipSuccess) return e;
+    }
     if (dtype == 1)
         return d == 64 ? launch_bwd16_typed<_Float16, 64>(mask, p, seqs, st)
                        : launch_bwd16_typed<_Float16, 128>(mask, p, seqs, st);

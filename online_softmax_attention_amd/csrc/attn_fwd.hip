@@ -721,6 +721,28 @@ __global__ void __launch_bounds__(kT16) fwd16_kernel(FwdParams p) {
     }
 }
 
+// The varlen work list on its own (the fp16/bf16 backward orders its tile pairs
+// with it): the same kernel and key block as the forward of width d.
+hipError_t launch_varlen_schedule(int d, int causal, const int32_t *cu, int num_seqs, int n,
+                                  int32_t *sched, int sched_max, int sched_shift, hipStream_t st) {
+    FwdParams p{};
+    p.cu = cu;
+    p.num_seqs = num_seqs;
+    p.n_q = n;
+    p.sched = sched;
+    p.sched_max = sched_max;
+    p.sched_shift = sched_shift;
+    const dim3 g1(1), b1(kSchedThreads);
+    if (d == 64) {
+        if (causal) hipLaunchKernelGGL((varlen_schedule_kernel<Fwd16Cfg<64, 2>::BC, true>), g1, b1, 0, st, p);
+        else hipLaunchKernelGGL((varlen_schedule_kernel<Fwd16Cfg<64, 2>::BC, false>), g1, b1, 0, st, p);
+    } else {
+        if (causal) hipLaunchKernelGGL((varlen_schedule_kernel<Fwd16Cfg<128, 2>::BC, true>), g1, b1, 0, st, p);
+        else hipLaunchKernelGGL((varlen_schedule_kernel<Fwd16Cfg<128, 2>::BC, false>), g1, b1, 0, st, p);
+    }
+    return hipGetLastError();
+}
+
 // Tile-pruned dense forward: one 128-row tile per workgroup, key blocks of 128
 // (D = 64 uses four stages of 128 keys so that both widths prune 128 x 128
 // tiles).

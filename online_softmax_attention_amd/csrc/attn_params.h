@@ -70,6 +70,11 @@ struct BwdParams {
     int q_tiles, k_tiles;  // tiles per (head, sequence) for the dQ / dKdV kernels
     int q_splits;          // key-range splits of the dQ reduction
     int k_splits;          // query-range splits of the dK/dV reduction
+    // fp16/bf16 varlen: the forward's sorted work list of tile pairs (same
+    // layout as FwdParams::sched), written into the workspace before the
+    // dK/dV and dQ launches; null for the natural grid.
+    const int32_t *sched;
+    int sched_max;
 };
 
 // CSR segment softmax over given edge scores.

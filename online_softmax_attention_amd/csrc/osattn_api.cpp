@@ -13,7 +13,8 @@
 namespace osattn {
 hipError_t launch_forward(int dtype, int d, int mask, FwdParams p, int max_seqlen, hipStream_t st);
 hipError_t launch_backward(int mask, BwdParams p, int seqs, hipStream_t st);
-hipError_t launch_backward16(int dtype, int d, int mask, BwdParams p, int seqs, hipStream_t st);
+hipError_t launch_backward16(int dtype, int d, int mask, BwdParams p, int seqs, int sched_shift,
+                             hipStream_t st);
 hipError_t launch_forward_pruned(int dtype, int d, FwdParams p, hipStream_t st);
 hipError_t launch_csr_softmax(int dtype, int d, const CsrParams &p, hipStream_t st);
 }  // namespace osattn
@@ -113,6 +114,28 @@ struct FwdPlan {
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Varlen work-list plan shared by the forward and the backward: false when no
+// list is used.  n == S * max_seqlen means every sequence has max_seqlen tokens:
+// the natural grid is then balanced already and the list would only add a
+// launch.
+bool plan_varlen_sched(int H, int64_t n_q, int d, int num_seqs, int max_seqlen, int *sched_max,
+                       int *sched_shift) {
+    if (num_seqs <= 0 || max_seqlen <= 0 || n_q == (int64_t)num_seqs * max_seqlen) return false;
+    const int64_t S = num_seqs, t_max = (max_seqlen + 127) / 128;
+    int64_t tiles = (n_q + 127 * S) / 128;
+    if (S * t_max < tiles) tiles = S * t_max;
+    int64_t bound = (tiles + S) / 2;
+    if (S * ((t_max + 1) / 2) < bound) bound = S * ((t_max + 1) / 2);
+    if (bound <= 0 || bound * H > 0x7fffffffLL) return false;
+    const int bc = d == 64 ? 256 : 128;  // key block of the 16-bit forward
+    const int64_t max_w = 2 * ((max_seqlen + bc - 1) / bc);
+    int shift = 0;
+    while ((max_w >> shift) >= kSchedBins) ++shift;
+    *sched_max = (int)bound;
+    *sched_shift = shift;
+    return true;
+}
+
 // Varlen (16-bit): a schedule kernel sorts the varlen items (tile pairs
 // (T-1-i, i) of one sequence) by the key blocks they scan, largest first, into
 // the workspace, and the forward takes its items from that list (without a
@@ -158,25 +181,9 @@ FwdPlan plan_forward(int dtype, int H, int64_t n_q, int64_t n_k, int d, int caus
         };
         while (pl.tile_rows > (d == 64 ? 32 : 64) && items(pl.tile_rows) < half) pl.tile_rows /= 2;
     }
-    // n == S * max_seqlen means every sequence has max_seqlen tokens: the natural
-    // grid is then balanced already and the list would only add a launch.
-    if (dtype != OSATTN_F32 && cu && num_seqs > 0 && max_seqlen > 0 &&
-        n_q != (int64_t)num_seqs * max_seqlen) {
-        const int64_t S = num_seqs, t_max = (max_seqlen + 127) / 128;
-        int64_t tiles = (n_q + 127 * S) / 128;
-        if (S * t_max < tiles) tiles = S * t_max;
-        int64_t bound = (tiles + S) / 2;
-        if (S * ((t_max + 1) / 2) < bound) bound = S * ((t_max + 1) / 2);
-        if (bound > 0 && bound * H <= 0x7fffffffLL) {
-            const int bc = d == 64 ? 256 : 128;  // key block of the 16-bit forward
-            const int64_t max_w = 2 * ((max_seqlen + bc - 1) / bc);
-            int shift = 0;
-            while ((max_w >> shift) >= kSchedBins) ++shift;
-            pl.sched_max = (int)bound;
-            pl.sched_shift = shift;
-            pl.total = round256(16 + 16 * (size_t)bound);
-        }
-    }
+    if (dtype != OSATTN_F32 && cu && plan_varlen_sched(H, n_q, d, num_seqs, max_seqlen,
+                                                       &pl.sched_max, &pl.sched_shift))
+        pl.total = round256(16 + 16 * (size_t)pl.sched_max);
     return pl;
 }
 
@@ -188,13 +195,14 @@ int mask_kind(int causal, const int32_t *cu) {
 // ---------------------------------------------------------------- bwd plan
 struct BwdPlan {
     int q_tiles, k_tiles, q_splits, k_splits, seqs;
-    size_t off_delta, off_mlog2, off_linv, off_dq, off_dk, off_dv, total;
+    int sched_max, sched_shift;  // fp16/bf16 varlen work list (0: none)
+    size_t off_delta, off_mlog2, off_linv, off_dq, off_dk, off_dv, off_sched, total;
 };
 
 int clampi(int64_t x, int lo, int hi) { return (int)(x < lo ? lo : (x > hi ? hi : x)); }
 
-BwdPlan plan_backward(int H, int64_t n_q, int64_t n_k, int d, const int32_t *cu, int num_seqs,
-                      int max_seqlen) {
+BwdPlan plan_backward(int dtype, int H, int64_t n_q, int64_t n_k, int d, const int32_t *cu,
+                      int num_seqs, int max_seqlen) {
     BwdPlan pl{};
     const bool varlen = cu != nullptr;
     pl.seqs = varlen ? num_seqs : 1;
@@ -220,6 +228,10 @@ BwdPlan plan_backward(int H, int64_t n_q, int64_t n_k, int d, const int32_t *cu,
     if (pl.k_splits > 1) off += round256((size_t)pl.k_splits * H * n_k * d * sizeof(float));
     pl.off_dv = off;
     if (pl.k_splits > 1) off += round256((size_t)pl.k_splits * H * n_k * d * sizeof(float));
+    pl.off_sched = off;
+    if (dtype != OSATTN_F32 && varlen &&
+        plan_varlen_sched(H, n_q, d, num_seqs, max_seqlen, &pl.sched_max, &pl.sched_shift))
+        off += round256(16 + 16 * (size_t)pl.sched_max);
     pl.total = off;
     return pl;
 }
@@ -397,7 +409,7 @@ size_t osattn_bwd_workspace_bytes(int dtype, int H, int64_t n_q, int64_t n_k, in
                                   const int32_t *cu_seqlens, int num_seqs, int max_seqlen) {
     if (check_common(dtype, H, n_q, n_k, d, 1.f, causal, cu_seqlens, num_seqs, max_seqlen)) return 0;
     if (check_bwd_supported(dtype, d)) return 0;
-    return plan_backward(H, n_q, n_k, d, cu_seqlens, num_seqs, max_seqlen).total;
+    return plan_backward(dtype, H, n_q, n_k, d, cu_seqlens, num_seqs, max_seqlen).total;
 }
 
 int osattn_bwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q, const void *k,
@@ -419,7 +431,7 @@ int osattn_bwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
     if ((st = check_tensor("dk", dk, kv_stride_h, kv_stride_n, es))) return st;
     if ((st = check_tensor("dv", dv, kv_stride_h, kv_stride_n, es))) return st;
     if (!m || !l) return fail(OSATTN_ERR_INVALID_ARG, "m and l must not be NULL");
-    const BwdPlan pl = plan_backward(H, n_q, n_k, d, cu_seqlens, num_seqs, max_seqlen);
+    const BwdPlan pl = plan_backward(dtype, H, n_q, n_k, d, cu_seqlens, num_seqs, max_seqlen);
     if (!workspace) return fail(OSATTN_ERR_WORKSPACE, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace) & 255u)
         return fail(OSATTN_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
@@ -447,10 +459,15 @@ int osattn_bwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
     p.dv_part = reinterpret_cast<float *>(ws + pl.off_dv);
     p.q_tiles = pl.q_tiles; p.k_tiles = pl.k_tiles;
     p.q_splits = pl.q_splits; p.k_splits = pl.k_splits;
+    if (pl.sched_max > 0) {
+        p.sched = reinterpret_cast<int32_t *>(ws + pl.off_sched);
+        p.sched_max = pl.sched_max;
+    }
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     const int mk = mask_kind(causal, cu_seqlens);
     const hipError_t e = dtype == OSATTN_F32 ? launch_backward(mk, p, pl.seqs, hs)
-                                             : launch_backward16(dtype, d, mk, p, pl.seqs, hs);
+                                             : launch_backward16(dtype, d, mk, p, pl.seqs,
+                                                                 pl.sched_shift, hs);
     if (e != hipSuccess) return fail(OSATTN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
     return ok();
 }

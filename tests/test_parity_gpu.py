@@ -245,6 +245,7 @@ BWD16_CASES = [
     (False, 300, 200, 2, None), (True, 300, 300, 2, None), (True, 700, 700, 1, None),
     (False, 1024, 256, 1, None), (False, 200, 1024, 1, None), (False, 1, 1, 1, None),
     (True, 0, 0, 2, [384, 1, 96, 640, 57]), (False, 0, 0, 1, [130, 0, 7, 300]),
+    (True, 0, 0, 2, [256, 256, 256]),  # equal lengths: the natural varlen grid (no work list)
 ]
 
 
