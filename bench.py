@@ -80,6 +80,11 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
+# The backward's kernels (fp16/bf16, f32), as named in profiles/traffic.json.
+BWD_KERNELS = {False: "bwd16_pre+bwd16_dkdv+bwd16_dq+bwd16_reduce",
+               True: "bwd_pre+bwd_dkdv32+bwd_dq32+reduce_parts_f32"}
+
+
 def recorded_traffic(workload: str, kernel: str):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -132,7 +137,7 @@ def cpu_baseline(w, inp, oracle, np, budget_s=10.0):
     passes = 0
     pos = 0
     cu = inp.cu_seqlens
-    while spent < budget_s and passes < 50:
+    while spent < budget_s and passes < 1000:
         rows = np.sort(order[pos:pos + chunk])
         t0 = time.perf_counter()
         oracle.attn_fwd(inp.q32, inp.k32, inp.v32, w.softmax_scale, causal=w.causal,
@@ -148,7 +153,8 @@ def cpu_baseline(w, inp, oracle, np, budget_s=10.0):
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": "f64 two-pass oracle forward on %d random (head, query) rows of the "
-                      "workload (%.1f s on host cores)" % (rows_done, spent)}
+                      "workload (%d full passes over its %d rows; %.1f s wall on %d threads)"
+                      % (rows_done, passes, w.H * w.n_q, spent, oracle.num_threads())}
 
 
 def capture(fn, n, torch, stream):
@@ -280,9 +286,11 @@ def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True, 
         torch.cuda.synchronize()
         bwd_ms = b0.elapsed_time(b1) / (n_per * reps)
         bwd_ach = bwd_flops(w) / (bwd_ms * 1e-3) / 1e12
-        bwd_rec = {"launch_us_avg": bwd_ms * 1e3, "achieved": bwd_ach, "peak": peak,
-                   "unit": "TFLOP/s", "frac": bwd_ach / peak, "flops_per_launch": bwd_flops(w),
-                   "kernels": "bwd_pre+dkdv+dq(+reduce)"}
+        bkern = BWD_KERNELS[w.dtype == "f32"]
+        bwd_rec = {"bound": "mfma", "launch_us_avg": bwd_ms * 1e3, "achieved": bwd_ach,
+                   "peak": peak, "unit": "TFLOP/s", "frac": bwd_ach / peak,
+                   "flops_per_launch": bwd_flops(w), "kernel": bkern,
+                   "traffic": recorded_traffic(name + "+bwd", bkern)}
     out = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
            "warmup": warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
@@ -362,6 +370,10 @@ def run_pruned(name, rho, steps, warmup, torch, np, osa, W, oracle):
                        "pass": "fwd_pruned", "rho": rho, "tile": "128 queries x 128 keys",
                        "flops": "executed: all tile scores + P.V of admitted tiles"},
             "pct_of_peak": 100.0 * value / peak,
+            "roofline": {"bound": "mfma", "achieved": value, "peak": peak, "unit": "TFLOP/s",
+                         "frac": value / peak, "kernel": "fwd16_pruned_kernel",
+                         "traffic": recorded_traffic(name + "+prune", "fwd16_pruned_kernel"),
+                         "launch_us_avg": times["pruned"] * 1e3},
             "pruning": {"rho": rho, "tiles_pruned_frac": pruned_frac, "oracle_heads": hs,
                         "min_decision_margin": margin, "pruned_ms": times["pruned"],
                         "exact_ms": times["exact"], "speedup": times["exact"] / times["pruned"],
@@ -426,7 +438,8 @@ def run_csr(steps, warmup, torch, np, osa, W, oracle):
             "config": {"workload": c["name"], "H": H, "n_dst": c["n_dst"], "n_src": c["n_src"],
                        "nnz": nnz, "D": D, "pass": "csr_softmax"},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": 8000.0, "unit": "GB/s",
-                         "frac": achieved / 8000.0, "traffic": None, "kernel": "csr_softmax_kernel",
+                         "frac": achieved / 8000.0, "kernel": "csr_softmax_kernel",
+                         "traffic": recorded_traffic(c["name"], "csr_softmax_kernel"),
                          "algorithmic_bytes": nbytes, "launch_us_avg": ms * 1e3},
             "parity": {"max_abs_err_o": err, "tol": TOL[c["dtype"]], "ok": bool(err <= TOL[c["dtype"]])}}
 
