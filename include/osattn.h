@@ -90,12 +90,13 @@ typedef enum osattn_status {
 
 /*
  * Bytes of optional forward workspace for this problem, 0 when none is used.
- * Two fp16/bf16 cases use one:
- *  - dense relation with too few 128-row query tiles to occupy the device:
- *    osattn_fwd splits each tile's key range over several workgroups that
- *    write partial (m, l, U) states to the workspace, and a second kernel on
- *    the same stream combines them;
- *  - varlen (cu_seqlens given): a first kernel writes a work list of the
+ * Two cases use one:
+ *  - dense relation with too few 128-row query tiles to occupy the device
+ *    (fp16/bf16: and long key ranges; f32: at least 512 keys): osattn_fwd
+ *    splits each tile's key range over several workgroups that write partial
+ *    (m, l, U) states to the workspace, and a second kernel on the same stream
+ *    combines them;
+ *  - varlen (cu_seqlens given, fp16/bf16): a first kernel writes a work list of the
  *    (sequence, query tile) items, largest first, to the workspace, and the
  *    forward takes its tiles in that order, which balances sequences of
  *    mixed lengths over the device.

@@ -126,6 +126,30 @@ __device__ __forceinline__ void fwd_epilogue(const FwdParams &p, const FwdWork &
     }
 }
 
+// Split-KV partial state of one row for the key range `split`: U and the row sum
+// against the exact running maximum (raw score units), in the layout the
+// combine kernel reads: (splits, H, n_q, D + 4) f32 = U then {m, m, l, 0}.
+template <int NDT>
+__device__ __forceinline__ void fwd_partial(const FwdParams &p, const FwdWork &w, int split,
+                                            int qrow, int g, f32x16 (&U)[NDT], float m_run,
+                                            float l_run) {
+    constexpr int D = 32 * NDT;
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (qrow >= w.q_hi) return;
+    float *prow = p.part + (((int64_t)split * p.H + w.h) * p.n_q + qrow) * (D + 4);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f32x4 val = {U[dt][4 * j], U[dt][4 * j + 1], U[dt][4 * j + 2], U[dt][4 * j + 3]};
+            *reinterpret_cast<f32x4 *>(prow + 32 * dt + 8 * j + 4 * g) = val;
+        }
+    if (g == 0) {
+        const f32x4 stv = {m_run, m_run, l_tot, 0.f};
+        *reinterpret_cast<f32x4 *>(prow + D) = stv;
+    }
+}
+
 // ------------------------------------------------------------ fp16 / bf16
 // v_mfma_f32_32x32x16_{f16,bf16}, f32 accumulation; P is rounded to T (RNE) as
 // the operand of the P.V product while the row sum takes the f32 P.
@@ -787,7 +811,26 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) fwd32_kernel(FwdPar
     __shared__ u32x4 sK[BC * KCH];
     __shared__ u32x4 sV[BC * KCH];
 
-    const FwdWork w = fwd_work<MASK>(p);
+    FwdWork w;
+    int split = -1;
+    if constexpr (MASK == kDense) {
+        if (p.splits > 1) {
+            // Split-KV item: key range `split` of one tile, split index slowest.
+            const int items = p.H * p.n_tiles;
+            split = (int)blockIdx.x / items;
+            const int r = (int)blockIdx.x % items;
+            w.h = r % p.H;
+            w.q_lo = (r / p.H) * kBR;
+            w.q_hi = min(w.q_lo + kBR, p.n_q);
+            w.ok = w.q_lo < p.n_q;
+            w.kv_lo = split * p.split_len;
+            w.kv_hi = min(w.kv_lo + p.split_len, p.n_k);
+        } else {
+            w = fwd_work<MASK>(p);
+        }
+    } else {
+        w = fwd_work<MASK>(p);
+    }
     if (!w.ok) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c32 = lane & 31, g = lane >> 5;
@@ -872,7 +915,8 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) fwd32_kernel(FwdPar
                 }
             }
     }
-    fwd_epilogue<NDT>(p, w, qrow, g, U, m_run, l_run);
+    if (split >= 0) fwd_partial<NDT>(p, w, split, qrow, g, U, m_run, l_run);
+    else fwd_epilogue<NDT>(p, w, qrow, g, U, m_run, l_run);
 }
 
 // ------------------------------------------------------------------ launch
@@ -920,8 +964,9 @@ hipError_t launch_forward(int dtype, int d, int mask, FwdParams p, int max_seqle
     if (d != 64 && p.tile_rows == 32) p.tile_rows = 64;
     p.n_tiles = (rows + p.tile_rows - 1) / p.tile_rows;
     const int64_t seqs = varlen ? p.num_seqs : 1;
-    // f32 kernel: one workgroup per (head, sequence, tile).
-    const int64_t grid32 = (int64_t)p.n_tiles * p.H * seqs;
+    // f32 kernel: one workgroup per (head, sequence, tile), times the key
+    // splits (dense only).
+    const int64_t grid32 = (int64_t)p.n_tiles * p.H * seqs * ((causal || varlen) ? 1 : p.splits);
     // 16-bit kernel: tile pairs for causal / varlen, single tiles otherwise.
     if (!causal || varlen) p.pair = varlen ? 1 : 0;
     const bool paired = p.pair != 0;
@@ -950,7 +995,7 @@ hipError_t launch_forward(int dtype, int d, int mask, FwdParams p, int max_seqle
         case kVarlen: launch_fwd_mask<kVarlen>(dtype, d, p, (int)g16, (int)grid32, st); break;
         default: launch_fwd_mask<kVarlenCausal>(dtype, d, p, (int)g16, (int)grid32, st); break;
     }
-    if (p.splits > 1 && dtype != 0) {  // merge the partial states in a second launch
+    if (p.splits > 1) {  // merge the partial states in a second launch
         const dim3 gr(p.H * ((p.n_q + kCombineRows - 1) / kCombineRows)), bl(256);
         if (d == 64) hipLaunchKernelGGL((fwd_combine_kernel<64>), gr, bl, 0, st, p);
         else hipLaunchKernelGGL((fwd_combine_kernel<128>), gr, bl, 0, st, p);

@@ -100,8 +100,9 @@ int device_cus() {
 // ---------------------------------------------------------------- fwd plan
 // Split-KV applies to the 16-bit dense forward when its query tiles cannot
 // occupy half the device AND each would scan many key blocks alone (long keys,
-// few queries: decode-like shapes).  The key range is cut into 128-key-aligned
-// pieces.  A split costs a second (combine) launch of a few microseconds, which
+// few queries: decode-like shapes), and to the f32 dense forward whenever its
+// tiles cannot fill the device's workgroup slots and the keys span at least
+// four 128-key units.  The key range is cut into 128-key-aligned pieces.  A split costs a second (combine) launch of a few microseconds, which
 // is why short key ranges are not split: measured on MI355X, N=1024 H=4 D=64
 // ran 15 us unsplit vs 9 + 8 us split.
 struct FwdPlan {
@@ -155,6 +156,21 @@ FwdPlan plan_forward(int dtype, int H, int64_t n_q, int64_t n_k, int d, int caus
         const int64_t blocks = (n_k + (d == 64 ? 255 : 127)) / (d == 64 ? 256 : 128);
         if (2 * items <= target && blocks >= 16) {
             const int64_t units = (n_k + 127) / 128;
+            int64_t splits = (target + items - 1) / items;
+            if (splits > units) splits = units;
+            if (splits > 64) splits = 64;
+            const int64_t per = (units + splits - 1) / splits;
+            pl.splits = (int)((units + per - 1) / per);
+            pl.split_len = (int)(per * 128);
+        }
+    } else if (dtype == OSATTN_F32 && !causal && !cu) {
+        // f32: 128-row tiles of 4 waves; split the keys until there is about one
+        // workgroup per CU.  Measured on MI355X (SQ=8192 SK=2048 H=1 D=64): 149 us
+        // unsplit (64 workgroups), 52 us in 4 splits, 55 us in 8 (two per CU).
+        const int64_t items = (int64_t)H * pl.n_tiles;
+        const int64_t target = device_cus();
+        const int64_t units = (n_k + 127) / 128;
+        if (items < target && units >= 4) {
             int64_t splits = (target + items - 1) / items;
             if (splits > units) splits = units;
             if (splits > 64) splits = 64;

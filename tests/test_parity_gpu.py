@@ -307,11 +307,13 @@ def test_workload_bwd_full_size(osattn, oracle, name, heads):
 
 # ------------------------------------------------------------ split-KV forward
 @pytest.mark.parametrize("dtype,D,n_q,n_k,H", [("f16", 64, 128, 16384, 4), ("bf16", 128, 300, 2100, 2),
-                                               ("f16", 128, 129, 4097, 1), ("bf16", 64, 1, 8191, 3)])
+                                               ("f16", 128, 129, 4097, 1), ("bf16", 64, 1, 8191, 3),
+                                               ("f32", 64, 300, 1000, 2), ("f32", 128, 129, 777, 1),
+                                               ("f32", 64, 1, 4097, 1)])
 def test_split_kv_matches_oracle_and_unsplit(osattn, oracle, dtype, D, n_q, n_k, H):
     lib = osattn.load()
     inp = W.make_inputs(small("s", H, n_q, n_k, D, dtype, False, 4000 + n_k))
-    need = lib.osattn_fwd_workspace_bytes({"f16": 1, "bf16": 2}[dtype], H, n_q, n_k, D, 0, None, 0, 0)
+    need = lib.osattn_fwd_workspace_bytes({"f32": 0, "f16": 1, "bf16": 2}[dtype], H, n_q, n_k, D, 0, None, 0, 0)
     assert need > 0, "these shapes are small enough to split"
     q, k, v = (to_dev(x, dtype) for x in (inp.q, inp.k, inp.v))
     ws = torch.full((need,), 0x7f, dtype=torch.uint8, device="cuda")  # contents are ignored
