@@ -9,7 +9,7 @@
 // tail whose scores are -inf.  Relations: TIGA-lang "Attention and dense
 // relations" (dense, causal j <= i, varlen block-diagonal with cu_seqlens).
 //
-// Work decomposition (MI355X).  fp16/bf16: a workgroup of 8 waves owns a tile
+// Work decomposition (MI355X).  fp16/bf16: a workgroup of 8 or 4 waves owns a tile
 // of 32 RG query rows of one head (RG row groups x 8/RG key groups, 128 rows by
 // default).  Each wave computes the transposed score tile S^T = K Q^T on MFMA so
 // that every lane owns ONE query row: the row maximum and row sum are in-lane
@@ -154,7 +154,7 @@ __device__ __forceinline__ void fwd_partial(const FwdParams &p, const FwdWork &w
 // v_mfma_f32_32x32x16_{f16,bf16}, f32 accumulation; P is rounded to T (RNE) as
 // the operand of the P.V product while the row sum takes the f32 P.
 //
-// A workgroup of 8 waves owns one query tile at a time (128 rows by default):
+// A workgroup of 8 (or 4) waves owns one query tile at a time (128 rows by default):
 // with RG row groups, wave w serves rows 32 (w % RG) .. +32 and key group w / RG
 // of every key block, so two waves per SIMD overlap one's exponentials with the
 // other's MFMAs.  The key groups keep separate running states (m, l, U) that
@@ -178,22 +178,26 @@ __device__ __forceinline__ void fwd_partial(const FwdParams &p, const FwdWork &w
 constexpr int kT16 = 512;
 constexpr float kLazyLog2 = 8.f;
 
-// NST pipeline stages share 128 KiB of LDS: 2 stages of BC keys, or 4 stages
-// of half as many keys each (deeper prefetch).  Measured on MI355X, 4 stages
-// gained nothing at the shapes here (0.98x-1.03x), so launches use 2.
-template <int D, int NST>
+// A workgroup has NW = 8 waves and 128 KiB of LDS (one per CU), or NW = 4
+// waves and 64 KiB (two per CU, so the two waves of a SIMD come from different
+// workgroups and are not held in step by one barrier).  NST pipeline stages
+// share the LDS: 2 stages of BC keys, or 4 stages of half as many keys each
+// (deeper prefetch).  Measured on MI355X, 4 stages gained nothing at the shapes
+// here (0.98x-1.03x), so launches use 2.
+template <int D, int NST, int NW = 8>
 struct Fwd16Cfg {
-    static constexpr int BC = ((D == 64) ? 256 : 128) * 2 / NST;  // keys per block
+    static constexpr int LDS = NW == 8 ? 131072 : 65536;  // bytes of all stages
+    static constexpr int BC = ((D == 64) ? 256 : 128) * 2 / NST * NW / 8;  // keys per block
     static constexpr int KH = BC / 2;                 // keys per wave group
     static constexpr int ROW = D * 2;                 // bytes per K / V row in LDS
     static constexpr int CPR = ROW / 16;              // 16-byte chunks per row
     static constexpr int TILE = BC * ROW;             // bytes of one K (or V) block
     static constexpr int STAGE = 2 * TILE;            // K then V
-    static constexpr int NDMA = TILE / (kT16 * 16);   // DMA instructions per tile per thread
+    static constexpr int NDMA = TILE / (64 * NW * 16);  // DMA instructions per tile per thread
     static constexpr int NS = KH / 32, NKK = D / 16, NDT = D / 32;  // 32-key chunks per wave
     static constexpr int NDMA_BLOCK = 2 * NDMA;      // DMA instructions per block per thread
-    static_assert(NDMA * kT16 * 16 == TILE, "block must split evenly over the DMA lanes");
-    static_assert(NST * STAGE == 131072, "stages fill 128 KiB");
+    static_assert(NDMA * 64 * NW * 16 == TILE, "block must split evenly over the DMA lanes");
+    static_assert(NST * STAGE == LDS, "stages fill the workgroup's LDS");
 };
 
 // Wait until at most `blocks` blocks of this thread's DMA are still in flight.
@@ -204,23 +208,24 @@ __device__ __forceinline__ void wait_dma_blocks(int blocks) {
     else wait_vmcnt<0>();
 }
 
-// The 8 waves of a workgroup form RG row groups of 32 query rows (a tile of
-// 32 RG rows) times KG = 8 / RG key groups; key group kg takes keys
+// The NW waves of a workgroup form RG row groups of 32 query rows (a tile of
+// 32 RG rows) times KG = NW / RG key groups; key group kg takes keys
 // [kg KH, (kg + 1) KH) of every block, and the KG partial states of a row are
 // merged through LDS at the end.  Launches use RG = 4 (128-row tiles) unless
 // such tiles are too few to occupy the device.
 // split < 0: write O, m, l.  split >= 0: write this key range's partial state.
 // PRUNE: tile-pruned dense forward (each block is one 128 x BC tile); smem then
 // carries 8 extra floats past the stages for the tile-maximum exchange.
-template <typename T, int D, int MASK, int NST, int RG, bool PRUNE = false>
+template <typename T, int D, int MASK, int NST, int RG, bool PRUNE = false, int NW = 8>
 __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h, int q_lo,
                                            int q_hi, int kv_lo, int kv_hi, int split) {
-    typedef Fwd16Cfg<D, NST> C;
+    typedef Fwd16Cfg<D, NST, NW> C;
     typedef typename Half8<T>::vec vec8;
     constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
-    constexpr int KG = 8 / RG, KH = C::BC / KG, NS = KH / 32;  // keys, 32-key chunks per wave
-    static_assert(RG * KG == 8 && NS * 32 == KH && NS >= 1, "wave layout must tile the block");
-    static_assert(8192 + (8 - RG) * (D / 8) * 64 * 16 <= NST * C::STAGE, "merge buffers fit in LDS");
+    constexpr int KG = NW / RG, KH = C::BC / KG, NS = KH / 32;  // keys, 32-key chunks per wave
+    static_assert(RG * KG == NW && NS * 32 == KH && NS >= 1, "wave layout must tile the block");
+    static_assert(8192 + (NW - RG) * (D / 8) * 64 * 16 <= NST * C::STAGE, "merge buffers fit in LDS");
+    static_assert(!PRUNE || NW == 8, "the pruned tile exchange assumes 8 waves");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rg = wave % RG, kg = wave / RG;
     const int c32 = lane & 31, g = lane >> 5;
@@ -240,13 +245,13 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
     const int kv_sn = (int)p.kv_sn;
 
     // F1: DMA block [k0, k0 + BC) of K and V into stage `buf`.  DMA
-    // instruction i of this wave fills LDS bytes [(8 i + wave) 1 KiB, +1 KiB)
+    // instruction i of this wave fills LDS bytes [(NW i + wave) 1 KiB, +1 KiB)
     // of each tile; each lane fetches the global chunk its swizzled LDS slot
     // holds.  Rows at or past kv_hi arrive as zeros.
     int dma_off[C::NDMA];
 #pragma unroll
     for (int i = 0; i < C::NDMA; ++i) {
-        const int byte = (8 * i + wave) * 1024 + 16 * lane;
+        const int byte = (NW * i + wave) * 1024 + 16 * lane;
         const int row = byte / C::ROW, pch = (byte % C::ROW) / 16;
         (void)pch;
         dma_off[i] = row * kv_sn * esz;  // + logical chunk, per tile below
@@ -259,10 +264,10 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
         char *sv = sk + C::TILE;
 #pragma unroll
         for (int i = 0; i < C::NDMA; ++i) {
-            const int byte = (8 * i + wave) * 1024 + 16 * lane;
+            const int byte = (NW * i + wave) * 1024 + 16 * lane;
             const int row = byte / C::ROW, pch = (byte % C::ROW) / 16;
-            dma16(rk, sk + (8 * i + wave) * 1024, dma_off[i] + swz_k<C::ROW>(row, pch) * 16);
-            dma16(rv, sv + (8 * i + wave) * 1024, dma_off[i] + swz_vt<C::ROW>(row, pch) * 16);
+            dma16(rk, sk + (NW * i + wave) * 1024, dma_off[i] + swz_k<C::ROW>(row, pch) * 16);
+            dma16(rv, sv + (NW * i + wave) * 1024, dma_off[i] + swz_vt<C::ROW>(row, pch) * 16);
         }
     };
 
@@ -335,7 +340,7 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
             bare_barrier();
             float m_tile = slot[0];
 #pragma unroll
-            for (int w = 1; w < 8; ++w) m_tile = vmax(m_tile, slot[w]);
+            for (int w = 1; w < NW; ++w) m_tile = vmax(m_tile, slot[w]);
             if (m_tile >= m_blk + p.prune_thr) {
                 m_blk = vmax(m_blk, m_tile);
                 if (act) {
@@ -463,8 +468,8 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
     // leave (m_ref, m_true, l) and U in LDS; group 0 rescales all KG states to
     // the largest reference M and sums them in a fixed order.
     l_run = xor32_sum(l_run);
-    float *st = reinterpret_cast<float *>(smem);           // (8 waves, 3, 64) floats
-    f32x4 *su = reinterpret_cast<f32x4 *>(smem + 8192);    // (8 waves, D/8, 64) float4
+    float *st = reinterpret_cast<float *>(smem);           // (NW waves, 3, 64) floats
+    f32x4 *su = reinterpret_cast<f32x4 *>(smem + 8192);    // (NW - RG waves, D/8, 64) float4
     if (kg != 0) {
         st[(wave * 3 + 0) * 64 + lane] = m_ref;
         st[(wave * 3 + 1) * 64 + lane] = m_true;
@@ -676,13 +681,14 @@ __global__ void __launch_bounds__(kSchedThreads) varlen_schedule_kernel(FwdParam
     for (int i = count + tid; i < p.sched_max; i += kSchedThreads) items[i] = make_int4(0, 0, -1, -1);
 }
 
-template <typename T, int D, int MASK, int NST, int RG>
-__global__ void __launch_bounds__(kT16) fwd16_kernel(FwdParams p) {
+// NW = 4: two workgroups per CU, so each wave may use at most 256 registers.
+template <typename T, int D, int MASK, int NST, int RG, int NW = 8>
+__global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdParams p) {
     constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
     constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
     constexpr int TR = 32 * RG;  // query rows per tile
     static_assert(!varlen || TR == kBR, "varlen tiles are kBR rows");
-    __shared__ __attribute__((aligned(16))) char smem[NST * Fwd16Cfg<D, NST>::STAGE];
+    __shared__ __attribute__((aligned(16))) char smem[NST * Fwd16Cfg<D, NST, NW>::STAGE];
     const int b = blockIdx.x;
     if (!causal && !varlen && p.splits > 1) {
         // Split-KV item; the split index varies slowest so that all splits of
@@ -692,7 +698,7 @@ __global__ void __launch_bounds__(kT16) fwd16_kernel(FwdParams p) {
         const int h = r % p.H, tile = r / p.H;
         const int q_lo = tile * TR, q_hi = min(q_lo + TR, p.n_q);
         const int k_lo = split * p.split_len, k_hi = min(k_lo + p.split_len, p.n_k);
-        fwd16_tile<T, D, MASK, NST, RG>(p, smem, h, q_lo, q_hi, k_lo, k_hi, split);
+        fwd16_tile<T, D, MASK, NST, RG, false, NW>(p, smem, h, q_lo, q_hi, k_lo, k_hi, split);
         return;
     }
     const int h = b % p.H;
@@ -705,7 +711,7 @@ __global__ void __launch_bounds__(kT16) fwd16_kernel(FwdParams p) {
             if (tile < 0) break;
             const int q_lo = it.x + tile * TR, q_hi = min(q_lo + TR, it.y);
             if (q_lo >= q_hi) break;
-            fwd16_tile<T, D, MASK, NST, RG>(p, smem, h, q_lo, q_hi, it.x, causal ? q_hi : it.y, -1);
+            fwd16_tile<T, D, MASK, NST, RG, false, NW>(p, smem, h, q_lo, q_hi, it.x, causal ? q_hi : it.y, -1);
         }
         return;
     }
@@ -741,12 +747,33 @@ __global__ void __launch_bounds__(kT16) fwd16_kernel(FwdParams p) {
         if (tile < 0) break;
         const int q_lo = seq_lo + tile * TR, q_hi = min(q_lo + TR, seq_hi);
         const int kv_hi = causal ? q_hi : (varlen ? seq_hi : p.n_k);
-        fwd16_tile<T, D, MASK, NST, RG>(p, smem, h, q_lo, q_hi, seq_lo, kv_hi, -1);
+        fwd16_tile<T, D, MASK, NST, RG, false, NW>(p, smem, h, q_lo, q_hi, seq_lo, kv_hi, -1);
     }
 }
 
 // The varlen work list on its own (the fp16/bf16 backward orders its tile pairs
 // with it): the same kernel and key block as the forward of width d.
+// Key block of the 16-bit forward for width d and NW waves per workgroup.
+int fwd16_block_keys(int d, int waves) {
+    if (d == 64) return waves == 4 ? Fwd16Cfg<64, 2, 4>::BC : Fwd16Cfg<64, 2>::BC;
+    return waves == 4 ? Fwd16Cfg<128, 2, 4>::BC : Fwd16Cfg<128, 2>::BC;
+}
+
+// The schedule kernel for a key block of bc keys (64, 128 or 256).
+static void launch_schedule(int bc, bool causal, const FwdParams &p, hipStream_t st) {
+    const dim3 g1(1), b1(kSchedThreads);
+    if (bc == 64) {
+        if (causal) hipLaunchKernelGGL((varlen_schedule_kernel<64, true>), g1, b1, 0, st, p);
+        else hipLaunchKernelGGL((varlen_schedule_kernel<64, false>), g1, b1, 0, st, p);
+    } else if (bc == 128) {
+        if (causal) hipLaunchKernelGGL((varlen_schedule_kernel<128, true>), g1, b1, 0, st, p);
+        else hipLaunchKernelGGL((varlen_schedule_kernel<128, false>), g1, b1, 0, st, p);
+    } else {
+        if (causal) hipLaunchKernelGGL((varlen_schedule_kernel<256, true>), g1, b1, 0, st, p);
+        else hipLaunchKernelGGL((varlen_schedule_kernel<256, false>), g1, b1, 0, st, p);
+    }
+}
+
 hipError_t launch_varlen_schedule(int d, int causal, const int32_t *cu, int num_seqs, int n,
                                   int32_t *sched, int sched_max, int sched_shift, hipStream_t st) {
     FwdParams p{};
@@ -756,14 +783,7 @@ hipError_t launch_varlen_schedule(int d, int causal, const int32_t *cu, int num_
     p.sched = sched;
     p.sched_max = sched_max;
     p.sched_shift = sched_shift;
-    const dim3 g1(1), b1(kSchedThreads);
-    if (d == 64) {
-        if (causal) hipLaunchKernelGGL((varlen_schedule_kernel<Fwd16Cfg<64, 2>::BC, true>), g1, b1, 0, st, p);
-        else hipLaunchKernelGGL((varlen_schedule_kernel<Fwd16Cfg<64, 2>::BC, false>), g1, b1, 0, st, p);
-    } else {
-        if (causal) hipLaunchKernelGGL((varlen_schedule_kernel<Fwd16Cfg<128, 2>::BC, true>), g1, b1, 0, st, p);
-        else hipLaunchKernelGGL((varlen_schedule_kernel<Fwd16Cfg<128, 2>::BC, false>), g1, b1, 0, st, p);
-    }
+    launch_schedule(fwd16_block_keys(d, 8), causal != 0, p, st);
     return hipGetLastError();
 }
 
@@ -935,6 +955,10 @@ static void launch_fwd16(const FwdParams &p, int grid, hipStream_t st) {
             }
         }
     }
+    if (p.waves == 4) {
+        hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 4, 4>), g, dim3(256), 0, st, p);
+        return;
+    }
     hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 4>), g, b, 0, st, p);
 }
 
@@ -976,14 +1000,8 @@ hipError_t launch_forward(int dtype, int d, int mask, FwdParams p, int max_seqle
     if (grid32 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     int64_t g16 = grid16;
     if (p.sched && varlen && dtype != 0) {  // sorted varlen work list first
-        const dim3 g1(1), b1(kSchedThreads);
-        if (d == 64) {
-            if (causal) hipLaunchKernelGGL((varlen_schedule_kernel<Fwd16Cfg<64, 2>::BC, true>), g1, b1, 0, st, p);
-            else hipLaunchKernelGGL((varlen_schedule_kernel<Fwd16Cfg<64, 2>::BC, false>), g1, b1, 0, st, p);
-        } else {
-            if (causal) hipLaunchKernelGGL((varlen_schedule_kernel<Fwd16Cfg<128, 2>::BC, true>), g1, b1, 0, st, p);
-            else hipLaunchKernelGGL((varlen_schedule_kernel<Fwd16Cfg<128, 2>::BC, false>), g1, b1, 0, st, p);
-        }
+        // the list's work estimate counts the forward's own key blocks
+        launch_schedule(fwd16_block_keys(d, p.waves), causal, p, st);
         g16 = (int64_t)p.sched_max * p.H;
     } else {
         p.sched = nullptr;

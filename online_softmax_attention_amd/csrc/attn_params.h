@@ -27,6 +27,7 @@ struct FwdParams {
     int n_tiles;           // query tiles per (head, sequence)
     int tile_rows;         // query rows per tile of the 16-bit kernel: 128, 64 or 32
     int pair;              // causal 16-bit: tile pairs (T-1-i, i) per workgroup (else one tile)
+    int waves;             // 16-bit 128-row tiles: 8 waves per workgroup, or 4 (two per CU)
     int num_seqs;          // 1 unless varlen
     const int32_t *cu;     // device cumulative lengths (varlen) or null
     float scale;           // softmax scale

@@ -16,6 +16,7 @@ hipError_t launch_backward(int mask, BwdParams p, int seqs, hipStream_t st);
 hipError_t launch_backward16(int dtype, int d, int mask, BwdParams p, int seqs, int sched_shift,
                              hipStream_t st);
 hipError_t launch_forward_pruned(int dtype, int d, FwdParams p, hipStream_t st);
+int fwd16_block_keys(int d, int waves);
 hipError_t launch_csr_softmax(int dtype, int d, const CsrParams &p, hipStream_t st);
 }  // namespace osattn
 
@@ -109,6 +110,7 @@ struct FwdPlan {
     int n_tiles, splits, split_len;
     int tile_rows;               // query rows per 16-bit tile
     int pair;                    // causal: two tiles (T-1-i, i) per workgroup
+    int waves;                   // waves per 128-row-tile workgroup (8, or 4: two per CU)
     int sched_max, sched_shift;  // varlen work list (0: none)
     size_t total;                // workspace bytes (0: none used)
 };
@@ -119,7 +121,7 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 // list is used.  n == S * max_seqlen means every sequence has max_seqlen tokens:
 // the natural grid is then balanced already and the list would only add a
 // launch.
-bool plan_varlen_sched(int H, int64_t n_q, int d, int num_seqs, int max_seqlen, int *sched_max,
+bool plan_varlen_sched(int H, int64_t n_q, int bc, int num_seqs, int max_seqlen, int *sched_max,
                        int *sched_shift) {
     if (num_seqs <= 0 || max_seqlen <= 0 || n_q == (int64_t)num_seqs * max_seqlen) return false;
     const int64_t S = num_seqs, t_max = (max_seqlen + 127) / 128;
@@ -128,7 +130,6 @@ bool plan_varlen_sched(int H, int64_t n_q, int d, int num_seqs, int max_seqlen, 
     int64_t bound = (tiles + S) / 2;
     if (S * ((t_max + 1) / 2) < bound) bound = S * ((t_max + 1) / 2);
     if (bound <= 0 || bound * H > 0x7fffffffLL) return false;
-    const int bc = d == 64 ? 256 : 128;  // key block of the 16-bit forward
     const int64_t max_w = 2 * ((max_seqlen + bc - 1) / bc);
     int shift = 0;
     while ((max_w >> shift) >= kSchedBins) ++shift;
@@ -197,8 +198,18 @@ FwdPlan plan_forward(int dtype, int H, int64_t n_q, int64_t n_k, int d, int caus
         };
         while (pl.tile_rows > (d == 64 ? 32 : 64) && items(pl.tile_rows) < half) pl.tile_rows /= 2;
     }
-    if (dtype != OSATTN_F32 && cu && plan_varlen_sched(H, n_q, d, num_seqs, max_seqlen,
-                                                       &pl.sched_max, &pl.sched_shift))
+    // Four-wave workgroups (64 KiB of LDS, two per CU, blocks of half as many
+    // keys) for varlen and for dense grids of 128-row tiles that fill two
+    // workgroups per CU.  Measured on MI355X: varlen causal 16k tokens H=8 D=64
+    // 62 -> 49 us, dense N=4096 H=16 D=128 144 -> 137 us; causal grids (tile
+    // pairs, one per CU) and smaller grids ran slower with four waves.
+    pl.waves = 8;
+    if (dtype != OSATTN_F32 && pl.splits == 1 && pl.tile_rows == 128 &&
+        (cu || (!causal && (int64_t)H * pl.n_tiles >= 2 * device_cus())))
+        pl.waves = 4;
+    if (dtype != OSATTN_F32 && cu && plan_varlen_sched(H, n_q, fwd16_block_keys(d, pl.waves),
+                                                       num_seqs, max_seqlen, &pl.sched_max,
+                                                       &pl.sched_shift))
         pl.total = round256(16 + 16 * (size_t)pl.sched_max);
     return pl;
 }
@@ -246,7 +257,8 @@ BwdPlan plan_backward(int dtype, int H, int64_t n_q, int64_t n_k, int d, const i
     if (pl.k_splits > 1) off += round256((size_t)pl.k_splits * H * n_k * d * sizeof(float));
     pl.off_sched = off;
     if (dtype != OSATTN_F32 && varlen &&
-        plan_varlen_sched(H, n_q, d, num_seqs, max_seqlen, &pl.sched_max, &pl.sched_shift))
+        plan_varlen_sched(H, n_q, fwd16_block_keys(d, 8), num_seqs, max_seqlen, &pl.sched_max,
+                          &pl.sched_shift))
         off += round256(16 + 16 * (size_t)pl.sched_max);
     pl.total = off;
     return pl;
@@ -340,6 +352,7 @@ int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
     }
     if (p.splits == 1) p.tile_rows = pl.tile_rows;
     p.pair = pl.pair;
+    p.waves = pl.waves;
     const hipError_t e = launch_forward(dtype, d, mask_kind(causal, cu_seqlens), p, max_seqlen,
                                         static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(OSATTN_ERR_HIP, "forward launch: %s", hipGetErrorString(e));

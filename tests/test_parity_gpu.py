@@ -87,6 +87,20 @@ def test_workload_causal_n4096_bf16_sampled(osattn):
     check_sampled(o, m, l, inp, True, rows, "bf16", "causal N=4096 H=16 D=128 bf16")
 
 
+# Dense grids of at least two 128-row tiles per CU run four-wave workgroups
+# (two per CU, blocks of half as many keys); ragged query and key tails.
+@pytest.mark.parametrize("dtype,D,n_q,n_k,H", [("f16", 64, 4096 - 37, 4000, 16),
+                                               ("bf16", 128, 8192 - 5, 3001, 8)])
+def test_dense_four_wave_grid_sampled(osattn, dtype, D, n_q, n_k, H):
+    lib = osattn.load()
+    inp = W.make_inputs(small("w4", H, n_q, n_k, D, dtype, False, 6000 + D))
+    o, m, l = run_fwd(osattn, inp, causal=False)
+    rows = sample_rows(H, n_q, extra=(n_q - 128, n_q - 2), count=10)
+    check_sampled(o, m, l, inp, False, rows, dtype, "dense four-wave %s D=%d" % (dtype, D))
+    # the grid is large enough not to split the keys (no workspace)
+    assert lib.osattn_fwd_workspace_bytes({"f16": 1, "bf16": 2}[dtype], H, n_q, n_k, D, 0, None, 0, 0) == 0
+
+
 def test_workload_varlen_16k_f16_sampled(osattn):
     w = W.WORKLOADS["varlen_causal_16k_h8_d64_f16"]
     inp = W.make_inputs(w)
