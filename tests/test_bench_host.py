@@ -1,0 +1,73 @@
+"""Host-side logic of bench.py, no GPU: the FLOP counts against their
+definitions, the refusal of more than one GPU, the admitted-key count behind
+the CPU baseline's FLOP figure, and the rules that tie recorded HBM counters to
+the kernel sources they were taken on."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_forward_flops_follow_the_metric_definition():
+    # 4 N_q N_k D H, halved for causal; varlen sums 2 L^2 D H per causal sequence
+    w = W.WORKLOADS["dense_n1024_h4_d64_f16"]
+    assert bench.fwd_flops(w) == 4 * 1024 * 1024 * 64 * 4
+    w = W.WORKLOADS["causal_n4096_h16_d128_bf16"]
+    assert bench.fwd_flops(w) == 2 * 4096 * 4096 * 128 * 16
+    w = W.WORKLOADS["rect_sq8192_sk2048_h1_d64_f32_fwdbwd"]
+    assert bench.fwd_flops(w) == 4 * 8192 * 2048 * 64
+    assert bench.bwd_flops(w) == 10 * 8192 * 2048 * 64  # five contractions
+    w = W.WORKLOADS["varlen_causal_16k_h8_d64_f16"]
+    assert sum(w.lengths) == 16384
+    assert bench.fwd_flops(w) == sum(2 * L * L * 64 * 8 for L in w.lengths)
+
+
+def test_admitted_count_matches_a_brute_force_mask():
+    lengths = [5, 0, 3, 1, 7]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    n = int(cu[-1])
+    seq = np.repeat(np.arange(len(lengths)), lengths)
+    for causal in (False, True):
+        w = W.Workload("t", 1, n, n, 64, "f16", causal, 0, lengths=lengths)
+        for i in range(n):
+            admit = (seq == seq[i]) & ((np.arange(n) <= i) if causal else True)
+            assert bench.admitted_count(w, i, cu) == int(admit.sum())
+    w = W.Workload("t", 1, 9, 9, 64, "f16", True, 0)
+    assert [bench.admitted_count(w, i, None) for i in range(9)] == list(range(1, 10))
+
+
+def test_more_than_one_gpu_is_refused_before_any_gpu_work():
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_source_hash_ignores_comments_and_layout_only():
+    a = "int f(int x) { return x + 1; } // note"
+    b = "/* block */ int f(int x)\n{\n    return x + 1;  // other note\n}"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only("int f(int x) { return x + 2; }")
+    # a comment marker inside a string literal is code
+    assert "a//b" in bench._code_only('const char *s = "a//b"; // tail')
+
+
+def test_recorded_traffic_needs_the_same_workload_kernel_and_sources(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.recorded_traffic("w", "k") is None  # no records at all
+    (tmp_path / "profiles").mkdir()
+    rec = {"w": {"kernel": "k", "source_sha": "abc", "traffic_bytes": 123.0}}
+    (tmp_path / "profiles" / "traffic.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "kernel_source_sha", lambda: "abc")
+    assert bench.recorded_traffic("w", "k") == 123.0
+    assert bench.recorded_traffic("w", "k2") is None
+    assert bench.recorded_traffic("w2", "k") is None
+    monkeypatch.setattr(bench, "kernel_source_sha", lambda: "changed")
+    assert bench.recorded_traffic("w", "k") is None
