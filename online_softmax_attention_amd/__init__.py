@@ -134,6 +134,37 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _one_gpu(*named):
+    """The device of the first tensor; every named tensor (None skipped) must be
+    on that same GPU (a host pointer reaching a kernel would fault it)."""
+    dev = named[0][0].device
+    if not named[0][0].is_cuda:
+        raise ValueError("%s must be a GPU tensor (got %s)" % (named[0][1], dev))
+    for t, name in named:
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != dev:
+            raise ValueError("%s must be on the GPU device %s (got %s)" % (name, dev, t.device))
+    return dev
+
+
+def _rows_f32(t: torch.Tensor, H: int, n: int, name: str):
+    """m and l: contiguous float32 (H, n)."""
+    if t.dtype != torch.float32 or tuple(t.shape) != (H, n) or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous float32 tensor of shape (%d, %d)" % (name, H, n))
+
+
+def _like(t: torch.Tensor, ref: torch.Tensor, dtype: torch.dtype, name: str):
+    """An output the ABI addresses with ref's strides: same shape and strides."""
+    if t.dtype != dtype or t.shape != ref.shape or t.stride() != ref.stride():
+        raise ValueError("%s must have dtype %s and the shape and strides of %s" %
+                         (name, dtype, tuple(ref.shape)))
+
+
+def _bytes(ws: torch.Tensor) -> int:
+    return ws.numel() * ws.element_size()
+
+
 # Forward split-KV workspaces, one per (device, stream).
 _fwd_ws = {}
 
@@ -174,18 +205,25 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float
         l = torch.empty((H, n_q), dtype=torch.float32, device=q.device)
     else:
         o, m, l = out
-    _, _, _, o_sh, o_sn = _hn(o, layout)
+    dev = _one_gpu((q, "q"), (k, "k"), (v, "v"), (o, "o"), (m, "m"), (l, "l"), (cu, "cu_seqlens"),
+                   (workspace, "workspace"))
+    Ho, n_o, Do, o_sh, o_sn = _hn(o, layout)
+    if o.dtype != torch.float32 or (Ho, n_o, Do) != (H, n_q, D):
+        raise ValueError("o must be float32 with q's shape")
+    _rows_f32(m, H, n_q, "m")
+    _rows_f32(l, H, n_q, "l")
     cu_ptr = None if cu is None else cu.data_ptr()
-    if workspace is None:
-        need = lib.osattn_fwd_workspace_bytes(_DT[q.dtype], H, n_q, n_k, D, int(bool(causal)),
-                                              cu_ptr, num_seqs, max_seqlen)
-        workspace = _fwd_workspace(q.device, int(need)) if need else None
-    ws_ptr = None if workspace is None else workspace.data_ptr()
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.osattn_fwd(_DT[q.dtype], H, n_q, n_k, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                        q_sh, q_sn, kv_sh, kv_sn, o.data_ptr(), o_sh, o_sn, m.data_ptr(),
-                        l.data_ptr(), scale, int(bool(causal)), cu_ptr, num_seqs, max_seqlen,
-                        ws_ptr, ws_bytes, _stream())
+    with torch.cuda.device(dev):
+        if workspace is None:
+            need = lib.osattn_fwd_workspace_bytes(_DT[q.dtype], H, n_q, n_k, D, int(bool(causal)),
+                                                  cu_ptr, num_seqs, max_seqlen)
+            workspace = _fwd_workspace(dev, int(need)) if need else None
+        ws_ptr = None if workspace is None else workspace.data_ptr()
+        ws_bytes = 0 if workspace is None else _bytes(workspace)
+        st = lib.osattn_fwd(_DT[q.dtype], H, n_q, n_k, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            q_sh, q_sn, kv_sh, kv_sn, o.data_ptr(), o_sh, o_sn, m.data_ptr(),
+                            l.data_ptr(), scale, int(bool(causal)), cu_ptr, num_seqs, max_seqlen,
+                            ws_ptr, ws_bytes, _stream())
     _check(st, "osattn_fwd")
     return o, m, l
 
@@ -210,10 +248,16 @@ def fwd_pruned(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: float,
         l = torch.empty((H, n_q), dtype=torch.float32, device=q.device)
     else:
         o, m, l = out
-    _, _, _, o_sh, o_sn = _hn(o, layout)
-    st = lib.osattn_fwd_pruned(_DT[q.dtype], H, n_q, n_k, D, q.data_ptr(), k.data_ptr(),
-                               v.data_ptr(), q_sh, q_sn, kv_sh, kv_sn, o.data_ptr(), o_sh, o_sn,
-                               m.data_ptr(), l.data_ptr(), scale, float(rho), _stream())
+    dev = _one_gpu((q, "q"), (k, "k"), (v, "v"), (o, "o"), (m, "m"), (l, "l"))
+    Ho, n_o, Do, o_sh, o_sn = _hn(o, layout)
+    if o.dtype != torch.float32 or (Ho, n_o, Do) != (H, n_q, D):
+        raise ValueError("o must be float32 with q's shape")
+    _rows_f32(m, H, n_q, "m")
+    _rows_f32(l, H, n_q, "l")
+    with torch.cuda.device(dev):
+        st = lib.osattn_fwd_pruned(_DT[q.dtype], H, n_q, n_k, D, q.data_ptr(), k.data_ptr(),
+                                   v.data_ptr(), q_sh, q_sn, kv_sh, kv_sn, o.data_ptr(), o_sh,
+                                   o_sn, m.data_ptr(), l.data_ptr(), scale, float(rho), _stream())
     _check(st, "osattn_fwd_pruned")
     return o, m, l
 
@@ -242,11 +286,19 @@ def csr_softmax(row_ptr: torch.Tensor, col_idx: torch.Tensor, scores: torch.Tens
         l = torch.empty((H, n_dst), dtype=torch.float32, device=v.device)
     else:
         o, m, l = out
-    st = lib.osattn_csr_softmax(_DT[v.dtype], H, n_dst, n_src, D, row_ptr.data_ptr(),
-                                col_idx.data_ptr() if nnz else None, nnz,
-                                scores.data_ptr() if nnz else None, scores.stride(0), v.data_ptr(),
-                                v_sh, v_sn, o.data_ptr(), o.stride(0), o.stride(1), m.data_ptr(),
-                                l.data_ptr(), _stream())
+    dev = _one_gpu((v, "v"), (row_ptr, "row_ptr"), (col_idx, "col_idx"), (scores, "scores"),
+                   (o, "o"), (m, "m"), (l, "l"))
+    Ho, n_o, Do, _, _ = _hn(o, "hnd")
+    if o.dtype != torch.float32 or (Ho, n_o, Do) != (H, n_dst, D):
+        raise ValueError("o must be float32 of shape (%d, %d, %d)" % (H, n_dst, D))
+    _rows_f32(m, H, n_dst, "m")
+    _rows_f32(l, H, n_dst, "l")
+    with torch.cuda.device(dev):
+        st = lib.osattn_csr_softmax(_DT[v.dtype], H, n_dst, n_src, D, row_ptr.data_ptr(),
+                                    col_idx.data_ptr() if nnz else None, nnz,
+                                    scores.data_ptr() if nnz else None, scores.stride(0),
+                                    v.data_ptr(), v_sh, v_sn, o.data_ptr(), o.stride(0),
+                                    o.stride(1), m.data_ptr(), l.data_ptr(), _stream())
     _check(st, "osattn_csr_softmax")
     return o, m, l
 
@@ -264,28 +316,45 @@ def bwd(q, k, v, o, do, m, l, scale: Optional[float] = None, causal: bool = Fals
         check: bool = True, workspace: Optional[torch.Tensor] = None, out=None):
     """Attention backward on the GPU; returns (dq, dk, dv) in the input dtype."""
     lib = load()
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype of float32/float16/bfloat16")
     H, n_q, D, q_sh, q_sn = _hn(q, layout)
-    _, n_k, _, kv_sh, kv_sn = _hn(k, layout)
-    _, _, _, o_sh, o_sn = _hn(o, layout)
+    Hk, n_k, Dk, kv_sh, kv_sn = _hn(k, layout)
+    Hv, n_v, Dv, v_sh, v_sn = _hn(v, layout)
+    if (Hk, Dk) != (H, D) or (Hv, n_v, Dv) != (H, n_k, D) or (v_sh, v_sn) != (kv_sh, kv_sn):
+        raise ValueError("k and v must have the same shape and strides, matching q's H and D")
+    Ho, n_o, Do, o_sh, o_sn = _hn(o, layout)
+    if o.dtype != torch.float32 or (Ho, n_o, Do) != (H, n_q, D):
+        raise ValueError("o must be the forward's float32 output, with q's shape")
     _, _, _, do_sh, do_sn = _hn(do, layout)
-    if (do_sh, do_sn) != (q_sh, q_sn) or do.dtype != q.dtype:
-        raise ValueError("do must match q's dtype and strides")
+    if do.shape != q.shape or (do_sh, do_sn) != (q_sh, q_sn) or do.dtype != q.dtype:
+        raise ValueError("do must match q's dtype, shape and strides")
+    _rows_f32(m, H, n_q, "m")
+    _rows_f32(l, H, n_q, "l")
     scale = D ** -0.5 if scale is None else float(scale)
     cu, num_seqs, max_seqlen = _cu_args(cu_seqlens, max_seqlen, n_q, check)
     if out is None:
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        # the ABI writes dq with q's strides and dk, dv with k's: allocate with them
+        dq, dk, dv = (torch.empty_strided(t.size(), t.stride(), dtype=q.dtype, device=q.device)
+                      for t in (q, k, k))
     else:
         dq, dk, dv = out
-    need = lib.osattn_bwd_workspace_bytes(_DT[q.dtype], H, n_q, n_k, D, int(bool(causal)),
-                                          None if cu is None else cu.data_ptr(), num_seqs,
-                                          max_seqlen)
-    if workspace is None:
-        workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=q.device)
-    st = lib.osattn_bwd(_DT[q.dtype], H, n_q, n_k, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                        o.data_ptr(), do.data_ptr(), q_sh, q_sn, kv_sh, kv_sn, o_sh, o_sn,
-                        m.data_ptr(), l.data_ptr(), scale, int(bool(causal)),
-                        None if cu is None else cu.data_ptr(), num_seqs, max_seqlen,
-                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-                        workspace.numel(), _stream())
+        _like(dq, q, q.dtype, "dq")
+        _like(dk, k, q.dtype, "dk")
+        _like(dv, k, q.dtype, "dv")
+    dev = _one_gpu((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do"), (m, "m"), (l, "l"),
+                   (cu, "cu_seqlens"), (dq, "dq"), (dk, "dk"), (dv, "dv"), (workspace, "workspace"))
+    with torch.cuda.device(dev):
+        need = lib.osattn_bwd_workspace_bytes(_DT[q.dtype], H, n_q, n_k, D, int(bool(causal)),
+                                              None if cu is None else cu.data_ptr(), num_seqs,
+                                              max_seqlen)
+        if workspace is None:
+            workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
+        st = lib.osattn_bwd(_DT[q.dtype], H, n_q, n_k, D, q.data_ptr(), k.data_ptr(),
+                            v.data_ptr(), o.data_ptr(), do.data_ptr(), q_sh, q_sn, kv_sh, kv_sn,
+                            o_sh, o_sn, m.data_ptr(), l.data_ptr(), scale, int(bool(causal)),
+                            None if cu is None else cu.data_ptr(), num_seqs, max_seqlen,
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                            _bytes(workspace), _stream())
     _check(st, "osattn_bwd")
     return dq, dk, dv

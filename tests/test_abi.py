@@ -222,3 +222,46 @@ def csr(lib, dtype=F16, H=1, n_dst=16, n_src=16, d=64, nnz=32, rp=A + 0x100000, 
 ])
 def test_csr_rejects_on_host(lib, kw, status):
     assert csr(lib, **kw) == status
+
+
+# ------------------------------------------------------------ Python binding
+# The binding validates what the raw pointers cannot carry -- device, dtype,
+# shapes and the strides the ABI reuses -- before any GPU call, so these run on
+# the host (CPU tensors are rejected before the library sees them).
+def _cpu(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.float16)
+
+
+def test_binding_rejects_host_tensors():
+    q = _cpu(2, 64, 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        osa.fwd(q, q, q)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        osa.fwd_pruned(q, q, q, 0.5)
+    import torch
+    o32 = _cpu(2, 64, 64, dtype=torch.float32)
+    ml = _cpu(2, 64, dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        osa.bwd(q, q, q, o32, q, ml, ml)
+    rp = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        osa.csr_softmax(rp, rp, _cpu(1, 3, dtype=torch.float32), _cpu(1, 4, 64))
+
+
+def test_binding_rejects_mismatched_shapes_before_the_device_check():
+    import torch
+    q, k = _cpu(2, 64, 64), _cpu(2, 32, 64)
+    with pytest.raises(ValueError, match="same shape and strides"):
+        osa.fwd(q, k, _cpu(2, 33, 64))
+    with pytest.raises(ValueError, match="same shape and strides"):
+        osa.bwd(q, k, _cpu(2, 64, 64), _cpu(2, 64, 64, dtype=torch.float32), q,
+                _cpu(2, 64, dtype=torch.float32), _cpu(2, 64, dtype=torch.float32))
+    with pytest.raises(ValueError, match="float32 output"):  # o in the input dtype
+        osa.bwd(q, k, k, q, q, _cpu(2, 64, dtype=torch.float32), _cpu(2, 64, dtype=torch.float32))
+    with pytest.raises(ValueError, match="do must match"):
+        osa.bwd(q, k, k, _cpu(2, 64, 64, dtype=torch.float32), _cpu(2, 63, 64),
+                _cpu(2, 64, dtype=torch.float32), _cpu(2, 64, dtype=torch.float32))
+    with pytest.raises(ValueError, match=r"m must be a contiguous float32 tensor of shape \(2, 64\)"):
+        osa.bwd(q, k, k, _cpu(2, 64, 64, dtype=torch.float32), q,
+                _cpu(2, 63, dtype=torch.float32), _cpu(2, 64, dtype=torch.float32))
