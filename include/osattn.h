@@ -96,7 +96,9 @@ typedef enum osattn_status {
  *    splits each tile's key range over several workgroups that write partial
  *    (m, l, U) states to the workspace, and a second kernel on the same stream
  *    combines them;
- *  - varlen (cu_seqlens given, fp16/bf16): a first kernel writes a work list of the
+ *  - varlen (cu_seqlens given, fp16/bf16) with more than 64 sequences (up to
+ *    64, each workgroup ranks its own item and no workspace is used): a
+ *    first kernel writes a work list of the
  *    (sequence, query tile) items, largest first, to the workspace, and the
  *    forward takes its tiles in that order, which balances sequences of
  *    mixed lengths over the device.

@@ -703,6 +703,42 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdPara
     }
     const int h = b % p.H;
     int rest = b / p.H;
+    if (varlen && p.sched_inline) {
+        // Item `rest` in a list of the tile pairs (T-1-i, i) that takes the
+        // sequences by tile count, most first (ties: lower index first), and
+        // each sequence's pairs in order of i; a pair scans about T + 1 key
+        // blocks, so this is the sorted work list without a separate launch.
+        // Lane s < num_seqs (at most 64) holds sequence s; every wave computes
+        // the same answer.
+        const int lane = threadIdx.x & 63, S = p.num_seqs;
+        int lo = 0, hi = 0;
+        if (lane < S) {
+            const Span sp = seq_bounds(p.cu, lane, p.n_q);
+            lo = sp.lo;
+            hi = sp.hi;
+        }
+        const int nt = (hi - lo + TR - 1) / TR, npair = (nt + 1) / 2;
+        const int key = (nt << 6) | (63 - lane);  // distinct per lane; nt < 2^24
+        int before = 0;                          // pairs listed ahead of this sequence's
+        for (int s2 = 0; s2 < S; ++s2) {
+            const int ks = __shfl(key, s2), ns = __shfl(npair, s2);
+            before += ks > key ? ns : 0;
+        }
+        const uint64_t own = __ballot(lane < S && rest >= before && rest < before + npair);
+        if (own == 0) return;  // past the last item
+        const int src = __ffsll((unsigned long long)own) - 1;
+        const int s_lo = __shfl(lo, src), s_hi = __shfl(hi, src), s_nt = __shfl(nt, src);
+        const int i = rest - __shfl(before, src);
+        const int ta = s_nt - 1 - i, tb = (i == ta) ? -1 : i;
+#pragma unroll 1
+        for (int k = 0; k < 2; ++k) {
+            const int tile = k == 0 ? ta : tb;
+            if (tile < 0) break;
+            const int q_lo = s_lo + tile * TR, q_hi = min(q_lo + TR, s_hi);
+            fwd16_tile<T, D, MASK, NST, RG, false, NW>(p, smem, h, q_lo, q_hi, s_lo, causal ? q_hi : s_hi, -1);
+        }
+        return;
+    }
     if (varlen && p.sched) {  // item `rest` of the sorted work list
         const int4 it = reinterpret_cast<const int4 *>(p.sched + 4)[rest];
 #pragma unroll 1
@@ -1003,8 +1039,12 @@ hipError_t launch_forward(int dtype, int d, int mask, FwdParams p, int max_seqle
         // the list's work estimate counts the forward's own key blocks
         launch_schedule(fwd16_block_keys(d, p.waves), causal, p, st);
         g16 = (int64_t)p.sched_max * p.H;
+    } else if (p.sched_inline && varlen && dtype != 0 && p.num_seqs <= 64) {
+        p.sched = nullptr;
+        g16 = (int64_t)p.sched_max * p.H;  // each workgroup ranks its own item
     } else {
         p.sched = nullptr;
+        p.sched_inline = 0;
     }
     if (g16 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     switch (mask) {

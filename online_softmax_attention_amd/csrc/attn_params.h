@@ -46,6 +46,10 @@ struct FwdParams {
     // sched_shift coarsens the sort key to fit the histogram.
     int32_t *sched;
     int sched_max, sched_shift;
+    // Varlen with at most 64 sequences and no list: each workgroup finds its
+    // own item (rank = blockIdx / H) among the tile pairs, sequences ordered by
+    // tile count, most first; the grid has sched_max * H workgroups.
+    int sched_inline;
     float prune_thr;       // tile pruning: ln(rho) / scale (raw score units)
 };
 

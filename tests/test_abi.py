@@ -148,16 +148,19 @@ def test_fwd_workspace_bytes(lib):
 
 
 def test_fwd_workspace_bytes_varlen_work_list(lib):
-    # 16-bit varlen: a 16-byte header plus one 16-byte entry per tile pair, at
-    # most (sum_s T_s + S) / 2 with sum_s T_s <= (n + 127 S) / 128, and at most
-    # S ceil(ceil(max_seqlen / 128) / 2).
+    # 16-bit varlen with more than 64 sequences: a 16-byte header plus one
+    # 16-byte entry per tile pair, at most (sum_s T_s + S) / 2 with
+    # sum_s T_s <= (n + 127 S) / 128, and at most S ceil(ceil(max_seqlen / 128) / 2).
+    # Up to 64 sequences the workgroups rank their items themselves: no list.
     cu = ctypes.c_void_p(0x1000)  # only tested for NULL on the host
     r256 = lambda x: (x + 255) // 256 * 256
     for causal in (0, 1):
-        n = lib.osattn_fwd_workspace_bytes(F16, 8, 16384, 16384, 64, causal, cu, 20, 1894)
-        assert n == r256(16 + 16 * (((16384 + 127 * 20) // 128 + 20) // 2))
-    n = lib.osattn_fwd_workspace_bytes(BF16, 2, 4096, 4096, 128, 1, cu, 64, 100)
-    assert n == r256(16 + 16 * 64)  # 64 one-tile sequences
+        assert lib.osattn_fwd_workspace_bytes(F16, 8, 16384, 16384, 64, causal, cu, 20, 1894) == 0
+        n = lib.osattn_fwd_workspace_bytes(F16, 8, 16384, 16384, 64, causal, cu, 100, 1894)
+        assert n == r256(16 + 16 * (((16384 + 127 * 100) // 128 + 100) // 2))
+    assert lib.osattn_fwd_workspace_bytes(BF16, 2, 4096, 4096, 128, 1, cu, 64, 100) == 0
+    n = lib.osattn_fwd_workspace_bytes(BF16, 2, 4096, 4096, 128, 1, cu, 65, 100)
+    assert n == r256(16 + 16 * 65)  # 65 one-tile sequences
     # equal lengths (n == S * max_seqlen): the natural order is balanced, no list
     assert lib.osattn_fwd_workspace_bytes(F16, 8, 16384, 16384, 64, 1, cu, 16, 1024) == 0
     assert lib.osattn_fwd_workspace_bytes(F32, 8, 16384, 16384, 64, 1, cu, 20, 1894) == 0

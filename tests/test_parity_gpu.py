@@ -345,11 +345,13 @@ def test_split_kv_matches_oracle_and_unsplit(osattn, oracle, dtype, D, n_q, n_k,
 # ------------------------------------------------------------ varlen work list
 @pytest.mark.parametrize("dtype,D,causal", [("f16", 64, True), ("bf16", 128, True),
                                             ("f16", 128, False), ("bf16", 64, False)])
-def test_varlen_work_list_matches_natural_order(osattn, oracle, dtype, D, causal):
-    """The sorted varlen work list only changes which workgroup computes a
-    tile: results equal the natural-order launch (no workspace) bit for bit
-    and the oracle within tolerance.  The workspace starts as garbage and a
-    second call with fewer sequences reuses it."""
+def test_varlen_orders_give_identical_results(osattn, oracle, dtype, D, causal):
+    """Up to 64 sequences each workgroup ranks its own tile pair; more use the
+    sorted list kernel with a workspace, or the natural grid without one.  The
+    order only changes which workgroup computes a tile: appending empty
+    sequences (nothing changes but the count, 12 -> 72) switches the path, and
+    the three results must agree bit for bit and match the oracle.  The list's
+    workspace starts as garbage and a second call with fewer sequences reuses it."""
     lib = osattn.load()
     lengths = [1300, 0, 5, 256, 129, 2048, 1, 700, 0, 383, 1024, 77]
     n = sum(lengths)
@@ -357,27 +359,43 @@ def test_varlen_work_list_matches_natural_order(osattn, oracle, dtype, D, causal
     q, k, v = (to_dev(x, dtype) for x in (inp.q, inp.k, inp.v))
     cu = cu_dev(inp.cu_seqlens)
     code = {"f16": 1, "bf16": 2}[dtype]
-    need = lib.osattn_fwd_workspace_bytes(code, 2, n, n, D, int(causal), cu.data_ptr(),
-                                          len(lengths), max(lengths))
-    assert need > 0
-    ws = torch.full((need,), 0x7f, dtype=torch.uint8, device="cuda")
-    none = torch.empty(0, dtype=torch.uint8, device="cuda")
     sc = inp.w.softmax_scale
+    none = torch.empty(0, dtype=torch.uint8, device="cuda")
     for n_seq in (len(lengths), 5):
         nt = int(inp.cu_seqlens[n_seq])
         qs, ks, vs = q[:, :nt], k[:, :nt], v[:, :nt]
         cus = cu[:n_seq + 1].contiguous()
-        a = osattn.fwd(qs, ks, vs, scale=sc, causal=causal, cu_seqlens=cus, workspace=ws)
-        b = osattn.fwd(qs, ks, vs, scale=sc, causal=causal, cu_seqlens=cus, workspace=none)
+        pad = torch.cat([cus, cus[-1:].repeat(72 - n_seq)])  # 72 sequences, the rest empty
+        assert lib.osattn_fwd_workspace_bytes(code, 2, nt, nt, D, int(causal), cus.data_ptr(),
+                                              n_seq, max(lengths[:n_seq])) == 0
+        need = lib.osattn_fwd_workspace_bytes(code, 2, nt, nt, D, int(causal), pad.data_ptr(), 72,
+                                              max(lengths[:n_seq]))
+        assert need > 0
+        ws = torch.full((need,), 0x7f, dtype=torch.uint8, device="cuda")
+        a = osattn.fwd(qs, ks, vs, scale=sc, causal=causal, cu_seqlens=cus)
+        b = osattn.fwd(qs, ks, vs, scale=sc, causal=causal, cu_seqlens=pad, workspace=ws)
+        c = osattn.fwd(qs, ks, vs, scale=sc, causal=causal, cu_seqlens=pad, workspace=none)
         torch.cuda.synchronize()
-        for x, y in zip(a, b):
-            assert torch.equal(x, y), "work-list order changed a result (%d sequences)" % n_seq
+        for x, y, z in zip(a, b, c):
+            assert torch.equal(x, y) and torch.equal(x, z), "the order changed a result (%d seqs)" % n_seq
         ro, rm, rl = oracle.attn_fwd(np.ascontiguousarray(inp.q32[:, :nt]),
                                      np.ascontiguousarray(inp.k32[:, :nt]),
                                      np.ascontiguousarray(inp.v32[:, :nt]), sc, causal=causal,
                                      cu_seqlens=inp.cu_seqlens[:n_seq + 1])
         assert_fwd_close(host(a[0]), host(a[1]), host(a[2]), ro, rm, rl, dtype,
-                         "work list %s D=%d causal=%s seqs=%d" % (dtype, D, causal, n_seq))
+                         "varlen order %s D=%d causal=%s seqs=%d" % (dtype, D, causal, n_seq))
+
+
+# 64 sequences, the most ranked in-kernel, with every length class at once.
+def test_varlen_64_sequences_ranked_in_kernel(osattn, oracle):
+    rng = np.random.default_rng(4321)
+    lengths = [int(x) for x in rng.choice([0, 1, 37, 127, 128, 129, 300, 777], 64)]
+    n = sum(lengths)
+    inp = W.make_inputs(small("r64", 2, n, n, 64, "f16", True, 4321, lengths=lengths))
+    o, m, l = run_fwd(osattn, inp, True, cu=inp.cu_seqlens)
+    ro, rm, rl = oracle.attn_fwd(inp.q32, inp.k32, inp.v32, inp.w.softmax_scale, causal=True,
+                                 cu_seqlens=inp.cu_seqlens)
+    assert_fwd_close(o, m, l, ro, rm, rl, "f16", "varlen 64 sequences")
 
 
 # ------------------------------------------------------------ tile sizes
