@@ -35,7 +35,11 @@
  *    stride_n = H*D.  k and v share one stride pair; q, d_o and dq share one;
  *    dk and dv use the k/v pair; o has its own pair.
  *  - Element types: dtype OSATTN_F32, OSATTN_F16 or OSATTN_BF16 for q, k, v,
- *    d_o, dq, dk, dv.  o is always f32.  m and l are f32, laid out (H, n_q)
+ *    d_o, dq, dk, dv.  o has o_dtype: OSATTN_F32 for any input (the default
+ *    reading: the f32 accumulator divided by l, unrounded), or the input's
+ *    own 16-bit type (OSATTN_F16 / OSATTN_BF16 with that input: the same f32
+ *    values rounded once, to nearest even); any other o_dtype returns
+ *    OSATTN_ERR_INVALID_ARG.  m and l are f32, laid out (H, n_q)
  *    contiguously; m is in natural-log units of the scaled score.
  *  - Alignment: q, k, v, d_o, dq, dk, dv, o must be 16-byte aligned and their
  *    strides multiples of 16 bytes' worth of elements (8 for f16/bf16, 4 for
@@ -110,8 +114,8 @@ size_t osattn_fwd_workspace_bytes(int dtype, int H, int64_t n_q, int64_t n_k, in
                                   int max_seqlen);
 
 /*
- * Forward pass.  Computes o (f32), m and l as defined above for H heads of
- * n_q queries against n_k keys of feature width d.
+ * Forward pass.  Computes o (of o_dtype), m and l as defined above for H heads
+ * of n_q queries against n_k keys of feature width d.
  *
  * workspace (device, 256-byte aligned, optional): NULL, or smaller than
  * osattn_fwd_workspace_bytes(...), runs the forward without it (unsplit, and
@@ -124,11 +128,11 @@ size_t osattn_fwd_workspace_bytes(int dtype, int H, int64_t n_q, int64_t n_k, in
  * Rows of o, m, l are written for every query position.  No atomics touch the
  * outputs; results are deterministic for a given problem and device.
  */
-int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d,
+int osattn_fwd(int dtype, int o_dtype, int H, int64_t n_q, int64_t n_k, int d,
                const void *q, const void *k, const void *v,
                int64_t q_stride_h, int64_t q_stride_n,
                int64_t kv_stride_h, int64_t kv_stride_n,
-               float *o, int64_t o_stride_h, int64_t o_stride_n,
+               void *o, int64_t o_stride_h, int64_t o_stride_n,
                float *m, float *l,
                float scale, int causal,
                const int32_t *cu_seqlens, int num_seqs, int max_seqlen,
@@ -154,11 +158,11 @@ int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d,
  * exact result call osattn_fwd).  f32 returns OSATTN_ERR_UNSUPPORTED.
  * Arguments, layouts and errors otherwise as osattn_fwd; no workspace.
  */
-int osattn_fwd_pruned(int dtype, int H, int64_t n_q, int64_t n_k, int d,
+int osattn_fwd_pruned(int dtype, int o_dtype, int H, int64_t n_q, int64_t n_k, int d,
                       const void *q, const void *k, const void *v,
                       int64_t q_stride_h, int64_t q_stride_n,
                       int64_t kv_stride_h, int64_t kv_stride_n,
-                      float *o, int64_t o_stride_h, int64_t o_stride_n,
+                      void *o, int64_t o_stride_h, int64_t o_stride_n,
                       float *m, float *l, float scale, float rho,
                       void *stream);
 
@@ -207,7 +211,8 @@ size_t osattn_bwd_workspace_bytes(int dtype, int H, int64_t n_q, int64_t n_k, in
  *   dV_j = sum_i P_ij dO_i
  *   dS_ij = P_ij (<dO_i, v_j> - D_i)
  *   dQ_i = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i
- * o, m, l are the forward's outputs for the same q, k, v, scale and mask.
+ * o, m, l are the forward's outputs for the same q, k, v, scale and mask; o
+ * of o_dtype (f32, or the 16-bit input type: D_i then sums the rounded o).
  * dq uses the q strides, dk and dv the k/v strides; all are written in full,
  * in the input dtype (fp16/bf16 gradients are f32 sums rounded to nearest
  * even once at the end).
@@ -215,9 +220,9 @@ size_t osattn_bwd_workspace_bytes(int dtype, int H, int64_t n_q, int64_t n_k, in
  * osattn_bwd_workspace_bytes(...) bytes; its contents on entry are ignored.
  * No atomics are used: repeated calls give bit-identical gradients.
  */
-int osattn_bwd(int dtype, int H, int64_t n_q, int64_t n_k, int d,
+int osattn_bwd(int dtype, int o_dtype, int H, int64_t n_q, int64_t n_k, int d,
                const void *q, const void *k, const void *v,
-               const float *o, const void *d_o,
+               const void *o, const void *d_o,
                int64_t q_stride_h, int64_t q_stride_n,
                int64_t kv_stride_h, int64_t kv_stride_n,
                int64_t o_stride_h, int64_t o_stride_n,

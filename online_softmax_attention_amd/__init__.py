@@ -52,11 +52,11 @@ def load(path: Optional[str] = None):
         raise RuntimeError("libosattn.so is not built (%s); run online_softmax_attention_amd.build" % p)
     lib = ctypes.CDLL(p)
     i32, i64, f32, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
-    lib.osattn_fwd.argtypes = [i32, i32, i64, i64, i32, vp, vp, vp, i64, i64, i64, i64,
+    lib.osattn_fwd.argtypes = [i32, i32, i32, i64, i64, i32, vp, vp, vp, i64, i64, i64, i64,
                                vp, i64, i64, vp, vp, f32, i32, vp, i32, i32, vp, ctypes.c_size_t, vp]
     lib.osattn_fwd.restype = i32
-    lib.osattn_fwd_pruned.argtypes = [i32, i32, i64, i64, i32, vp, vp, vp, i64, i64, i64, i64,
-                                      vp, i64, i64, vp, vp, f32, f32, vp]
+    lib.osattn_fwd_pruned.argtypes = [i32, i32, i32, i64, i64, i32, vp, vp, vp, i64, i64, i64,
+                                      i64, vp, i64, i64, vp, vp, f32, f32, vp]
     lib.osattn_fwd_pruned.restype = i32
     lib.osattn_csr_softmax.argtypes = [i32, i32, i64, i64, i32, vp, vp, i64, vp, i64, vp, i64, i64,
                                        vp, i64, i64, vp, vp, vp]
@@ -65,7 +65,7 @@ def load(path: Optional[str] = None):
     lib.osattn_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.osattn_bwd_workspace_bytes.argtypes = [i32, i32, i64, i64, i32, i32, vp, i32, i32]
     lib.osattn_bwd_workspace_bytes.restype = ctypes.c_size_t
-    lib.osattn_bwd.argtypes = [i32, i32, i64, i64, i32, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+    lib.osattn_bwd.argtypes = [i32, i32, i32, i64, i64, i32, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                i64, i64, vp, vp, f32, i32, vp, i32, i32, vp, vp, vp, vp,
                                ctypes.c_size_t, vp]
     lib.osattn_bwd.restype = i32
@@ -178,13 +178,22 @@ def _fwd_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     return ws
 
 
+def _o_code(o: torch.Tensor, q: torch.Tensor) -> int:
+    """o_dtype of the ABI: float32 for any input, or the 16-bit input dtype."""
+    if o.dtype == torch.float32 or (o.dtype == q.dtype and q.dtype != torch.float32):
+        return _DT[o.dtype]
+    raise ValueError("o must be float32 or the input dtype %s (got %s)" % (q.dtype, o.dtype))
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
         causal: bool = False, cu_seqlens: Optional[torch.Tensor] = None,
         max_seqlen: Optional[int] = None, layout: str = "hnd", check: bool = True,
         out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
-        workspace: Optional[torch.Tensor] = None):
+        workspace: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32):
     """Attention forward on the GPU; returns (o, m, l).
 
+    ``out_dtype``: o's dtype, float32 (default) or q's 16-bit dtype (the same
+    values rounded once); with ``out`` given, o's own dtype decides.
     ``workspace``: optional device buffer for split-KV partial states (see
     osattn_fwd_workspace_bytes); by default a cached one per (device, stream).
     An empty tensor forces the unsplit forward."""
@@ -200,16 +209,17 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float
     cu, num_seqs, max_seqlen = _cu_args(cu_seqlens, max_seqlen, n_q, check)
     if out is None:
         shape = (H, n_q, D) if layout == "hnd" else (n_q, H, D)
-        o = torch.empty(shape, dtype=torch.float32, device=q.device)
+        o = torch.empty(shape, dtype=out_dtype, device=q.device)
         m = torch.empty((H, n_q), dtype=torch.float32, device=q.device)
         l = torch.empty((H, n_q), dtype=torch.float32, device=q.device)
     else:
         o, m, l = out
+    o_code = _o_code(o, q)
     dev = _one_gpu((q, "q"), (k, "k"), (v, "v"), (o, "o"), (m, "m"), (l, "l"), (cu, "cu_seqlens"),
                    (workspace, "workspace"))
     Ho, n_o, Do, o_sh, o_sn = _hn(o, layout)
-    if o.dtype != torch.float32 or (Ho, n_o, Do) != (H, n_q, D):
-        raise ValueError("o must be float32 with q's shape")
+    if (Ho, n_o, Do) != (H, n_q, D):
+        raise ValueError("o must have q's shape")
     _rows_f32(m, H, n_q, "m")
     _rows_f32(l, H, n_q, "l")
     cu_ptr = None if cu is None else cu.data_ptr()
@@ -220,7 +230,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float
             workspace = _fwd_workspace(dev, int(need)) if need else None
         ws_ptr = None if workspace is None else workspace.data_ptr()
         ws_bytes = 0 if workspace is None else _bytes(workspace)
-        st = lib.osattn_fwd(_DT[q.dtype], H, n_q, n_k, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+        st = lib.osattn_fwd(_DT[q.dtype], o_code, H, n_q, n_k, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                             q_sh, q_sn, kv_sh, kv_sn, o.data_ptr(), o_sh, o_sn, m.data_ptr(),
                             l.data_ptr(), scale, int(bool(causal)), cu_ptr, num_seqs, max_seqlen,
                             ws_ptr, ws_bytes, _stream())
@@ -230,7 +240,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float
 
 def fwd_pruned(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: float,
                scale: Optional[float] = None, layout: str = "hnd",
-               out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+               out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+               out_dtype: torch.dtype = torch.float32):
     """Tile-pruned dense forward (an approximation; see osattn_fwd_pruned); returns (o, m, l)."""
     lib = load()
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -243,19 +254,20 @@ def fwd_pruned(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: float,
     scale = D ** -0.5 if scale is None else float(scale)
     if out is None:
         shape = (H, n_q, D) if layout == "hnd" else (n_q, H, D)
-        o = torch.empty(shape, dtype=torch.float32, device=q.device)
+        o = torch.empty(shape, dtype=out_dtype, device=q.device)
         m = torch.empty((H, n_q), dtype=torch.float32, device=q.device)
         l = torch.empty((H, n_q), dtype=torch.float32, device=q.device)
     else:
         o, m, l = out
+    o_code = _o_code(o, q)
     dev = _one_gpu((q, "q"), (k, "k"), (v, "v"), (o, "o"), (m, "m"), (l, "l"))
     Ho, n_o, Do, o_sh, o_sn = _hn(o, layout)
-    if o.dtype != torch.float32 or (Ho, n_o, Do) != (H, n_q, D):
-        raise ValueError("o must be float32 with q's shape")
+    if (Ho, n_o, Do) != (H, n_q, D):
+        raise ValueError("o must have q's shape")
     _rows_f32(m, H, n_q, "m")
     _rows_f32(l, H, n_q, "l")
     with torch.cuda.device(dev):
-        st = lib.osattn_fwd_pruned(_DT[q.dtype], H, n_q, n_k, D, q.data_ptr(), k.data_ptr(),
+        st = lib.osattn_fwd_pruned(_DT[q.dtype], o_code, H, n_q, n_k, D, q.data_ptr(), k.data_ptr(),
                                    v.data_ptr(), q_sh, q_sn, kv_sh, kv_sn, o.data_ptr(), o_sh,
                                    o_sn, m.data_ptr(), l.data_ptr(), scale, float(rho), _stream())
     _check(st, "osattn_fwd_pruned")
@@ -324,8 +336,9 @@ def bwd(q, k, v, o, do, m, l, scale: Optional[float] = None, causal: bool = Fals
     if (Hk, Dk) != (H, D) or (Hv, n_v, Dv) != (H, n_k, D) or (v_sh, v_sn) != (kv_sh, kv_sn):
         raise ValueError("k and v must have the same shape and strides, matching q's H and D")
     Ho, n_o, Do, o_sh, o_sn = _hn(o, layout)
-    if o.dtype != torch.float32 or (Ho, n_o, Do) != (H, n_q, D):
-        raise ValueError("o must be the forward's float32 output, with q's shape")
+    if (Ho, n_o, Do) != (H, n_q, D):
+        raise ValueError("o must be the forward's output, with q's shape")
+    o_code = _o_code(o, q)
     _, _, _, do_sh, do_sn = _hn(do, layout)
     if do.shape != q.shape or (do_sh, do_sn) != (q_sh, q_sn) or do.dtype != q.dtype:
         raise ValueError("do must match q's dtype, shape and strides")
@@ -350,7 +363,7 @@ def bwd(q, k, v, o, do, m, l, scale: Optional[float] = None, causal: bool = Fals
                                               max_seqlen)
         if workspace is None:
             workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=dev)
-        st = lib.osattn_bwd(_DT[q.dtype], H, n_q, n_k, D, q.data_ptr(), k.data_ptr(),
+        st = lib.osattn_bwd(_DT[q.dtype], o_code, H, n_q, n_k, D, q.data_ptr(), k.data_ptr(),
                             v.data_ptr(), o.data_ptr(), do.data_ptr(), q_sh, q_sn, kv_sh, kv_sn,
                             o_sh, o_sn, m.data_ptr(), l.data_ptr(), scale, int(bool(causal)),
                             None if cu is None else cu.data_ptr(), num_seqs, max_seqlen,

@@ -41,7 +41,7 @@ __global__ void __launch_bounds__(kBThreads) bwd_pre_kernel(BwdParams p) {
     if (row < total) {
         const int h = (int)(row / p.n_q), i = (int)(row % p.n_q);
         const T *dorow = static_cast<const T *>(p.d_o) + (int64_t)h * p.q_sh + (int64_t)i * p.q_sn;
-        const float *orow = p.o + (int64_t)h * p.o_sh + (int64_t)i * p.o_sn;
+        const float *orow = static_cast<const float *>(p.o) + (int64_t)h * p.o_sh + (int64_t)i * p.o_sn;
 #pragma unroll
         for (int e = 0; e < PER; ++e)
             acc += (float)dorow[sub * PER + e] * orow[sub * PER + e];

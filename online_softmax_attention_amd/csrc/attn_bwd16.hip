@@ -77,9 +77,16 @@ __global__ void __launch_bounds__(256) bwd16_pre_kernel(BwdParams p) {
     if (row < total) {
         const int h = (int)(row / p.n_q), i = (int)(row % p.n_q);
         const T *dorow = static_cast<const T *>(p.d_o) + (int64_t)h * p.q_sh + (int64_t)i * p.q_sn;
-        const float *orow = p.o + (int64_t)h * p.o_sh + (int64_t)i * p.o_sn;
+        const int64_t off = (int64_t)h * p.o_sh + (int64_t)i * p.o_sn + sub * PER;
+        if (p.o16) {
+            const T *orow = static_cast<const T *>(p.o) + off;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc += (float)dorow[sub * PER + e] * orow[sub * PER + e];
+            for (int e = 0; e < PER; ++e) acc += (float)dorow[sub * PER + e] * (float)orow[e];
+        } else {
+            const float *orow = static_cast<const float *>(p.o) + off;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc += (float)dorow[sub * PER + e] * orow[e];
+        }
     }
     acc += __shfl_xor(acc, 8);
     acc += __shfl_xor(acc, 4);

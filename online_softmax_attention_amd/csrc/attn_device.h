@@ -177,6 +177,13 @@ __device__ __forceinline__ void bare_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Four f32 values rounded (RNE) to 16-bit type T and stored as 8 bytes.
+template <typename T>
+__device__ __forceinline__ void store4_16(T *dst, f32x4 v) {
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<t4 *>(dst) = __builtin_convertvector(v, t4);
+}
+
 // Raw buffer resource over [base, base + bytes): loads past the end return 0,
 // which is how the kernels guard ragged tails without branches.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {

@@ -111,7 +111,7 @@ __device__ __forceinline__ void fwd_epilogue(const FwdParams &p, const FwdWork &
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (qrow >= w.q_hi) return;
     const float inv = 1.f / l_tot;
-    float *orow = p.o + (int64_t)w.h * p.o_sh + (int64_t)qrow * p.o_sn;
+    float *orow = static_cast<float *>(p.o) + (int64_t)w.h * p.o_sh + (int64_t)qrow * p.o_sn;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -525,14 +525,16 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
             }
         } else if (qrow < q_hi) {
             const float inv = 1.f / l;
-            float *orow = p.o + (int64_t)h * p.o_sh + (int64_t)qrow * p.o_sn;
+            const int64_t off = (int64_t)h * p.o_sh + (int64_t)qrow * p.o_sn;
 #pragma unroll
             for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const f32x4 val = {U[dt][4 * j] * inv, U[dt][4 * j + 1] * inv,
                                        U[dt][4 * j + 2] * inv, U[dt][4 * j + 3] * inv};
-                    *reinterpret_cast<f32x4 *>(orow + 32 * dt + 8 * j + 4 * g) = val;
+                    const int col = 32 * dt + 8 * j + 4 * g;
+                    if (p.o16) store4_16(static_cast<T *>(p.o) + off + col, val);
+                    else *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + off + col) = val;
                 }
             if (g == 0) {
                 p.m[(int64_t)h * p.n_q + qrow] = mt * p.scale;
@@ -550,7 +552,8 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
 // it.  A workgroup of 256 threads covers 32 rows, 8 threads per row.
 constexpr int kCombineRows = 32;
 
-template <int D>
+// OT: the type of O (f32, or the 16-bit input type).
+template <int D, typename OT>
 __global__ void __launch_bounds__(256) fwd_combine_kernel(FwdParams p) {
     constexpr int QD = D / 8;  // features per thread
     const int h = blockIdx.x % p.H, grp = blockIdx.x / p.H;
@@ -582,11 +585,12 @@ __global__ void __launch_bounds__(256) fwd_combine_kernel(FwdParams p) {
         M = Mn;
     }
     const float inv = 1.f / L;
-    float *orow = p.o + (int64_t)h * p.o_sh + (int64_t)row * p.o_sn + part * QD;
+    OT *orow = static_cast<OT *>(p.o) + (int64_t)h * p.o_sh + (int64_t)row * p.o_sn + part * QD;
 #pragma unroll
     for (int i = 0; i < QD / 4; ++i) {
         f32x4 v = {acc[4 * i] * inv, acc[4 * i + 1] * inv, acc[4 * i + 2] * inv, acc[4 * i + 3] * inv};
-        *reinterpret_cast<f32x4 *>(orow + 4 * i) = v;
+        if constexpr (sizeof(OT) == 4) *reinterpret_cast<f32x4 *>(orow + 4 * i) = v;
+        else store4_16(orow + 4 * i, v);
     }
     if (part == 0) {
         p.m[(int64_t)h * p.n_q + row] = MT * p.scale;
@@ -1055,8 +1059,16 @@ hipError_t launch_forward(int dtype, int d, int mask, FwdParams p, int max_seqle
     }
     if (p.splits > 1) {  // merge the partial states in a second launch
         const dim3 gr(p.H * ((p.n_q + kCombineRows - 1) / kCombineRows)), bl(256);
-        if (d == 64) hipLaunchKernelGGL((fwd_combine_kernel<64>), gr, bl, 0, st, p);
-        else hipLaunchKernelGGL((fwd_combine_kernel<128>), gr, bl, 0, st, p);
+        if (!p.o16) {
+            if (d == 64) hipLaunchKernelGGL((fwd_combine_kernel<64, float>), gr, bl, 0, st, p);
+            else hipLaunchKernelGGL((fwd_combine_kernel<128, float>), gr, bl, 0, st, p);
+        } else if (dtype == 1) {
+            if (d == 64) hipLaunchKernelGGL((fwd_combine_kernel<64, _Float16>), gr, bl, 0, st, p);
+            else hipLaunchKernelGGL((fwd_combine_kernel<128, _Float16>), gr, bl, 0, st, p);
+        } else {
+            if (d == 64) hipLaunchKernelGGL((fwd_combine_kernel<64, __bf16>), gr, bl, 0, st, p);
+            else hipLaunchKernelGGL((fwd_combine_kernel<128, __bf16>), gr, bl, 0, st, p);
+        }
     }
     return hipGetLastError();
 }

@@ -18,7 +18,8 @@ constexpr int kSchedBins = 4096;
 
 struct FwdParams {
     const void *q, *k, *v;
-    float *o, *m, *l;
+    void *o;               // f32, or the input dtype when o16 (16-bit inputs only)
+    float *m, *l;
     int64_t q_sh, q_sn;    // element strides of q
     int64_t kv_sh, kv_sn;  // element strides of k and v
     int64_t o_sh, o_sn;    // element strides of o
@@ -50,12 +51,15 @@ struct FwdParams {
     // own item (rank = blockIdx / H) among the tile pairs, sequences ordered by
     // tile count, most first; the grid has sched_max * H workgroups.
     int sched_inline;
+    int o16;               // o holds the input dtype instead of f32
     float prune_thr;       // tile pruning: ln(rho) / scale (raw score units)
 };
 
 struct BwdParams {
     const void *q, *k, *v, *d_o;
-    const float *o, *m, *l;
+    const void *o;         // the forward's output: f32, or the input dtype when o16
+    const float *m, *l;
+    int o16;
     void *dq, *dk, *dv;
     int64_t q_sh, q_sn;
     int64_t kv_sh, kv_sn;

@@ -73,6 +73,20 @@ int check_common(int dtype, int H, int64_t n_q, int64_t n_k, int d, float scale,
     return OSATTN_OK;
 }
 
+// O's element type: f32 for any input, or the 16-bit input type itself.
+int check_o_dtype(int dtype, int o_dtype, size_t *es_o) {
+    if (o_dtype == OSATTN_F32) {
+        *es_o = 4;
+        return 0;
+    }
+    if (dtype != OSATTN_F32 && o_dtype == dtype) {
+        *es_o = 2;
+        return 0;
+    }
+    return fail(OSATTN_ERR_INVALID_ARG, "o_dtype must be OSATTN_F32 or the input dtype (got %d for %d)",
+                o_dtype, dtype);
+}
+
 int check_tensor(const char *name, const void *p, int64_t sh, int64_t sn, size_t esize) {
     if (!p) return fail(OSATTN_ERR_INVALID_ARG, "%s is NULL", name);
     if (sh < 0 || sn < 0) return fail(OSATTN_ERR_INVALID_ARG, "%s has a negative stride", name);
@@ -307,20 +321,23 @@ size_t osattn_fwd_workspace_bytes(int dtype, int H, int64_t n_q, int64_t n_k, in
     return plan_forward(dtype, H, n_q, n_k, d, causal, cu_seqlens, num_seqs, max_seqlen).total;
 }
 
-int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q, const void *k,
-               const void *v, int64_t q_stride_h, int64_t q_stride_n, int64_t kv_stride_h,
-               int64_t kv_stride_n, float *o, int64_t o_stride_h, int64_t o_stride_n, float *m,
-               float *l, float scale, int causal, const int32_t *cu_seqlens, int num_seqs,
-               int max_seqlen, void *workspace, size_t workspace_bytes, void *stream) {
+int osattn_fwd(int dtype, int o_dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
+               const void *k, const void *v, int64_t q_stride_h, int64_t q_stride_n,
+               int64_t kv_stride_h, int64_t kv_stride_n, void *o, int64_t o_stride_h,
+               int64_t o_stride_n, float *m, float *l, float scale, int causal,
+               const int32_t *cu_seqlens, int num_seqs, int max_seqlen, void *workspace,
+               size_t workspace_bytes, void *stream) {
     int st = check_common(dtype, H, n_q, n_k, d, scale, causal, cu_seqlens, num_seqs, max_seqlen);
     if (st) return st;
     if (d != 64 && d != 128)
         return fail(OSATTN_ERR_UNSUPPORTED, "forward supports d = 64 or 128 (got %d)", d);
+    size_t es_o = 4;
+    if ((st = check_o_dtype(dtype, o_dtype, &es_o))) return st;
     const size_t es = elem_size(dtype);
     if ((st = check_tensor("q", q, q_stride_h, q_stride_n, es))) return st;
     if ((st = check_tensor("k", k, kv_stride_h, kv_stride_n, es))) return st;
     if ((st = check_tensor("v", v, kv_stride_h, kv_stride_n, es))) return st;
-    if ((st = check_tensor("o", o, o_stride_h, o_stride_n, 4))) return st;
+    if ((st = check_tensor("o", o, o_stride_h, o_stride_n, es_o))) return st;
     // The kernels address one 256-row block with 32-bit byte offsets.
     if (q_stride_n * (int64_t)es > kMaxRowBytes || kv_stride_n * (int64_t)es > kMaxRowBytes)
         return fail(OSATTN_ERR_UNSUPPORTED, "row strides above %lld bytes are not supported",
@@ -330,6 +347,7 @@ int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
     FwdParams p{};
     p.q = q; p.k = k; p.v = v;
     p.o = o; p.m = m; p.l = l;
+    p.o16 = es_o == 2;
     p.q_sh = q_stride_h; p.q_sn = q_stride_n;
     p.kv_sh = kv_stride_h; p.kv_sn = kv_stride_n;
     p.o_sh = o_stride_h; p.o_sn = o_stride_n;
@@ -370,11 +388,11 @@ int osattn_fwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
     return ok();
 }
 
-int osattn_fwd_pruned(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
-                      const void *k, const void *v, int64_t q_stride_h, int64_t q_stride_n,
-                      int64_t kv_stride_h, int64_t kv_stride_n, float *o, int64_t o_stride_h,
-                      int64_t o_stride_n, float *m, float *l, float scale, float rho,
-                      void *stream) {
+int osattn_fwd_pruned(int dtype, int o_dtype, int H, int64_t n_q, int64_t n_k, int d,
+                      const void *q, const void *k, const void *v, int64_t q_stride_h,
+                      int64_t q_stride_n, int64_t kv_stride_h, int64_t kv_stride_n, void *o,
+                      int64_t o_stride_h, int64_t o_stride_n, float *m, float *l, float scale,
+                      float rho, void *stream) {
     int st = check_common(dtype, H, n_q, n_k, d, scale, 0, nullptr, 0, 0);
     if (st) return st;
     if (dtype == OSATTN_F32)
@@ -383,11 +401,13 @@ int osattn_fwd_pruned(int dtype, int H, int64_t n_q, int64_t n_k, int d, const v
     if (!(rho > 0.f && rho <= 1.f))
         return fail(OSATTN_ERR_INVALID_ARG, "rho must be in (0, 1] (got %g); omit pruning for the "
                     "exact result", (double)rho);
+    size_t es_o = 4;
+    if ((st = check_o_dtype(dtype, o_dtype, &es_o))) return st;
     const size_t es = elem_size(dtype);
     if ((st = check_tensor("q", q, q_stride_h, q_stride_n, es))) return st;
     if ((st = check_tensor("k", k, kv_stride_h, kv_stride_n, es))) return st;
     if ((st = check_tensor("v", v, kv_stride_h, kv_stride_n, es))) return st;
-    if ((st = check_tensor("o", o, o_stride_h, o_stride_n, 4))) return st;
+    if ((st = check_tensor("o", o, o_stride_h, o_stride_n, es_o))) return st;
     if (q_stride_n * (int64_t)es > kMaxRowBytes || kv_stride_n * (int64_t)es > kMaxRowBytes)
         return fail(OSATTN_ERR_UNSUPPORTED, "row strides above %lld bytes are not supported",
                     (long long)kMaxRowBytes);
@@ -395,6 +415,7 @@ int osattn_fwd_pruned(int dtype, int H, int64_t n_q, int64_t n_k, int d, const v
     FwdParams p{};
     p.q = q; p.k = k; p.v = v;
     p.o = o; p.m = m; p.l = l;
+    p.o16 = es_o == 2;
     p.q_sh = q_stride_h; p.q_sn = q_stride_n;
     p.kv_sh = kv_stride_h; p.kv_sn = kv_stride_n;
     p.o_sh = o_stride_h; p.o_sn = o_stride_n;
@@ -452,8 +473,8 @@ size_t osattn_bwd_workspace_bytes(int dtype, int H, int64_t n_q, int64_t n_k, in
     return plan_backward(dtype, H, n_q, n_k, d, cu_seqlens, num_seqs, max_seqlen).total;
 }
 
-int osattn_bwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q, const void *k,
-               const void *v, const float *o, const void *d_o, int64_t q_stride_h,
+int osattn_bwd(int dtype, int o_dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
+               const void *k, const void *v, const void *o, const void *d_o, int64_t q_stride_h,
                int64_t q_stride_n, int64_t kv_stride_h, int64_t kv_stride_n, int64_t o_stride_h,
                int64_t o_stride_n, const float *m, const float *l, float scale, int causal,
                const int32_t *cu_seqlens, int num_seqs, int max_seqlen, void *dq, void *dk, void *dv,
@@ -461,12 +482,14 @@ int osattn_bwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
     int st = check_common(dtype, H, n_q, n_k, d, scale, causal, cu_seqlens, num_seqs, max_seqlen);
     if (st) return st;
     if ((st = check_bwd_supported(dtype, d))) return st;
+    size_t es_o = 4;
+    if ((st = check_o_dtype(dtype, o_dtype, &es_o))) return st;
     const size_t es = elem_size(dtype);
     if ((st = check_tensor("q", q, q_stride_h, q_stride_n, es))) return st;
     if ((st = check_tensor("k", k, kv_stride_h, kv_stride_n, es))) return st;
     if ((st = check_tensor("v", v, kv_stride_h, kv_stride_n, es))) return st;
     if ((st = check_tensor("d_o", d_o, q_stride_h, q_stride_n, es))) return st;
-    if ((st = check_tensor("o", o, o_stride_h, o_stride_n, 4))) return st;
+    if ((st = check_tensor("o", o, o_stride_h, o_stride_n, es_o))) return st;
     if ((st = check_tensor("dq", dq, q_stride_h, q_stride_n, es))) return st;
     if ((st = check_tensor("dk", dk, kv_stride_h, kv_stride_n, es))) return st;
     if ((st = check_tensor("dv", dv, kv_stride_h, kv_stride_n, es))) return st;
@@ -482,6 +505,7 @@ int osattn_bwd(int dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
     BwdParams p{};
     p.q = q; p.k = k; p.v = v; p.d_o = d_o;
     p.o = o; p.m = m; p.l = l;
+    p.o16 = es_o == 2;
     p.dq = dq; p.dk = dk; p.dv = dv;
     p.q_sh = q_stride_h; p.q_sn = q_stride_n;
     p.kv_sh = kv_stride_h; p.kv_sn = kv_stride_n;

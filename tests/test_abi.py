@@ -54,8 +54,8 @@ def test_status_strings(lib):
 # host check and reach a launch with the fake pointers.
 def fwd(lib, dtype=F16, H=2, n_q=128, n_k=128, d=64, q=A, k=B, v=C, qs=(128 * 64, 64),
         kvs=(128 * 64, 64), o=O, os_=(128 * 64, 64), m=None, l=L, scale=0.125, causal=0,
-        cu=None, num_seqs=0, max_seqlen=0, ws=None, ws_bytes=0):
-    return lib.osattn_fwd(dtype, H, n_q, n_k, d, q, k, v, qs[0], qs[1], kvs[0], kvs[1], o,
+        cu=None, num_seqs=0, max_seqlen=0, ws=None, ws_bytes=0, o_dtype=F32):
+    return lib.osattn_fwd(dtype, o_dtype, H, n_q, n_k, d, q, k, v, qs[0], qs[1], kvs[0], kvs[1], o,
                           os_[0], os_[1], m, l, scale, causal, cu, num_seqs, max_seqlen, ws,
                           ws_bytes, None)
 
@@ -86,6 +86,12 @@ def fwd(lib, dtype=F16, H=2, n_q=128, n_k=128, d=64, q=A, k=B, v=C, qs=(128 * 64
     (dict(cu=A, num_seqs=2, max_seqlen=200), osa.ERR_INVALID_ARG),
     (dict(cu=A, num_seqs=2, max_seqlen=64, n_k=100), osa.ERR_INVALID_ARG),
     (dict(n_q=(1 << 30) + 1, n_k=(1 << 30) + 1), osa.ERR_UNSUPPORTED),
+    # o is f32, or the input's own 16-bit type
+    (dict(o_dtype=BF16), osa.ERR_INVALID_ARG),
+    (dict(o_dtype=7), osa.ERR_INVALID_ARG),
+    (dict(dtype=F32, o_dtype=F16, qs=(128 * 64, 64), kvs=(128 * 64, 64)), osa.ERR_INVALID_ARG),
+    # a 16-bit o needs 16-byte alignment in its own element size (8 elements)
+    (dict(o_dtype=F16, os_=(128 * 64, 68)), osa.ERR_ALIGNMENT),
 ])
 def test_fwd_rejects_on_host(lib, kw, status):
     assert fwd(lib, **kw) == status
@@ -101,11 +107,11 @@ def test_fwd_stride_units_follow_dtype(lib):
 
 # The workspace defaults to NULL so no case can pass every host check.
 def bwd(lib, dtype=F32, H=1, n_q=256, n_k=128, d=64, ptrs=None, ws=None, ws_bytes=1 << 30,
-        causal=0, scale=0.125):
+        causal=0, scale=0.125, o_dtype=F32):
     p = dict(q=A, k=B, v=C, o=O, do=A + 0x600000, m=M, l=L, dq=A + 0x700000,
              dk=A + 0x800000, dv=A + 0x900000)
     p.update(ptrs or {})
-    return lib.osattn_bwd(dtype, H, n_q, n_k, d, p["q"], p["k"], p["v"], p["o"], p["do"],
+    return lib.osattn_bwd(dtype, o_dtype, H, n_q, n_k, d, p["q"], p["k"], p["v"], p["o"], p["do"],
                           n_q * d, d, n_k * d, d, n_q * d, d, p["m"], p["l"], scale, causal,
                           None, 0, 0, p["dq"], p["dk"], p["dv"], ws, ws_bytes, None)
 
@@ -183,8 +189,9 @@ def test_fwd_rejects_huge_row_stride(lib):
 
 
 # Tile-pruned forward: every case fails a host check before any launch.
-def fwd_pruned(lib, dtype=F16, H=1, n_q=256, n_k=128, d=64, rho=0.5, m=None, scale=0.125):
-    return lib.osattn_fwd_pruned(dtype, H, n_q, n_k, d, A, B, C, n_q * d, d, n_k * d, d,
+def fwd_pruned(lib, dtype=F16, H=1, n_q=256, n_k=128, d=64, rho=0.5, m=None, scale=0.125,
+               o_dtype=F32):
+    return lib.osattn_fwd_pruned(dtype, o_dtype, H, n_q, n_k, d, A, B, C, n_q * d, d, n_k * d, d,
                                  O, n_q * d, d, m, L, scale, rho, None)
 
 
@@ -260,8 +267,11 @@ def test_binding_rejects_mismatched_shapes_before_the_device_check():
     with pytest.raises(ValueError, match="same shape and strides"):
         osa.bwd(q, k, _cpu(2, 64, 64), _cpu(2, 64, 64, dtype=torch.float32), q,
                 _cpu(2, 64, dtype=torch.float32), _cpu(2, 64, dtype=torch.float32))
-    with pytest.raises(ValueError, match="float32 output"):  # o in the input dtype
-        osa.bwd(q, k, k, q, q, _cpu(2, 64, dtype=torch.float32), _cpu(2, 64, dtype=torch.float32))
+    with pytest.raises(ValueError, match="float32 or the input dtype"):  # o in a third dtype
+        osa.bwd(q, k, k, _cpu(2, 64, 64, dtype=torch.bfloat16), q, _cpu(2, 64, dtype=torch.float32),
+                _cpu(2, 64, dtype=torch.float32))
+    with pytest.raises(ValueError, match="float32 or the input dtype"):
+        osa.fwd(q, q, q, out_dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="do must match"):
         osa.bwd(q, k, k, _cpu(2, 64, 64, dtype=torch.float32), _cpu(2, 63, 64),
                 _cpu(2, 64, dtype=torch.float32), _cpu(2, 64, dtype=torch.float32))

@@ -491,3 +491,67 @@ def test_csr_softmax_causal_relation_matches_attention(osattn, oracle):
     torch.cuda.synchronize()
     ro, rm, rl = oracle.attn_fwd(inp.q32, inp.k32, inp.v32, inp.w.softmax_scale, causal=True)
     assert_fwd_close(host(o), host(m), host(l), ro, rm, rl, "f16", "csr causal relation")
+
+
+# ------------------------------------------------------------ 16-bit O
+# o_dtype = the input dtype: the kernels round the very f32 values they would
+# store otherwise (to nearest even), so o16 equals the f32 output rounded by
+# torch bit for bit, and m, l do not change -- on every epilogue: the 8-wave
+# small grid, causal pairs, the four-wave grid, the split combine, in-kernel
+# varlen ranking and the pruned forward.
+O16_CASES = [
+    ("f16", 64, False, 300, 300, 2, None),
+    ("bf16", 128, True, 700, 700, 2, None),
+    ("f16", 64, False, 4096 - 37, 4000, 16, None),
+    ("bf16", 128, False, 129, 4097, 1, None),
+    ("f16", 64, True, 0, 0, 2, [384, 1, 96, 640, 57, 0, 129, 128]),
+    ("bf16", 64, False, 0, 0, 3, [300, 17, 0, 513]),
+]
+
+
+@pytest.mark.parametrize("dtype,D,causal,n_q,n_k,H,lengths", O16_CASES)
+def test_o16_is_the_f32_output_rounded(osattn, dtype, D, causal, n_q, n_k, H, lengths):
+    if lengths is not None:
+        n_q = n_k = sum(lengths)
+    inp = W.make_inputs(small("o16", H, n_q, n_k, D, dtype, causal, 8800 + n_q + D, lengths=lengths))
+    q, k, v = (to_dev(x, dtype) for x in (inp.q, inp.k, inp.v))
+    cu = cu_dev(inp.cu_seqlens)
+    tdt = q.dtype
+    o32, m32, l32 = osattn.fwd(q, k, v, scale=inp.w.softmax_scale, causal=causal, cu_seqlens=cu)
+    o16, m16, l16 = osattn.fwd(q, k, v, scale=inp.w.softmax_scale, causal=causal, cu_seqlens=cu,
+                               out_dtype=tdt)
+    torch.cuda.synchronize()
+    assert o16.dtype == tdt
+    assert torch.equal(o16, o32.to(tdt)), "16-bit O is not the f32 O rounded"
+    assert torch.equal(m16, m32) and torch.equal(l16, l32)
+
+
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128)])
+def test_o16_pruned_is_the_f32_output_rounded(osattn, dtype, D):
+    inp = W.make_inputs(small("o16p", 2, 300, 700, D, dtype, False, 8900 + D))
+    q, k, v = (to_dev(x, dtype) for x in (inp.q, inp.k, inp.v))
+    o32, m32, l32 = osattn.fwd_pruned(q, k, v, 0.5, scale=inp.w.softmax_scale)
+    o16, m16, l16 = osattn.fwd_pruned(q, k, v, 0.5, scale=inp.w.softmax_scale, out_dtype=q.dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(q.dtype)) and torch.equal(m16, m32) and torch.equal(l16, l32)
+
+
+# The backward from a 16-bit O (D_i then sums the rounded O) still meets the
+# gradient bound against the oracle.
+@pytest.mark.parametrize("dtype,D,causal,lengths", [("f16", 64, True, None), ("bf16", 128, False, None),
+                                                    ("bf16", 64, True, [384, 1, 96, 640, 57])])
+def test_bwd_from_o16(osattn, oracle, dtype, D, causal, lengths):
+    n = sum(lengths) if lengths else 300
+    w = small("bo16", 2, n, n, D, dtype, causal, 9100 + D, lengths=lengths, backward=True)
+    inp = W.make_inputs(w)
+    q, k, v, do = (to_dev(x, dtype) for x in (inp.q, inp.k, inp.v, inp.do))
+    cu = cu_dev(inp.cu_seqlens)
+    o, m, l = osattn.fwd(q, k, v, scale=w.softmax_scale, causal=causal, cu_seqlens=cu,
+                         out_dtype=q.dtype)
+    dq, dk, dv = osattn.bwd(q, k, v, o, do, m, l, scale=w.softmax_scale, causal=causal,
+                            cu_seqlens=cu)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, *_ = oracle.attn_bwd(inp.q32, inp.k32, inp.v32, inp.do32, w.softmax_scale,
+                                        causal=causal, cu_seqlens=inp.cu_seqlens)
+    for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        assert_grad_close(host(g), r, dtype, "%s from 16-bit O %s D=%d" % (name, dtype, D))
