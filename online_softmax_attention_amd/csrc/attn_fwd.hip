@@ -22,6 +22,8 @@
 // round-robin dispatch over the 8 XCDs keeps each head's K/V on one XCD's L2 when
 // H is a multiple of 8; causal tiles are paired (T-1-i, i) for equal work, and
 // varlen tiles can follow a sorted work list (see the schedule kernel).
+#include <type_traits>
+
 #include "attn_device.h"
 
 namespace osattn {
@@ -216,7 +218,9 @@ __device__ __forceinline__ void wait_dma_blocks(int blocks) {
 // split < 0: write O, m, l.  split >= 0: write this key range's partial state.
 // PRUNE: tile-pruned dense forward (each block is one 128 x BC tile); smem then
 // carries 8 extra floats past the stages for the tile-maximum exchange.
-template <typename T, int D, int MASK, int NST, int RG, bool PRUNE = false, int NW = 8>
+// O16: O is written in T (the same f32 values rounded once) instead of f32.
+template <typename T, int D, int MASK, int NST, int RG, bool PRUNE = false, int NW = 8,
+          bool O16 = false>
 __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h, int q_lo,
                                            int q_hi, int kv_lo, int kv_hi, int split) {
     typedef Fwd16Cfg<D, NST, NW> C;
@@ -526,16 +530,27 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
         } else if (qrow < q_hi) {
             const float inv = 1.f / l;
             const int64_t off = (int64_t)h * p.o_sh + (int64_t)qrow * p.o_sn;
+            if constexpr (O16) {  // O in the input dtype: the same values, rounded once
+                T *orow = static_cast<T *>(p.o) + off;
 #pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt)
+                for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const f32x4 val = {U[dt][4 * j] * inv, U[dt][4 * j + 1] * inv,
-                                       U[dt][4 * j + 2] * inv, U[dt][4 * j + 3] * inv};
-                    const int col = 32 * dt + 8 * j + 4 * g;
-                    if (p.o16) store4_16(static_cast<T *>(p.o) + off + col, val);
-                    else *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + off + col) = val;
-                }
+                    for (int j = 0; j < 4; ++j) {
+                        const f32x4 val = {U[dt][4 * j] * inv, U[dt][4 * j + 1] * inv,
+                                           U[dt][4 * j + 2] * inv, U[dt][4 * j + 3] * inv};
+                        store4_16(orow + 32 * dt + 8 * j + 4 * g, val);
+                    }
+            } else {
+                float *orow = static_cast<float *>(p.o) + off;
+#pragma unroll
+                for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const f32x4 val = {U[dt][4 * j] * inv, U[dt][4 * j + 1] * inv,
+                                           U[dt][4 * j + 2] * inv, U[dt][4 * j + 3] * inv};
+                        *reinterpret_cast<f32x4 *>(orow + 32 * dt + 8 * j + 4 * g) = val;
+                    }
+            }
             if (g == 0) {
                 p.m[(int64_t)h * p.n_q + qrow] = mt * p.scale;
                 p.l[(int64_t)h * p.n_q + qrow] = l * fast_exp2((M - mt) * c);
@@ -686,7 +701,7 @@ __global__ void __launch_bounds__(kSchedThreads) varlen_schedule_kernel(FwdParam
 }
 
 // NW = 4: two workgroups per CU, so each wave may use at most 256 registers.
-template <typename T, int D, int MASK, int NST, int RG, int NW = 8>
+template <typename T, int D, int MASK, int NST, int RG, int NW = 8, bool O16 = false>
 __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdParams p) {
     constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
     constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
@@ -702,7 +717,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdPara
         const int h = r % p.H, tile = r / p.H;
         const int q_lo = tile * TR, q_hi = min(q_lo + TR, p.n_q);
         const int k_lo = split * p.split_len, k_hi = min(k_lo + p.split_len, p.n_k);
-        fwd16_tile<T, D, MASK, NST, RG, false, NW>(p, smem, h, q_lo, q_hi, k_lo, k_hi, split);
+        fwd16_tile<T, D, MASK, NST, RG, false, NW, O16>(p, smem, h, q_lo, q_hi, k_lo, k_hi, split);
         return;
     }
     const int h = b % p.H;
@@ -739,7 +754,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdPara
             const int tile = k == 0 ? ta : tb;
             if (tile < 0) break;
             const int q_lo = s_lo + tile * TR, q_hi = min(q_lo + TR, s_hi);
-            fwd16_tile<T, D, MASK, NST, RG, false, NW>(p, smem, h, q_lo, q_hi, s_lo, causal ? q_hi : s_hi, -1);
+            fwd16_tile<T, D, MASK, NST, RG, false, NW, O16>(p, smem, h, q_lo, q_hi, s_lo, causal ? q_hi : s_hi, -1);
         }
         return;
     }
@@ -751,7 +766,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdPara
             if (tile < 0) break;
             const int q_lo = it.x + tile * TR, q_hi = min(q_lo + TR, it.y);
             if (q_lo >= q_hi) break;
-            fwd16_tile<T, D, MASK, NST, RG, false, NW>(p, smem, h, q_lo, q_hi, it.x, causal ? q_hi : it.y, -1);
+            fwd16_tile<T, D, MASK, NST, RG, false, NW, O16>(p, smem, h, q_lo, q_hi, it.x, causal ? q_hi : it.y, -1);
         }
         return;
     }
@@ -787,7 +802,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdPara
         if (tile < 0) break;
         const int q_lo = seq_lo + tile * TR, q_hi = min(q_lo + TR, seq_hi);
         const int kv_hi = causal ? q_hi : (varlen ? seq_hi : p.n_k);
-        fwd16_tile<T, D, MASK, NST, RG, false, NW>(p, smem, h, q_lo, q_hi, seq_lo, kv_hi, -1);
+        fwd16_tile<T, D, MASK, NST, RG, false, NW, O16>(p, smem, h, q_lo, q_hi, seq_lo, kv_hi, -1);
     }
 }
 
@@ -830,14 +845,14 @@ hipError_t launch_varlen_schedule(int d, int causal, const int32_t *cu, int num_
 // Tile-pruned dense forward: one 128-row tile per workgroup, key blocks of 128
 // (D = 64 uses four stages of 128 keys so that both widths prune 128 x 128
 // tiles).
-template <typename T, int D>
+template <typename T, int D, bool O16>
 __global__ void __launch_bounds__(kT16) fwd16_pruned_kernel(FwdParams p) {
     constexpr int NST = D == 64 ? 4 : 2;
     static_assert(Fwd16Cfg<D, NST>::BC == 128, "pruning tiles are 128 keys");
     __shared__ __attribute__((aligned(16))) char smem[NST * Fwd16Cfg<D, NST>::STAGE + 256];
     const int h = blockIdx.x % p.H, tile = blockIdx.x / p.H;
     const int q_lo = tile * kBR, q_hi = min(q_lo + kBR, p.n_q);
-    fwd16_tile<T, D, kDense, NST, 4, true>(p, smem, h, q_lo, q_hi, 0, p.n_k, -1);
+    fwd16_tile<T, D, kDense, NST, 4, true, 8, O16>(p, smem, h, q_lo, q_hi, 0, p.n_k, -1);
 }
 
 hipError_t launch_forward_pruned(int dtype, int d, FwdParams p, hipStream_t st) {
@@ -846,12 +861,20 @@ hipError_t launch_forward_pruned(int dtype, int d, FwdParams p, hipStream_t st) 
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const dim3 g((unsigned)grid), b(kT16);
+    const auto go = [&](auto t, auto dd, auto o16) {
+        hipLaunchKernelGGL((fwd16_pruned_kernel<decltype(t), decltype(dd)::value, decltype(o16)::value>),
+                           g, b, 0, st, p);
+    };
+    using D64 = std::integral_constant<int, 64>;
+    using D128 = std::integral_constant<int, 128>;
+    using F = std::false_type;
+    using O = std::true_type;
     if (dtype == 1) {
-        if (d == 64) hipLaunchKernelGGL((fwd16_pruned_kernel<_Float16, 64>), g, b, 0, st, p);
-        else hipLaunchKernelGGL((fwd16_pruned_kernel<_Float16, 128>), g, b, 0, st, p);
+        if (d == 64) p.o16 ? go(_Float16{}, D64{}, O{}) : go(_Float16{}, D64{}, F{});
+        else p.o16 ? go(_Float16{}, D128{}, O{}) : go(_Float16{}, D128{}, F{});
     } else {
-        if (d == 64) hipLaunchKernelGGL((fwd16_pruned_kernel<__bf16, 64>), g, b, 0, st, p);
-        else hipLaunchKernelGGL((fwd16_pruned_kernel<__bf16, 128>), g, b, 0, st, p);
+        if (d == 64) p.o16 ? go(__bf16{}, D64{}, O{}) : go(__bf16{}, D64{}, F{});
+        else p.o16 ? go(__bf16{}, D128{}, O{}) : go(__bf16{}, D128{}, F{});
     }
     return hipGetLastError();
 }
@@ -980,26 +1003,33 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) fwd32_kernel(FwdPar
 }
 
 // ------------------------------------------------------------------ launch
-template <typename T, int D, int MASK>
-static void launch_fwd16(const FwdParams &p, int grid, hipStream_t st) {
+template <typename T, int D, int MASK, bool O16>
+static void launch_fwd16_o(const FwdParams &p, int grid, hipStream_t st) {
     const dim3 g(grid), b(kT16);
     if constexpr (MASK == kDense || MASK == kCausal) {
         if (p.tile_rows == 64) {
-            hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 2>), g, b, 0, st, p);
+            hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 2, 8, O16>), g, b, 0, st, p);
             return;
         }
         if constexpr (D == 64) {
             if (p.tile_rows == 32) {
-                hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 1>), g, b, 0, st, p);
+                hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 1, 8, O16>), g, b, 0, st, p);
                 return;
             }
         }
     }
-    if (p.waves == 4) {
-        hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 4, 4>), g, dim3(256), 0, st, p);
-        return;
+    if constexpr (MASK == kVarlen || MASK == kVarlenCausal) {  // always four waves
+        hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 4, 4, O16>), g, dim3(256), 0, st, p);
+    } else {
+        if (p.waves == 4) hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 4, 4, O16>), g, dim3(256), 0, st, p);
+        else hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 4, 8, O16>), g, b, 0, st, p);
     }
-    hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 4>), g, b, 0, st, p);
+}
+
+template <typename T, int D, int MASK>
+static void launch_fwd16(const FwdParams &p, int grid, hipStream_t st) {
+    if (p.o16) launch_fwd16_o<T, D, MASK, true>(p, grid, st);
+    else launch_fwd16_o<T, D, MASK, false>(p, grid, st);
 }
 
 template <int MASK>
