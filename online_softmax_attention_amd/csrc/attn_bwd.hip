@@ -400,10 +400,24 @@ __global__ void __launch_bounds__(kBThreads, 1) bwd_dq32_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- reduce
+// Up to three split reductions (dK, dV, dQ) in one launch: workgroup b serves
+// reduction k while b < end[k].  Each thread sums one float4 of its output over
+// the splits in a fixed order (deterministic), four loads in flight.
+struct Reduce3 {
+    ReduceParams r[3];
+    int64_t end[3];  // cumulative workgroup counts
+    int count;
+};
+
 template <int D>
-__global__ void __launch_bounds__(kBThreads) reduce_parts_f32_kernel(ReduceParams r) {
+__global__ void __launch_bounds__(kBThreads) reduce_parts_f32_kernel(Reduce3 q) {
+    int k = 0;
+    int64_t b = blockIdx.x;
+    while (k + 1 < q.count && b >= q.end[k]) ++k;
+    if (k > 0) b -= q.end[k - 1];
+    const ReduceParams &r = q.r[k];
     const int64_t total4 = (int64_t)r.H * r.n * D / 4;
-    const int64_t i4 = (int64_t)blockIdx.x * kBThreads + threadIdx.x;
+    const int64_t i4 = (int64_t)b * kBThreads + threadIdx.x;
     if (i4 >= total4) return;
     const int64_t e = i4 * 4;
     const int64_t plane = (int64_t)r.n * D;
@@ -412,6 +426,7 @@ __global__ void __launch_bounds__(kBThreads) reduce_parts_f32_kernel(ReduceParam
     const int i = (int)(rem / D), d = (int)(rem % D);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const int64_t stride = (int64_t)r.H * plane;
+#pragma unroll 4
     for (int s = 0; s < r.splits; ++s)
         acc += *reinterpret_cast<const f32x4 *>(r.part + s * stride + e);
     *reinterpret_cast<f32x4 *>(static_cast<float *>(r.out) + (int64_t)h * r.out_sh + (int64_t)i * r.out_sn + d) = acc;
@@ -426,14 +441,14 @@ static void launch_bwd_mask(const BwdParams &p, int grid_k, int grid_q, hipStrea
         hipLaunchKernelGGL((bwd_dq32_kernel<64, MASK>), dim3(grid_q), dim3(kBThreads), 0, st, p);
 }
 
-static hipError_t launch_reduce(const float *part, void *out, int64_t sh, int64_t sn, int H, int n,
-                                int splits, hipStream_t st) {
-    ReduceParams r{part, out, sh, sn, H, n, splits};
-    const int64_t total4 = (int64_t)H * n * 64 / 4;
-    const int64_t grid = (total4 + kBThreads - 1) / kBThreads;
-    if (grid > 0)
-        hipLaunchKernelGGL((reduce_parts_f32_kernel<64>), dim3((unsigned)grid), dim3(kBThreads), 0, st, r);
-    return hipGetLastError();
+// Adds one reduction to the combined launch.
+static void add_reduce(Reduce3 &q, const float *part, void *out, int64_t sh, int64_t sn, int H,
+                       int n, int splits) {
+    const int64_t grid = ((int64_t)H * n * 64 / 4 + kBThreads - 1) / kBThreads;
+    if (grid <= 0) return;
+    q.r[q.count] = ReduceParams{part, out, sh, sn, H, n, splits};
+    q.end[q.count] = (q.count ? q.end[q.count - 1] : 0) + grid;
+    ++q.count;
 }
 
 // Host entry used by the C ABI (arguments and workspace already validated;
@@ -455,17 +470,19 @@ hipError_t launch_backward(int mask, BwdParams p, int seqs, hipStream_t st) {
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    Reduce3 q{};
     if (p.k_splits > 1) {
-        e = launch_reduce(p.dk_part, p.dk, p.kv_sh, p.kv_sn, p.H, p.n_k, p.k_splits, st);
-        if (e != hipSuccess) return e;
-        e = launch_reduce(p.dv_part, p.dv, p.kv_sh, p.kv_sn, p.H, p.n_k, p.k_splits, st);
-        if (e != hipSuccess) return e;
+        add_reduce(q, p.dk_part, p.dk, p.kv_sh, p.kv_sn, p.H, p.n_k, p.k_splits);
+        add_reduce(q, p.dv_part, p.dv, p.kv_sh, p.kv_sn, p.H, p.n_k, p.k_splits);
     }
-    if (p.q_splits > 1) {
-        e = launch_reduce(p.dq_part, p.dq, p.q_sh, p.q_sn, p.H, p.n_q, p.q_splits, st);
-        if (e != hipSuccess) return e;
+    if (p.q_splits > 1) add_reduce(q, p.dq_part, p.dq, p.q_sh, p.q_sn, p.H, p.n_q, p.q_splits);
+    if (q.count > 0) {
+        if (q.end[q.count - 1] > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((reduce_parts_f32_kernel<64>), dim3((unsigned)q.end[q.count - 1]),
+                           dim3(kBThreads), 0, st, q);
+        e = hipGetLastError();
     }
-    return hipSuccess;
+    return e;
 }
 
 }  // namespace osattn
