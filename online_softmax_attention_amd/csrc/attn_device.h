@@ -101,14 +101,6 @@ template <int ROW_BYTES>
 __device__ __forceinline__ int swz_k(int row, int chunk) {
     return ROW_BYTES >= 256 ? (chunk ^ (row & 15)) : (chunk ^ ((row >> 1) & 7));
 }
-// Transposed V tile (row = feature d): the readers take 16 consecutive d at one
-// logical chunk, the writers rows d = 8 d8 + x for 16 values of d8.
-// (d ^ (d >> 3)) & 15 is a permutation on both patterns.
-template <int ROW_BYTES>
-__device__ __forceinline__ int swz_v(int d, int chunk) {
-    return ROW_BYTES >= 256 ? (chunk ^ ((d ^ (d >> 3)) & 15)) : (chunk ^ ((d >> 1) & 7));
-}
-
 // Swizzle of a row-major V tile read by ds_read_b64_tr_b16: 16 lanes read four
 // consecutive key rows x 32 bytes, and a wave half reads those rows x 64 bytes.
 // XOR-ing the chunk index with a per-row quarter (256-byte rows) or half
@@ -192,16 +184,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 }
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, int byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
-}
-
-// Key slot order of the transposed V tile.  Register r of an S^T accumulator
-// tile holds key 8 * (r / 4) + 4 * g + (r % 4); the P.V product consumes
-// registers 8h .. 8h+7, i.e. keys {16h + 4g + 0..3, 16h + 8 + 4g + 0..3}.
-// Swapping bits 2 and 3 of the key index places exactly those eight keys in
-// consecutive slots 16h + 8g .. 16h + 8g + 7, so one 16-byte LDS read yields
-// the matching A operand.
-__device__ __forceinline__ int key_slot(int k) {
-    return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
 // Row of the 32x32 MFMA result held in register r by lane half g.
