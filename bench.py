@@ -81,7 +81,7 @@ def kernel_source_sha() -> str:
 
 
 # The backward's kernels (fp16/bf16, f32), as named in profiles/traffic.json.
-BWD_KERNELS = {False: "bwd16_pre+bwd16_dkdv+bwd16_dq+bwd16_reduce",
+BWD_KERNELS = {False: "bwd16_pre+bwd16_kernel+bwd16_reduce",
                True: "bwd_pre+bwd_dkdv32+bwd_dq32+reduce_parts_f32"}
 
 

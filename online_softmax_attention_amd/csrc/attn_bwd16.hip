@@ -12,9 +12,10 @@
 // beta = m log2(e) + log2(l), so that p = 2^(s c - beta) with c = scale log2(e)
 // (one exponential, no division), next to D.
 //
-// Kernels (one stream):
+// Kernels (one stream): bwd16_pre, then bwd16_kernel, whose blocks run the
+// dK/dV items first and the dQ items after them in the same launch:
 //   bwd16_pre  : D_i, beta_i                                             (B0)
-//   bwd16_dkdv : a workgroup owns 128 keys, resident in LDS; its 8 waves are
+//   dK/dV item : a workgroup owns 128 keys, resident in LDS; its 8 waves are
 //                4 key groups of 32 keys x 2 query halves, and scan blocks of
 //                queries whose Q, dO, beta and D arrive by LDS DMA, two stages
 //                deep.  Per 32-query chunk: S = Q K^T, dP = dO V^T (row
@@ -22,7 +23,7 @@
 //                dK^T += Q^T dS with the transposed operands read by
 //                ds_read_b64_tr_b16; every lane owns one key column.  The two
 //                query halves merge through LDS at the end.              (B1)
-//   bwd16_dq   : a workgroup owns 128 queries (4 row groups x 2 key halves,
+//   dQ item    : a workgroup owns 128 queries (4 row groups x 2 key halves,
 //                one query column per lane) and scans key blocks whose K and V
 //                arrive by LDS DMA: S^T = K Q^T, dP^T = V dO^T, P^T, dS^T,
 //                dQ^T += K^T dS^T with K^T read transposed.              (B2)
@@ -347,13 +348,11 @@ __device__ __forceinline__ void dkdv16_tile(const BwdParams &p, char *smem, int 
     __syncthreads();  // the next tile reuses this LDS
 }
 
-// SCHED: varlen items from the sorted work list (one or two tiles each);
-// otherwise one tile of the natural grid.
+// Work item b of the dK/dV pass.  SCHED: varlen items from the sorted work
+// list (one or two tiles each); otherwise one tile of the natural grid.
 template <typename T, int D, int MASK, bool SCHED>
-__global__ void __launch_bounds__(kB16T) bwd16_dkdv_kernel(BwdParams p) {
+__device__ __forceinline__ void dkdv16_item(const BwdParams &p, char *smem, int b) {
     constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
-    __shared__ __attribute__((aligned(16))) char smem[Bwd16Cfg<D>::LDS_DKDV];
-    const int b = blockIdx.x;
     const int h = b % p.H;
     int rest = b / p.H;
     // The item: a key range [lo, hi) with up to two 128-key tiles of it, and
@@ -545,14 +544,11 @@ __device__ __forceinline__ void dq16_tile(const BwdParams &p, char *smem, int h,
     __syncthreads();  // the next tile reuses this LDS
 }
 
-// SCHED: varlen items from the sorted work list (one or two tiles each);
-// otherwise one tile of the natural grid.
+// Work item b of the dQ pass, numbered like the dK/dV items.
 template <typename T, int D, int MASK, bool SCHED>
-__global__ void __launch_bounds__(kB16T) bwd16_dq_kernel(BwdParams p) {
+__device__ __forceinline__ void dq16_item(const BwdParams &p, char *smem, int b) {
     constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
     constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
-    __shared__ __attribute__((aligned(16))) char smem[Bwd16Cfg<D>::LDS_DQ];
-    const int b = blockIdx.x;
     const int h = b % p.H;
     int rest = b / p.H;
     // The item: a query range [lo, hi) with up to two 128-query tiles of it,
@@ -587,6 +583,22 @@ __global__ void __launch_bounds__(kB16T) bwd16_dq_kernel(BwdParams p) {
     }
 }
 
+// One launch for both passes: blocks [0, grid_k) take the dK/dV items, the
+// rest the dQ items.  The two passes write disjoint outputs and read only
+// what the pre-pass wrote, so dQ items start on the CUs that the dK/dV tail
+// leaves idle instead of waiting for the whole dK/dV grid to drain.
+template <typename T, int D, int MASK, bool SCHED>
+__global__ void __launch_bounds__(kB16T) bwd16_kernel(BwdParams p) {
+    typedef Bwd16Cfg<D> C;
+    constexpr int LDS = C::LDS_DKDV > C::LDS_DQ ? C::LDS_DKDV : C::LDS_DQ;
+    __shared__ __attribute__((aligned(16))) char smem[LDS];
+    const int b = blockIdx.x;
+    if (b < p.grid_k)
+        dkdv16_item<T, D, MASK, SCHED>(p, smem, b);
+    else
+        dq16_item<T, D, MASK, SCHED>(p, smem, b - p.grid_k);
+}
+
 // ---------------------------------------------------------------- reduce
 template <typename T, int D>
 __global__ void __launch_bounds__(256) bwd16_reduce_kernel(ReduceParams r) {
@@ -608,19 +620,13 @@ __global__ void __launch_bounds__(256) bwd16_reduce_kernel(ReduceParams r) {
 
 // ------------------------------------------------------------------ launch
 template <typename T, int D, int MASK>
-static void launch_bwd16_mask(const BwdParams &p, int grid_k, int grid_q, hipStream_t st) {
+static void launch_bwd16_mask(const BwdParams &p, int grid, hipStream_t st) {
     constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
-    if (varlen && p.sched) {
-        if (grid_k > 0)
-            hipLaunchKernelGGL((bwd16_dkdv_kernel<T, D, MASK, varlen>), dim3(grid_k), dim3(kB16T), 0, st, p);
-        if (grid_q > 0)
-            hipLaunchKernelGGL((bwd16_dq_kernel<T, D, MASK, varlen>), dim3(grid_q), dim3(kB16T), 0, st, p);
-        return;
-    }
-    if (grid_k > 0)
-        hipLaunchKernelGGL((bwd16_dkdv_kernel<T, D, MASK, false>), dim3(grid_k), dim3(kB16T), 0, st, p);
-    if (grid_q > 0)
-        hipLaunchKernelGGL((bwd16_dq_kernel<T, D, MASK, false>), dim3(grid_q), dim3(kB16T), 0, st, p);
+    if (grid <= 0) return;
+    if (varlen && p.sched)
+        hipLaunchKernelGGL((bwd16_kernel<T, D, MASK, varlen>), dim3(grid), dim3(kB16T), 0, st, p);
+    else
+        hipLaunchKernelGGL((bwd16_kernel<T, D, MASK, false>), dim3(grid), dim3(kB16T), 0, st, p);
 }
 
 hipError_t launch_varlen_schedule(int d, int causal, const int32_t *cu, int num_seqs, int n,
@@ -635,12 +641,15 @@ static hipError_t launch_bwd16_typed(int mask, const BwdParams &p, int seqs, hip
     int64_t grid_k = (int64_t)p.H * p.k_splits * seqs * p.k_tiles;
     int64_t grid_q = (int64_t)p.H * p.q_splits * seqs * p.q_tiles;
     if (p.sched) grid_k = grid_q = (int64_t)p.H * p.sched_max;  // one workgroup per listed pair
-    if (grid_k > 0x7fffffffLL || grid_q > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (grid_k + grid_q > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    BwdParams pf = p;
+    pf.grid_k = (int)grid_k;
+    const int grid = (int)(grid_k + grid_q);
     switch (mask) {
-        case kDense: launch_bwd16_mask<T, D, kDense>(p, (int)grid_k, (int)grid_q, st); break;
-        case kCausal: launch_bwd16_mask<T, D, kCausal>(p, (int)grid_k, (int)grid_q, st); break;
-        case kVarlen: launch_bwd16_mask<T, D, kVarlen>(p, (int)grid_k, (int)grid_q, st); break;
-        default: launch_bwd16_mask<T, D, kVarlenCausal>(p, (int)grid_k, (int)grid_q, st); break;
+        case kDense: launch_bwd16_mask<T, D, kDense>(pf, grid, st); break;
+        case kCausal: launch_bwd16_mask<T, D, kCausal>(pf, grid, st); break;
+        case kVarlen: launch_bwd16_mask<T, D, kVarlen>(pf, grid, st); break;
+        default: launch_bwd16_mask<T, D, kVarlenCausal>(pf, grid, st); break;
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;

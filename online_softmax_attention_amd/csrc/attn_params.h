@@ -84,6 +84,7 @@ struct BwdParams {
     // dK/dV and dQ launches; null for the natural grid.
     const int32_t *sched;
     int sched_max;
+    int grid_k;            // fp16/bf16: blocks of the one launch that run dK/dV items
 };
 
 // CSR segment softmax over given edge scores.
