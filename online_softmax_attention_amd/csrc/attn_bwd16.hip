@@ -169,7 +169,10 @@ __device__ __forceinline__ void dkdv16_tile(const BwdParams &p, char *smem, int 
     const int qa = causal ? max(qs_all.lo, k_lo) : qs_all.lo;
     const Range16 qr = split16(qa, qs_all.hi, split, p.k_splits, C::BQ);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // The wave index is uniform; taking it into a scalar register makes the
+    // per-wave tests below (tail, diagonal chunk) scalar branches instead of
+    // masked selects on every element.
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kq = wave & 3, qg = wave >> 2;  // key group, query half
     const int c32 = lane & 31, g = lane >> 5;
     const int key = k_lo + 32 * kq + c32;      // this lane's key column
@@ -253,23 +256,25 @@ __device__ __forceinline__ void dkdv16_tile(const BwdParams &p, char *smem, int 
             if (qc0 >= qr.hi) break;
             if (causal && k_lo + 32 * kq > qc0 + 31) continue;  // every pair masked
             // S = Q K^T and dP = dO V^T: rows = the chunk's queries, column =
-            // this lane's key.
+            // this lane's key.  The two chains alternate so that each one's
+            // LDS reads are in flight while the other's MFMA runs.
             f32x16 S = zero_vec<f32x16>(), dP = zero_vec<f32x16>();
             const int qrow = ql0 + c32;
 #pragma unroll
             for (int kk = 0; kk < C::NKK; ++kk) {
                 const vec8 qa8 = *reinterpret_cast<const vec8 *>(sq + qrow * C::ROW + swz_rt<C::ROW>(qrow, 2 * kk + g) * 16);
                 const vec8 kb8 = *reinterpret_cast<const vec8 *>(sK + krow * C::ROW + swz_k<C::ROW>(krow, 2 * kk + g) * 16);
-                S = Half8<T>::mma(qa8, kb8, S);
-            }
-#pragma unroll
-            for (int kk = 0; kk < C::NKK; ++kk) {
                 const vec8 da8 = *reinterpret_cast<const vec8 *>(sdo + qrow * C::ROW + swz_rt<C::ROW>(qrow, 2 * kk + g) * 16);
                 const vec8 vb8 = *reinterpret_cast<const vec8 *>(sV + krow * C::ROW + swz_k<C::ROW>(krow, 2 * kk + g) * 16);
+                S = Half8<T>::mma(qa8, kb8, S);
                 dP = Half8<T>::mma(da8, vb8, dP);
             }
             // P = 2^(s c - beta), zero where key > query; dS = P (dP - D).
-            const bool diag = causal && k_lo + 32 * kq + 31 > qc0;
+            if (causal && k_lo + 32 * kq + 31 > qc0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (key > qc0 + acc_row(r, g)) S[r] = kNegInf;
+            }
             f32x16 P, dS;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -278,8 +283,7 @@ __device__ __forceinline__ void dkdv16_tile(const BwdParams &p, char *smem, int 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * i + e;
-                    float pv = fast_exp2(fmaf(S[r], c, -bv[e]));
-                    if (diag && key > qc0 + acc_row(r, g)) pv = 0.f;
+                    const float pv = fast_exp2(fmaf(S[r], c, -bv[e]));
                     P[r] = pv;
                     dS[r] = pv * (dP[r] - dv[e]);
                 }
@@ -402,7 +406,7 @@ __device__ __forceinline__ void dq16_tile(const BwdParams &p, char *smem, int h,
     const Range16 kr = split16(ks_all.lo, kv_end, split, p.q_splits, C::BC);
     const int kv_lo = kr.lo, kv_hi = kr.hi;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
     const int rg = wave & 3, kg = wave >> 2;
     const int c32 = lane & 31, g = lane >> 5;
     const int qrow = q_lo + 32 * rg + c32;
@@ -471,11 +475,8 @@ __device__ __forceinline__ void dq16_tile(const BwdParams &p, char *smem, int h,
 #pragma unroll
                 for (int kk = 0; kk < C::NKK; ++kk) {
                     const vec8 ka = *reinterpret_cast<const vec8 *>(sk + row * C::ROW + swz_rt<C::ROW>(row, 2 * kk + g) * 16);
-                    S = Half8<T>::mma(ka, qreg[kk], S);
-                }
-#pragma unroll
-                for (int kk = 0; kk < C::NKK; ++kk) {
                     const vec8 va = *reinterpret_cast<const vec8 *>(sv + row * C::ROW + swz_k<C::ROW>(row, 2 * kk + g) * 16);
+                    S = Half8<T>::mma(ka, qreg[kk], S);
                     dP = Half8<T>::mma(va, doreg[kk], dP);
                 }
                 if (kc0 + 32 > kv_hi || (causal && kc0 + 31 > wrow_lo)) {
