@@ -2,6 +2,7 @@
 // workspace plan, and dispatch to the HIP kernels.  Declared in osattn.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -99,17 +100,18 @@ int check_tensor(const char *name, const void *p, int64_t sh, int64_t sn, size_t
 }
 
 // Compute units of the current device (cached per device; 256 if unknown).
+// Threads may race to fill an entry; they store the same value.
 int device_cus() {
-    static int cache[64] = {0};
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 
 // ---------------------------------------------------------------- fwd plan
