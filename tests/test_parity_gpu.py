@@ -166,6 +166,55 @@ def test_nhd_layout(osattn, oracle, dtype):
     assert_fwd_close(o, m, l, ro, rm, rl, dtype, "nhd layout")
 
 
+# Head strides past 2^31 elements: head 1 of every tensor starts beyond 4 GiB
+# (bf16) or 8 GiB (f32) from its base, so any 32-bit element or byte offset
+# product in a kernel would land in the wrong place.  q, k and v live in one
+# buffer at different offsets of each head's span (inputs may alias; outputs
+# may not).  The strided results must equal, bit for bit, those of compact
+# copies (the launch plan depends on shapes only), and head 1 is checked
+# against the oracle.
+BIG_STRIDE = (1 << 31) + 4096
+
+
+@pytest.mark.parametrize("dtype,D,causal", [("bf16", 128, True), ("f32", 64, False)])
+def test_head_offsets_past_32_bits(osattn, oracle, dtype, D, causal):
+    H, N = 2, 1024
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    gen = torch.Generator(device="cuda").manual_seed(31)
+    buf = torch.empty(BIG_STRIDE * (H - 1) + 4 * N * D, dtype=tdt, device="cuda")
+    views = []
+    for i in range(4):  # q, k, v, dO
+        t = buf.as_strided((H, N, D), (BIG_STRIDE, D, 1), i * N * D)
+        t.copy_(torch.randn(H, N, D, generator=gen, device="cuda").to(tdt))
+        views.append(t)
+    q, k, v, do = views
+
+    def strided(dt):
+        return torch.empty(BIG_STRIDE * (H - 1) + N * D, dtype=dt, device="cuda").as_strided(
+            (H, N, D), (BIG_STRIDE, D, 1))
+
+    o = strided(torch.float32)
+    m = torch.empty(H, N, device="cuda")
+    l = torch.empty(H, N, device="cuda")
+    osattn.fwd(q, k, v, causal=causal, out=(o, m, l))
+    qc, kc, vc, doc = (t.contiguous() for t in views)
+    oc, mc, lc = osattn.fwd(qc, kc, vc, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o, oc) and torch.equal(m, mc) and torch.equal(l, lc)
+    dq, dk, dv = osattn.bwd(q, k, v, o, do, m, l, causal=causal)
+    dqc, dkc, dvc = osattn.bwd(qc, kc, vc, oc, doc, mc, lc, causal=causal)
+    torch.cuda.synchronize()
+    assert dq.stride() == q.stride() and dk.stride() == k.stride()
+    assert torch.equal(dq, dqc) and torch.equal(dk, dkc) and torch.equal(dv, dvc)
+    # head 1 against the oracle
+    h1 = [host(t[1:2]) for t in (qc, kc, vc)]
+    ro, rm, rl = oracle.attn_fwd(*h1, D ** -0.5, causal=causal)
+    assert_fwd_close(host(o[1:2]), host(m[1:2]), host(l[1:2]), ro, rm, rl, dtype,
+                     "head 1 past 2^31 elements")
+    del buf, views, q, k, v, do, o, dq, dk, dv
+    torch.cuda.empty_cache()  # 24-40 GiB of strided buffers
+
+
 # ------------------------------------------------- pins on the GPU path
 @pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128), ("f32", 64)])
 def test_gpu_zero_query_is_mean_of_values(osattn, dtype, D):
