@@ -11,9 +11,10 @@
 // One wave per (row, head), head fastest so the waves of one row share its
 // column indices in L2.  Pass 1: the row maximum over the segment's scores
 // (64 edges per load).  Pass 2: the 64 lanes form 8 edge slots x 8 feature
-// parts; a slot gathers one source row per step with 16-byte loads (a 128- or
-// 256-byte row split over its 8 lanes), weights it by exp(s - m) and
-// accumulates in f32; the slots then reduce across lanes.  The row pointer and
+// parts; a slot gathers four source rows per step with 16-byte loads (a 128-
+// or 256-byte row split over its 8 lanes), all issued before the first is
+// used, weights them by exp(s - m) and accumulates in f32 in edge order; the
+// slots then reduce across lanes.  The row pointer and
 // column indices are clamped into range, so malformed CSR gives wrong results
 // but no out-of-bounds access.
 #include "attn_device.h"
@@ -21,6 +22,7 @@
 namespace osattn {
 
 constexpr int kCsrWaves = 4;
+constexpr int kCsrUnroll = 4;  // edges per slot per step (row loads in flight per lane)
 
 template <typename T, int D>
 __global__ void __launch_bounds__(64 * kCsrWaves) csr_softmax_kernel(CsrParams p) {
@@ -56,24 +58,39 @@ __global__ void __launch_bounds__(64 * kCsrWaves) csr_softmax_kernel(CsrParams p
         for (int t = 0; t < EPC; ++t) acc[k][t] = 0.f;
     float lsum = 0.f;
     const float m0 = (mx == kNegInf) ? 0.f : mx;  // a row of -inf scores weighs nothing
-    for (int e = lo + slot; e < hi; e += 8) {
-        const float w = fast_exp2((sh[e] - m0) * kLog2e);
-        if (part == 0) lsum += w;
-        int col = p.col_idx[e];
-        col = col < 0 ? 0 : (col >= p.n_src ? p.n_src - 1 : col);
-        const char *vrow = vh + (int64_t)col * p.v_sn * esz;
+    // Each step takes kCsrUnroll edges per slot and issues all their gathers
+    // before the first use, so every lane has that many row loads in flight.
+    for (int e0 = lo + slot; e0 < hi; e0 += 8 * kCsrUnroll) {
+        float w[kCsrUnroll];
+        u32x4 raw[kCsrUnroll][NCH];
 #pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            const u32x4 raw = *reinterpret_cast<const u32x4 *>(vrow + (part + 8 * k) * 16);
-            if constexpr (esz == 4) {
-                const f32x4 x = __builtin_bit_cast(f32x4, raw);
+        for (int u = 0; u < kCsrUnroll; ++u) {
+            const int e = e0 + 8 * u;
+            const bool in = e < hi;
+            const int es = in ? e : e0;  // an edge past the row's end re-reads e0 and weighs 0
+            int col = p.col_idx[es];
+            col = col < 0 ? 0 : (col >= p.n_src ? p.n_src - 1 : col);
+            const char *vrow = vh + (int64_t)col * p.v_sn * esz;
 #pragma unroll
-                for (int t = 0; t < 4; ++t) acc[k][t] = fmaf(w, x[t], acc[k][t]);
-            } else {
-                typedef typename Half8<T>::vec vec8;
-                const vec8 x = __builtin_bit_cast(vec8, raw);
+            for (int k = 0; k < NCH; ++k) raw[u][k] = *reinterpret_cast<const u32x4 *>(vrow + (part + 8 * k) * 16);
+            const float wu = fast_exp2((sh[es] - m0) * kLog2e);
+            w[u] = in ? wu : 0.f;
+        }
 #pragma unroll
-                for (int t = 0; t < 8; ++t) acc[k][t] = fmaf(w, (float)x[t], acc[k][t]);
+        for (int u = 0; u < kCsrUnroll; ++u) {
+            if (part == 0) lsum += w[u];
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) {
+                if constexpr (esz == 4) {
+                    const f32x4 x = __builtin_bit_cast(f32x4, raw[u][k]);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) acc[k][t] = fmaf(w[u], x[t], acc[k][t]);
+                } else {
+                    typedef typename Half8<T>::vec vec8;
+                    const vec8 x = __builtin_bit_cast(vec8, raw[u][k]);
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) acc[k][t] = fmaf(w[u], (float)x[t], acc[k][t]);
+                }
             }
         }
     }
