@@ -202,6 +202,13 @@ struct Fwd16Cfg {
     static_assert(NST * STAGE == LDS, "stages fill the workgroup's LDS");
 };
 
+// The end-of-tile merge is shared by all waves when there are four or more key
+// groups and every wave's U fits in the stages' LDS; otherwise key group 0
+// merges alone.
+template <int D, int NST, int NW, int RG>
+constexpr bool kSharedMerge =
+    NW / RG >= 4 && 8192 + NW * (D / 8) * 64 * 16 <= NST * Fwd16Cfg<D, NST, NW>::STAGE;
+
 // Wait until at most `blocks` blocks of this thread's DMA are still in flight.
 template <int NDMA_BLOCK, int NST>
 __device__ __forceinline__ void wait_dma_blocks(int blocks) {
@@ -468,10 +475,81 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
     }
     __syncthreads();  // every wave is done with the last stage
 
-    // F7: merge the KG key groups of each row, then O = U / l.  Groups 1..KG-1
-    // leave (m_ref, m_true, l) and U in LDS; group 0 rescales all KG states to
-    // the largest reference M and sums them in a fixed order.
+    // F7: merge the KG key groups of each row, then O = U / l.
     l_run = xor32_sum(l_run);
+    if constexpr (kSharedMerge<D, NST, NW, RG>) {
+        // Four or more key groups: every wave leaves (m_ref, m_true, l) and U
+        // in LDS, then the KG waves of a row group each take an equal share of
+        // the 16-byte feature slots, rescale all KG states to the largest
+        // reference M, sum them in group order and store their share of O (or
+        // of the partial state).
+        constexpr int SL = (D / 8) / KG;  // feature slots (4 features x 64 lanes) per wave
+        float *st = reinterpret_cast<float *>(smem);         // (NW waves, 3, 64) floats
+        f32x4 *su = reinterpret_cast<f32x4 *>(smem + 8192);  // (NW waves, D/8, 64) float4
+        st[(wave * 3 + 0) * 64 + lane] = m_ref;
+        st[(wave * 3 + 1) * 64 + lane] = m_true;
+        st[(wave * 3 + 2) * 64 + lane] = l_run;
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 v = {U[dt][4 * j], U[dt][4 * j + 1], U[dt][4 * j + 2], U[dt][4 * j + 3]};
+                su[(wave * (D / 8) + dt * 4 + j) * 64 + lane] = v;
+            }
+        __syncthreads();
+        float M_raw = kNegInf, mt = kNegInf;
+#pragma unroll
+        for (int k = 0; k < KG; ++k) {
+            M_raw = vmax(M_raw, st[((rg + RG * k) * 3 + 0) * 64 + lane]);
+            mt = vmax(mt, st[((rg + RG * k) * 3 + 1) * 64 + lane]);
+        }
+        const float M = (M_raw == kNegInf) ? 0.f : M_raw;
+        float a[KG];
+#pragma unroll
+        for (int k = 0; k < KG; ++k) a[k] = fast_exp2((st[((rg + RG * k) * 3 + 0) * 64 + lane] - M) * c);
+        float l = st[(rg * 3 + 2) * 64 + lane] * a[0];
+#pragma unroll
+        for (int k = 1; k < KG; ++k) l += st[((rg + RG * k) * 3 + 2) * 64 + lane] * a[k];
+        if (qrow < q_hi) {
+            const float inv = 1.f / l;
+#pragma unroll
+            for (int i = 0; i < SL; ++i) {
+                const int sl = kg * SL + i, dt = sl >> 2, j = sl & 3;
+                const int feat = 32 * dt + 8 * j + 4 * g;
+                f32x4 acc = su[(rg * (D / 8) + sl) * 64 + lane] * a[0];
+#pragma unroll
+                for (int k = 1; k < KG; ++k) {
+                    const f32x4 u = su[((rg + RG * k) * (D / 8) + sl) * 64 + lane];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] = fmaf(u[e], a[k], acc[e]);
+                }
+                if (split >= 0) {
+                    float *prow = p.part + (((int64_t)split * p.H + h) * p.n_q + qrow) * (D + 4);
+                    *reinterpret_cast<f32x4 *>(prow + feat) = acc;
+                } else {
+                    const int64_t off = (int64_t)h * p.o_sh + (int64_t)qrow * p.o_sn + feat;
+                    const f32x4 val = acc * inv;
+                    if constexpr (O16) store4_16(static_cast<T *>(p.o) + off, val);
+                    else *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + off) = val;
+                }
+            }
+            if (kg == 0 && g == 0) {
+                if (split >= 0) {
+                    float *prow = p.part + (((int64_t)split * p.H + h) * p.n_q + qrow) * (D + 4);
+                    const f32x4 stv = {M_raw, mt, l, 0.f};
+                    *reinterpret_cast<f32x4 *>(prow + D) = stv;
+                } else {
+                    p.m[(int64_t)h * p.n_q + qrow] = mt * p.scale;
+                    p.l[(int64_t)h * p.n_q + qrow] = l * fast_exp2((M - mt) * c);
+                }
+            }
+        }
+        __syncthreads();  // the next tile's prologue reuses this LDS
+        return;
+    }
+    // Fewer key groups: groups 1..KG-1 leave (m_ref, m_true, l) and U in LDS;
+    // group 0 rescales all KG states to the largest reference M and sums them
+    // in a fixed order.
     float *st = reinterpret_cast<float *>(smem);           // (NW waves, 3, 64) floats
     f32x4 *su = reinterpret_cast<f32x4 *>(smem + 8192);    // (NW - RG waves, D/8, 64) float4
     if (kg != 0) {
