@@ -39,7 +39,7 @@ struct FwdWork {
 };
 
 template <int MASK>
-__device__ __forceinline__ FwdWork fwd_work(const FwdParams &p) {
+__device__ __forceinline__ FwdWork fwd_work(const FwdParams &p, int tile_rows = kBR) {
     constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
     constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
     const int b = blockIdx.x;
@@ -54,8 +54,8 @@ __device__ __forceinline__ FwdWork fwd_work(const FwdParams &p) {
         seq_hi = s.hi;
     }
     const int tile = causal ? (p.n_tiles - 1 - rest) : rest;  // heaviest first
-    w.q_lo = seq_lo + tile * kBR;
-    w.q_hi = min(w.q_lo + kBR, seq_hi);
+    w.q_lo = seq_lo + tile * tile_rows;
+    w.q_hi = min(w.q_lo + tile_rows, seq_hi);
     w.ok = w.q_lo < seq_hi;
     w.kv_lo = seq_lo;
     w.kv_hi = varlen ? (causal ? w.q_hi : seq_hi) : (causal ? w.q_hi : p.n_k);
@@ -961,21 +961,29 @@ hipError_t launch_forward_pruned(int dtype, int d, FwdParams p, hipStream_t st) 
 // MFMA v_mfma_f32_32x32x2_f32.  The contraction slots of K Q^T are assigned so
 // that lane half g covers features [g D/2, (g+1) D/2): Q stays in registers and
 // K is read in 16-byte vectors.  P stays f32.
-template <int D, int BC, int MASK>
+// KG = 1: 128-row tiles, each wave 32 rows against all BC keys of a block.
+// KG = 4 (dense only): 32-row tiles, each wave a key group of BC keys of every
+// 4 BC-key block; the four states merge through LDS at the end, each wave
+// merging and storing a quarter of the features.  A grid of 32-row tiles
+// fills the device where 128-row tiles would need their keys split over
+// workgroups and a combine launch.
+template <int D, int BC, int MASK, int KG = 1>
 __global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) fwd32_kernel(FwdParams p) {
     constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
+    constexpr int BK = KG * BC;                // keys per block
     constexpr int KCH = D / 4;                 // 16-byte chunks per row
-    constexpr int LD = BC * KCH / kThreads;    // chunks per thread per tensor
+    constexpr int LD = BK * KCH / kThreads;    // chunks per thread per tensor
     constexpr int NS = BC / 32, NDT = D / 32, NQ = D / 2, NJ = D / 8;
-    static_assert(LD * kThreads == BC * KCH, "block must split evenly over the threads");
+    static_assert(LD * kThreads == BK * KCH, "block must split evenly over the threads");
+    static_assert(KG == 1 || (KG == 4 && MASK == kDense), "key groups serve the dense relation");
 
-    __shared__ u32x4 sK[BC * KCH];
-    __shared__ u32x4 sV[BC * KCH];
+    __shared__ u32x4 sK[BK * KCH];
+    __shared__ u32x4 sV[BK * KCH];
 
     FwdWork w;
     int split = -1;
     if constexpr (MASK == kDense) {
-        if (p.splits > 1) {
+        if (KG == 1 && p.splits > 1) {
             // Split-KV item: key range `split` of one tile, split index slowest.
             const int items = p.H * p.n_tiles;
             split = (int)blockIdx.x / items;
@@ -987,7 +995,7 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) fwd32_kernel(FwdPar
             w.kv_lo = split * p.split_len;
             w.kv_hi = min(w.kv_lo + p.split_len, p.n_k);
         } else {
-            w = fwd_work<MASK>(p);
+            w = fwd_work<MASK>(p, 128 / KG);
         }
     } else {
         w = fwd_work<MASK>(p);
@@ -995,11 +1003,12 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) fwd32_kernel(FwdPar
     if (!w.ok) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c32 = lane & 31, g = lane >> 5;
+    const int kg = KG == 1 ? 0 : wave;         // key group
     const float *qh = static_cast<const float *>(p.q) + (int64_t)w.h * p.q_sh;
     const float *kh = static_cast<const float *>(p.k) + (int64_t)w.h * p.kv_sh;
     const float *vh = static_cast<const float *>(p.v) + (int64_t)w.h * p.kv_sh;
 
-    const int qrow = w.q_lo + wave * 32 + c32;
+    const int qrow = w.q_lo + (KG == 1 ? wave * 32 : 0) + c32;
     const bool qok = qrow < w.q_hi;
     float qreg[NQ];
 #pragma unroll
@@ -1035,22 +1044,24 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) fwd32_kernel(FwdPar
     for (int dt = 0; dt < NDT; ++dt) U[dt] = zero_vec<f32x16>();
     float m_run = kNegInf, l_run = 0.f;
     const float c = p.scale_log2;
-    const int nblk = (w.kv_hi - w.kv_lo + BC - 1) / BC;
+    const int nblk = (w.kv_hi - w.kv_lo + BK - 1) / BK;
     const float *sVf = reinterpret_cast<const float *>(sV);
 
     gload(w.kv_lo);
     for (int kb = 0; kb < nblk; ++kb) {
-        const int k0 = w.kv_lo + kb * BC;
+        const int k0 = w.kv_lo + kb * BK;
+        const int kw0 = k0 + kg * BC;          // this wave's first key
         __syncthreads();
         lds_store();
         __syncthreads();
-        if (kb + 1 < nblk) gload(k0 + BC);
+        if (kb + 1 < nblk) gload(k0 + BK);
+        if (KG > 1 && kw0 >= w.kv_hi) continue;  // a tail block without this group's keys
 
         f32x16 S[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             S[s] = zero_vec<f32x16>();
-            const u32x4 *krow = &sK[(32 * s + c32) * KCH];
+            const u32x4 *krow = &sK[(kg * BC + 32 * s + c32) * KCH];
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const f32x4 a = __builtin_bit_cast(f32x4, krow[swz(c32, (D / 8) * g + j)]);
@@ -1058,8 +1069,8 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) fwd32_kernel(FwdPar
                 for (int e = 0; e < 4; ++e) S[s] = mma_f32(a[e], qreg[4 * j + e], S[s]);
             }
         }
-        if (k0 + BC > w.kv_hi || (causal && k0 + BC - 1 > w.q_lo))
-            mask_block<NS, causal>(S, k0, g, w.kv_hi, qrow);
+        if (kw0 + BC > w.kv_hi || (causal && kw0 + BC - 1 > w.q_lo))
+            mask_block<NS, causal>(S, kw0, g, w.kv_hi, qrow);
         const float alpha = online_update<NS>(S, m_run, l_run, c);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) U[dt] *= alpha;
@@ -1067,7 +1078,7 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) fwd32_kernel(FwdPar
         for (int s = 0; s < NS; ++s)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int kl = 32 * s + acc_row(r, g);
+                const int kl = kg * BC + 32 * s + acc_row(r, g);
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
                     const int d = 32 * dt + c32;
@@ -1075,6 +1086,59 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) fwd32_kernel(FwdPar
                     U[dt] = mma_f32(a, S[s][r], U[dt]);
                 }
             }
+    }
+    if constexpr (KG > 1) {
+        // Merge the key groups: every wave leaves (m, l, U) in LDS; wave kg then
+        // rescales the KG states of each row to the largest maximum, sums them
+        // in group order over its quarter of the features and stores it.
+        constexpr int SL = (D / 8) / KG;  // 16-byte feature slots per wave
+        static_assert(SL * KG == D / 8 && KG * (D / 8) * 64 * 16 <= (int)sizeof(sK) &&
+                          KG * 2 * 64 * 4 <= (int)sizeof(sV),
+                      "merge buffers fit in the key and value tiles");
+        const float l_tot = l_run + __shfl_xor(l_run, 32);
+        __syncthreads();  // every wave is done with the last block
+        float *st = reinterpret_cast<float *>(sV);  // (KG, 2, 64) floats: m, l
+        f32x4 *su = reinterpret_cast<f32x4 *>(sK);  // (KG, D/8, 64) float4: U
+        st[(kg * 2 + 0) * 64 + lane] = m_run;
+        st[(kg * 2 + 1) * 64 + lane] = l_tot;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 v = {U[dt][4 * j], U[dt][4 * j + 1], U[dt][4 * j + 2], U[dt][4 * j + 3]};
+                su[(kg * (D / 8) + dt * 4 + j) * 64 + lane] = v;
+            }
+        __syncthreads();
+        float M = kNegInf;
+#pragma unroll
+        for (int k = 0; k < KG; ++k) M = fmaxf(M, st[(k * 2 + 0) * 64 + lane]);
+        const float Mu = (M == kNegInf) ? 0.f : M;
+        float a[KG];
+#pragma unroll
+        for (int k = 0; k < KG; ++k) a[k] = fast_exp2((st[(k * 2 + 0) * 64 + lane] - Mu) * c);
+        float l = st[1 * 64 + lane] * a[0];
+#pragma unroll
+        for (int k = 1; k < KG; ++k) l += st[(k * 2 + 1) * 64 + lane] * a[k];
+        if (!qok) return;
+        const float inv = 1.f / l;
+        float *orow = static_cast<float *>(p.o) + (int64_t)w.h * p.o_sh + (int64_t)qrow * p.o_sn;
+#pragma unroll
+        for (int i = 0; i < SL; ++i) {
+            const int sl = kg * SL + i;
+            f32x4 acc = su[sl * 64 + lane] * a[0];
+#pragma unroll
+            for (int k = 1; k < KG; ++k) {
+                const f32x4 u = su[(k * (D / 8) + sl) * 64 + lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = fmaf(u[e], a[k], acc[e]);
+            }
+            *reinterpret_cast<f32x4 *>(orow + 32 * (sl >> 2) + 8 * (sl & 3) + 4 * g) = acc * inv;
+        }
+        if (kg == 0 && g == 0) {
+            p.m[(int64_t)w.h * p.n_q + qrow] = M * p.scale;
+            p.l[(int64_t)w.h * p.n_q + qrow] = l;
+        }
+        return;
     }
     if (split >= 0) fwd_partial<NDT>(p, w, split, qrow, g, U, m_run, l_run);
     else fwd_epilogue<NDT>(p, w, qrow, g, U, m_run, l_run);
@@ -1120,7 +1184,9 @@ static void launch_fwd_mask(int dtype, int d, const FwdParams &p, int grid16, in
         if (d == 64) launch_fwd16<__bf16, 64, MASK>(p, grid16, st);
         else launch_fwd16<__bf16, 128, MASK>(p, grid16, st);
     } else {
-        if (d == 64) hipLaunchKernelGGL((fwd32_kernel<64, 64, MASK>), dim3(grid32), dim3(kThreads), 0, st, p);
+        if (d == 64 && MASK == kDense && p.f32_groups == 4)
+            hipLaunchKernelGGL((fwd32_kernel<64, 32, kDense, 4>), dim3(grid32), dim3(kThreads), 0, st, p);
+        else if (d == 64) hipLaunchKernelGGL((fwd32_kernel<64, 64, MASK>), dim3(grid32), dim3(kThreads), 0, st, p);
         else hipLaunchKernelGGL((fwd32_kernel<128, 32, MASK>), dim3(grid32), dim3(kThreads), 0, st, p);
     }
 }
@@ -1133,6 +1199,7 @@ hipError_t launch_forward(int dtype, int d, int mask, FwdParams p, int max_seqle
     // 16-bit tiles are p.tile_rows (128, or 64 / 32 for small dense and causal
     // problems); f32 tiles are kBR.
     if (dtype == 0 || varlen || (p.tile_rows != 64 && p.tile_rows != 32)) p.tile_rows = kBR;
+    if (dtype == 0 && p.f32_groups == 4) p.tile_rows = 32;  // f32 key groups: 32-row tiles
     if (d != 64 && p.tile_rows == 32) p.tile_rows = 64;
     p.n_tiles = (rows + p.tile_rows - 1) / p.tile_rows;
     const int64_t seqs = varlen ? p.num_seqs : 1;

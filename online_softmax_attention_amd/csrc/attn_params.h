@@ -53,6 +53,7 @@ struct FwdParams {
     int sched_inline;
     int o16;               // o holds the input dtype instead of f32
     float prune_thr;       // tile pruning: ln(rho) / scale (raw score units)
+    int f32_groups;        // f32 dense, d = 64: 4 = 32-row tiles of four key groups, else 1
 };
 
 struct BwdParams {
