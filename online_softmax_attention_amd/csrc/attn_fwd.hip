@@ -547,9 +547,82 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
         __syncthreads();  // the next tile's prologue reuses this LDS
         return;
     }
-    // Fewer key groups: groups 1..KG-1 leave (m_ref, m_true, l) and U in LDS;
-    // group 0 rescales all KG states to the largest reference M and sums them
-    // in a fixed order.
+    if constexpr (KG == 2) {
+        // Two key groups: each wave leaves its row state and the half of U its
+        // partner merges in LDS, then merges and stores its own half (group 0's
+        // state first, as below).
+        constexpr int SL = D / 16;  // 16-byte feature slots per wave: half of D / 8
+        float *st = reinterpret_cast<float *>(smem);         // (NW waves, 3, 64) floats
+        f32x4 *su = reinterpret_cast<f32x4 *>(smem + 8192);  // (NW waves, SL, 64) float4
+        const int wp = kg == 0 ? wave + RG : wave - RG;      // the partner wave (same rows)
+        st[(wave * 3 + 0) * 64 + lane] = m_ref;
+        st[(wave * 3 + 1) * 64 + lane] = m_true;
+        st[(wave * 3 + 2) * 64 + lane] = l_run;
+        const auto put = [&](auto kgc) {  // the partner's half of U
+            constexpr int K = decltype(kgc)::value;
+#pragma unroll
+            for (int i = 0; i < SL; ++i) {
+                const int sl = (1 - K) * SL + i, dt = sl >> 2, j = sl & 3;
+                const f32x4 v = {U[dt][4 * j], U[dt][4 * j + 1], U[dt][4 * j + 2], U[dt][4 * j + 3]};
+                su[(wave * SL + i) * 64 + lane] = v;
+            }
+        };
+        if (kg == 0) put(std::integral_constant<int, 0>{});
+        else put(std::integral_constant<int, 1>{});
+        __syncthreads();
+        const float m_p = st[(wp * 3 + 0) * 64 + lane], mt_p = st[(wp * 3 + 1) * 64 + lane];
+        const float l_p = st[(wp * 3 + 2) * 64 + lane];
+        const float m0 = kg == 0 ? m_ref : m_p, m1 = kg == 0 ? m_p : m_ref;
+        const float M_raw = vmax(m0, m1);
+        const float mt = vmax(kg == 0 ? m_true : mt_p, kg == 0 ? mt_p : m_true);
+        const float M = (M_raw == kNegInf) ? 0.f : M_raw;
+        const float a0 = fast_exp2((m0 - M) * c), a1 = fast_exp2((m1 - M) * c);
+        float l = (kg == 0 ? l_run : l_p) * a0;
+        l += (kg == 0 ? l_p : l_run) * a1;
+        const auto fin = [&](auto kgc) {  // this wave's half of O (or of the partial state)
+            constexpr int K = decltype(kgc)::value;
+            const float inv = 1.f / l;
+#pragma unroll
+            for (int i = 0; i < SL; ++i) {
+                const int sl = K * SL + i, dt = sl >> 2, j = sl & 3;
+                const int feat = 32 * dt + 8 * j + 4 * g;
+                const f32x4 own = {U[dt][4 * j], U[dt][4 * j + 1], U[dt][4 * j + 2], U[dt][4 * j + 3]};
+                const f32x4 par = su[(wp * SL + i) * 64 + lane];
+                const f32x4 u0 = K == 0 ? own : par, u1 = K == 0 ? par : own;
+                f32x4 acc = u0 * a0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = fmaf(u1[e], a1, acc[e]);
+                if (split >= 0) {
+                    float *prow = p.part + (((int64_t)split * p.H + h) * p.n_q + qrow) * (D + 4);
+                    *reinterpret_cast<f32x4 *>(prow + feat) = acc;
+                } else {
+                    const int64_t off = (int64_t)h * p.o_sh + (int64_t)qrow * p.o_sn + feat;
+                    const f32x4 val = acc * inv;
+                    if constexpr (O16) store4_16(static_cast<T *>(p.o) + off, val);
+                    else *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + off) = val;
+                }
+            }
+        };
+        if (qrow < q_hi) {
+            if (kg == 0) fin(std::integral_constant<int, 0>{});
+            else fin(std::integral_constant<int, 1>{});
+            if (kg == 0 && g == 0) {
+                if (split >= 0) {
+                    float *prow = p.part + (((int64_t)split * p.H + h) * p.n_q + qrow) * (D + 4);
+                    const f32x4 stv = {M_raw, mt, l, 0.f};
+                    *reinterpret_cast<f32x4 *>(prow + D) = stv;
+                } else {
+                    p.m[(int64_t)h * p.n_q + qrow] = mt * p.scale;
+                    p.l[(int64_t)h * p.n_q + qrow] = l * fast_exp2((M - mt) * c);
+                }
+            }
+        }
+        __syncthreads();  // the next tile's prologue reuses this LDS
+        return;
+    }
+    // One key group, or more than two without room for the shared merge:
+    // groups 1..KG-1 leave (m_ref, m_true, l) and U in LDS; group 0 rescales
+    // all KG states to the largest reference M and sums them in a fixed order.
     float *st = reinterpret_cast<float *>(smem);           // (NW waves, 3, 64) floats
     f32x4 *su = reinterpret_cast<f32x4 *>(smem + 8192);    // (NW - RG waves, D/8, 64) float4
     if (kg != 0) {
