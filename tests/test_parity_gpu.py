@@ -215,6 +215,83 @@ def test_head_offsets_past_32_bits(osattn, oracle, dtype, D, causal):
     torch.cuda.empty_cache()  # 24-40 GiB of strided buffers
 
 
+# Captured HIP graphs: the forward and backward (with their workspaces, the
+# split-KV combine, the varlen list kernel and the split reductions) captured
+# once and replayed with new input contents written between replays; every
+# replay must equal, bit for bit, an eager call on the same inputs made between
+# the replays.  Nothing in a launch may depend on state a previous launch left.
+GRAPH_CASES = [
+    # (H, n_q, n_k, D, dtype, causal, lengths)
+    (2, 256, 4096, 64, torch.float16, False, None),    # 16-bit split-KV + combine
+    (2, 640, 640, 128, torch.bfloat16, True, None),    # causal tile pairs
+    (2, 0, 0, 64, torch.float16, True, "inline"),      # varlen, items ranked in-kernel
+    (1, 0, 0, 64, torch.bfloat16, False, "list"),      # varlen, > 64 sequences: list kernel
+    (1, 1024, 2048, 64, torch.float32, False, None),   # f32 split-KV + split reductions
+    (1, 128, 128, 64, torch.float32, False, None),     # f32 32-row tiles of four key groups
+]
+
+
+@pytest.mark.parametrize("case", GRAPH_CASES, ids=lambda c: "%s-%s-%s" % (c[4], c[5], c[6] or c[1]))
+def test_graph_replays_match_eager(osattn, case):
+    H, n_q, n_k, D, dt, causal, lens = case
+    gen = torch.Generator().manual_seed(2024)
+    cu, ms = None, None
+    if lens is not None:
+        count = 20 if lens == "inline" else 80
+        lengths = torch.randint(1, 300, (count,), generator=gen)
+        lengths[3] = 0
+        n_q = n_k = int(lengths.sum())
+        cu = torch.cat([torch.zeros(1, dtype=torch.int64), lengths.cumsum(0)]).to(torch.int32).cuda()
+        ms = int(lengths.max())
+    q, do = (torch.empty(H, n_q, D, dtype=dt, device="cuda") for _ in range(2))
+    k, v = (torch.empty(H, n_k, D, dtype=dt, device="cuda") for _ in range(2))
+
+    def fill():
+        for t in (q, k, v, do):
+            t.copy_(torch.randn(t.shape, generator=gen).to(dt))
+
+    o = torch.empty(H, n_q, D, device="cuda")
+    m, l = torch.empty(H, n_q, device="cuda"), torch.empty(H, n_q, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ncu = 0 if cu is None else cu.numel() - 1
+    dcode = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}[dt]
+    fws = torch.empty(max(osattn.load().osattn_fwd_workspace_bytes(
+        dcode, H, n_q, n_k, D, int(causal), None if cu is None else cu.data_ptr(), ncu, ms or 0), 256),
+        dtype=torch.uint8, device="cuda")
+    bws = torch.empty(max(osattn.bwd_workspace_bytes(dt, H, n_q, n_k, D, causal, cu, ms or 0), 256),
+                      dtype=torch.uint8, device="cuda")
+
+    def step():
+        osattn.fwd(q, k, v, causal=causal, cu_seqlens=cu, max_seqlen=ms, check=False,
+                   out=(o, m, l), workspace=fws)
+        osattn.bwd(q, k, v, o, do, m, l, causal=causal, cu_seqlens=cu, max_seqlen=ms, check=False,
+                   workspace=bws, out=(dq, dk, dv))
+
+    fill()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        fill()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (o, m, l, dq, dk, dv)]
+        ro, rm, rl = osattn.fwd(q, k, v, causal=causal, cu_seqlens=cu, max_seqlen=ms)
+        rdq, rdk, rdv = osattn.bwd(q, k, v, ro, do, rm, rl, causal=causal, cu_seqlens=cu, max_seqlen=ms)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("o", "m", "l", "dq", "dk", "dv"), got, (ro, rm, rl, rdq, rdk, rdv)):
+            assert torch.equal(a, b), "replay %d: %s differs from the eager call" % (rep, name)
+    del g
+
+
 # ------------------------------------------------- pins on the GPU path
 @pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128), ("f32", 64)])
 def test_gpu_zero_query_is_mean_of_values(osattn, dtype, D):
