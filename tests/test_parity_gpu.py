@@ -413,6 +413,35 @@ def test_bwd_parity_16bit(osattn, oracle, dtype, D, causal, n_q, n_k, H, lengths
         assert torch.equal(a, b)
 
 
+# Wide score range: q scaled by 4 and k by 4 x 2^(4 j / n_k) (powers of two,
+# so the stored values stay exact), which puts the scores in the hundreds of
+# natural-log units and raises the row maximum block after block: the softmax
+# is nearly one-hot and the running reference moves (the U rescale) many times
+# per row.
+@pytest.mark.parametrize("dtype,D,causal", [("f16", 64, False), ("bf16", 128, True), ("f32", 64, False),
+                                            ("f16", 128, True)])
+def test_wide_score_range(osattn, oracle, dtype, D, causal):
+    n = 700
+    w = small("wide", 2, n, n, D, dtype, causal, 880 + D, backward=True)
+    inp = W.make_inputs(w)
+    ramp = (2.0 ** np.floor(4 * np.arange(n) / n)).astype(np.float32)
+    q, q32 = W.round_to_dtype(inp.q32 * 4, dtype)
+    k, k32 = W.round_to_dtype(inp.k32 * 4 * ramp[None, :, None], dtype)
+    np.testing.assert_array_equal(q32, inp.q32 * 4)  # scaling by powers of two is exact
+    np.testing.assert_array_equal(k32, inp.k32 * 4 * ramp[None, :, None])
+    qd, kd, vd, dod = to_dev(q, dtype), to_dev(k, dtype), to_dev(inp.v, dtype), to_dev(inp.do, dtype)
+    o, m, l = osattn.fwd(qd, kd, vd, scale=w.softmax_scale, causal=causal)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attn_fwd(q32, k32, inp.v32, w.softmax_scale, causal=causal)
+    assert np.max(np.abs(rm)) > 100  # scores in the hundreds of natural-log units
+    assert_fwd_close(host(o), host(m), host(l), ro, rm, rl, dtype, "wide scores %s D=%d" % (dtype, D))
+    dq, dk, dv = osattn.bwd(qd, kd, vd, o, dod, m, l, scale=w.softmax_scale, causal=causal)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, *_ = oracle.attn_bwd(q32, k32, inp.v32, inp.do32, w.softmax_scale, causal=causal)
+    for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        assert_grad_close(host(g), r, dtype, "wide scores %s %s D=%d" % (name, dtype, D))
+
+
 # Full-size backward at the fp16/bf16 workloads' shapes.  The oracle runs on the
 # sampled heads only, and on varlen one packed sequence at a time (sequences
 # are independent: the oracle pins check varlen against per-sequence runs).
