@@ -655,7 +655,8 @@ def test_csr_softmax_causal_relation_matches_attention(osattn, oracle):
 # small grid, causal pairs, the four-wave grid, the split combine, in-kernel
 # varlen ranking and the pruned forward.
 O16_CASES = [
-    ("f16", 64, False, 300, 300, 2, None),
+    ("f16", 64, False, 300, 300, 2, None),   # 32-row tiles: eight key groups share the merge
+    ("f16", 64, True, 1000, 1000, 8, None),  # 64-row tiles: four key groups share the merge
     ("bf16", 128, True, 700, 700, 2, None),
     ("f16", 64, False, 4096 - 37, 4000, 16, None),
     ("bf16", 128, False, 129, 4097, 1, None),
