@@ -259,7 +259,7 @@ struct BwdPlan {
 
 int clampi(int64_t x, int lo, int hi) { return (int)(x < lo ? lo : (x > hi ? hi : x)); }
 
-BwdPlan plan_backward(int dtype, int H, int64_t n_q, int64_t n_k, int d, const int32_t *cu,
+BwdPlan plan_backward(int dtype, int H, int64_t n_q, int64_t n_k, int d, int causal, const int32_t *cu,
                       int num_seqs, int max_seqlen) {
     BwdPlan pl{};
     const bool varlen = cu != nullptr;
@@ -268,9 +268,17 @@ BwdPlan plan_backward(int dtype, int H, int64_t n_q, int64_t n_k, int d, const i
     const int64_t klen = varlen ? max_seqlen : n_k;
     pl.q_tiles = (int)((qlen + 127) / 128);
     pl.k_tiles = (int)((klen + 127) / 128);
-    // Aim for ~512 workgroups (two per CU) per pass; a split keeps at least
-    // 256 positions of the reduced axis.
-    const int64_t target = 512;
+    // Workgroups per pass to aim for; a split keeps at least 256 positions of
+    // the reduced axis.  Every backward kernel runs one workgroup per CU, so a
+    // second round of workgroups only adds partial sums to write and reduce.
+    // f32: one round per pass (SQ=8192 SK=2048 H=1 D=64: 162.4 -> 155.1 us
+    // against two rounds).  fp16/bf16 runs both passes in one launch: dense aims
+    // at half the CUs per pass, one round in all (N=4096 H=1 D=128 bf16: 81.3
+    // -> 52.6 us; N=2048 H=2 D=64 fp16: 36.7 -> 29.8 us); causal items are
+    // unequal and balance better with a full round per pass (N=4096 H=2 D=128:
+    // 82.1 -> 65.0 us, 72.8 us at half).
+    const int64_t cus = device_cus();
+    const int64_t target = (dtype == OSATTN_F32 || causal) ? cus : cus / 2;
     const int64_t base_k = (int64_t)H * pl.seqs * pl.k_tiles;
     const int64_t base_q = (int64_t)H * pl.seqs * pl.q_tiles;
     pl.k_splits = varlen ? 1 : clampi((target + base_k - 1) / base_k, 1, clampi(n_q / 256, 1, 16));
@@ -481,7 +489,7 @@ size_t osattn_bwd_workspace_bytes(int dtype, int H, int64_t n_q, int64_t n_k, in
                                   const int32_t *cu_seqlens, int num_seqs, int max_seqlen) {
     if (check_common(dtype, H, n_q, n_k, d, 1.f, causal, cu_seqlens, num_seqs, max_seqlen)) return 0;
     if (check_bwd_supported(dtype, d)) return 0;
-    return plan_backward(dtype, H, n_q, n_k, d, cu_seqlens, num_seqs, max_seqlen).total;
+    return plan_backward(dtype, H, n_q, n_k, d, causal, cu_seqlens, num_seqs, max_seqlen).total;
 }
 
 int osattn_bwd(int dtype, int o_dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
@@ -505,7 +513,7 @@ int osattn_bwd(int dtype, int o_dtype, int H, int64_t n_q, int64_t n_k, int d, c
     if ((st = check_tensor("dk", dk, kv_stride_h, kv_stride_n, es))) return st;
     if ((st = check_tensor("dv", dv, kv_stride_h, kv_stride_n, es))) return st;
     if (!m || !l) return fail(OSATTN_ERR_INVALID_ARG, "m and l must not be NULL");
-    const BwdPlan pl = plan_backward(dtype, H, n_q, n_k, d, cu_seqlens, num_seqs, max_seqlen);
+    const BwdPlan pl = plan_backward(dtype, H, n_q, n_k, d, causal, cu_seqlens, num_seqs, max_seqlen);
     if (!workspace) return fail(OSATTN_ERR_WORKSPACE, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace) & 255u)
         return fail(OSATTN_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
