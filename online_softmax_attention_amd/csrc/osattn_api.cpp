@@ -206,22 +206,25 @@ FwdPlan plan_forward(int dtype, int H, int64_t n_q, int64_t n_k, int d, int caus
         }
     }
     if (pl.splits > 1) pl.total = round256((size_t)pl.splits * H * n_q * (d + 4) * sizeof(float));
-    // Small dense / causal problems whose 128-row tiles (pairs, causal) would
-    // not occupy half the device use 64- or 32-row tiles: the workgroup's 8
+    // Dense / causal problems whose 128-row tiles (pairs, causal) would not
+    // give every CU a workgroup use 64- or 32-row tiles: the workgroup's 8
     // waves then split each key block 4 or 8 ways instead of 2, so more
-    // workgroups each scan the keys with more waves per row.
+    // workgroups each scan the keys with more waves per row.  Measured on
+    // MI355X against stopping at half the CUs: causal N=2048 H=16 D=128
+    // 42.3 -> 34.6 us, causal N=4096 H=8 D=64 47.8 -> 33.3 us; dense shapes at
+    // that boundary ran the same either way.
     // Causal tiles are paired (T-1-i, i) so that every workgroup does equal
     // work, unless the 128-row tiles alone cannot fill the device: then each
     // workgroup takes one tile, heaviest first, to keep the serial chain short.
     pl.tile_rows = 128;
     pl.pair = causal && (int64_t)H * ((n_q + 127) / 128) >= device_cus();
     if (dtype != OSATTN_F32 && !cu && pl.splits == 1) {
-        const int64_t half = device_cus() / 2;
+        const int64_t cus = device_cus();
         const auto items = [&](int64_t tr) {
             const int64_t t = (n_q + tr - 1) / tr;
             return (int64_t)H * (pl.pair ? (t + 1) / 2 : t);
         };
-        while (pl.tile_rows > (d == 64 ? 32 : 64) && items(pl.tile_rows) < half) pl.tile_rows /= 2;
+        while (pl.tile_rows > (d == 64 ? 32 : 64) && items(pl.tile_rows) < cus) pl.tile_rows /= 2;
     }
     // Four-wave workgroups (64 KiB of LDS, two per CU, blocks of half as many
     // keys) for varlen and for dense grids of 128-row tiles that fill two

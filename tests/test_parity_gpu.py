@@ -555,14 +555,16 @@ def test_varlen_64_sequences_ranked_in_kernel(osattn, oracle):
 
 # ------------------------------------------------------------ tile sizes
 # The 16-bit dense / causal forward uses 128-row tiles unless those (causal:
-# tile pairs, when paired) number fewer than half the compute units (128 on
+# tile pairs, when paired) number fewer than the compute units (256 on
 # MI355X); it then halves the tile to 64 and, for D = 64, to 32 rows.  Causal
 # tiles are paired only when H * ceil(n / 128) fills the device.  These shapes
-# select each variant on a 256-CU device.
+# select each variant on a 256-CU device (rows at D = 64; D = 128 stops at 64).
 TILE_CASES = [  # (causal, H, n_q, n_k, tile rows selected at D = 64)
-    (False, 16, 1100, 333, 128), (False, 8, 1100, 333, 64), (False, 2, 700, 1500, 32),
-    (True, 32, 1000, 1000, 128),  # paired
-    (True, 16, 1000, 1000, 128), (True, 8, 1000, 1000, 64), (True, 2, 777, 777, 32),
+    (False, 32, 1100, 333, 128), (False, 16, 1100, 333, 64), (False, 8, 1100, 333, 32),
+    (False, 2, 700, 1500, 32),
+    (True, 64, 1000, 1000, 128),  # paired
+    (True, 32, 1000, 1000, 64),   # paired
+    (True, 16, 1000, 1000, 64), (True, 8, 1000, 1000, 32), (True, 2, 777, 777, 32),
 ]
 
 
@@ -656,7 +658,7 @@ def test_csr_softmax_causal_relation_matches_attention(osattn, oracle):
 # varlen ranking and the pruned forward.
 O16_CASES = [
     ("f16", 64, False, 300, 300, 2, None),   # 32-row tiles: eight key groups share the merge
-    ("f16", 64, True, 1000, 1000, 8, None),  # 64-row tiles: four key groups share the merge
+    ("f16", 64, True, 1000, 1000, 16, None),  # 64-row tiles: four key groups share the merge
     ("bf16", 128, True, 700, 700, 2, None),
     ("f16", 64, False, 4096 - 37, 4000, 16, None),
     ("bf16", 128, False, 129, 4097, 1, None),
