@@ -713,3 +713,72 @@ def test_bwd_from_o16(osattn, oracle, dtype, D, causal, lengths):
                                         causal=causal, cu_seqlens=inp.cu_seqlens)
     for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
         assert_grad_close(host(g), r, dtype, "%s from 16-bit O %s D=%d" % (name, dtype, D))
+
+
+# ------------------------------------------------- seeded random shapes
+# Each case draws its dtype, width, relation, head count, lengths (with empty
+# and one-token sequences, and more than 64 of them so both varlen item paths
+# run), scale (at most D^-1/2: the bounds are stated for unit-normal inputs at
+# that scale), layout, output dtype and whether the forward may split, then
+# checks the forward and, where supported, the backward against the oracle.
+RANDOM_SIZES = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 513, 777, 1025]
+
+
+def random_case(idx):
+    import random
+    r = random.Random(90210 + idx)
+    dtype, D = r.choice(["f32", "f16", "bf16"]), r.choice([64, 128])
+    mode = r.choice(["dense", "causal", "varlen", "varlen_causal"])
+    H, lengths = r.randint(1, 4), None
+    size = lambda: r.choice(RANDOM_SIZES) if r.random() < 0.6 else r.randint(1, 1100)
+    if mode.startswith("varlen"):
+        ns = r.choice([1, 3, 9, 40, 64, 65, 80])
+        lengths = [0 if u < 0.1 else 1 if u < 0.2 else r.randint(2, 250 if ns > 20 else 800)
+                   for u in (r.random() for _ in range(ns))]
+        lengths[-1] = max(lengths[-1], 5)
+        n_q = n_k = sum(lengths)
+    elif mode == "causal":
+        n_q = n_k = size()
+    else:
+        n_q, n_k = size(), size()
+    fac = r.choice([1.0, 1.0, 0.5, r.uniform(0.1, 1.0)])
+    return dict(dtype=dtype, D=D, causal=mode in ("causal", "varlen_causal"), H=H, n_q=n_q, n_k=n_k,
+                lengths=lengths, scale=D ** -0.5 * fac, layout=r.choice(["hnd", "hnd", "nhd"]),
+                o16=dtype != "f32" and r.random() < 0.3, unsplit=r.random() < 0.25,
+                bwd=(dtype != "f32" or D == 64) and r.random() < 0.6)
+
+
+@pytest.mark.parametrize("idx", range(40))
+def test_random_shapes_match_oracle(osattn, oracle, idx):
+    c = random_case(idx)
+    print("random case", idx, c, flush=True)
+    dtype, layout = c["dtype"], c["layout"]
+    w = W.Workload("rnd", c["H"], c["n_q"], c["n_k"], c["D"], dtype, c["causal"], 60000 + idx,
+                   backward=c["bwd"], lengths=c["lengths"], scale=c["scale"])
+    inp = W.make_inputs(w)
+    q, k, v = (to_dev(x, dtype) for x in (inp.q, inp.k, inp.v))
+    flip = (lambda t: t.permute(1, 0, 2).contiguous()) if layout == "nhd" else (lambda t: t)
+    back = (lambda a: a.transpose(1, 0, 2)) if layout == "nhd" else (lambda a: a)
+    q, k, v = flip(q), flip(k), flip(v)
+    cu = cu_dev(inp.cu_seqlens)
+    kw = dict(scale=c["scale"], causal=c["causal"], cu_seqlens=cu, layout=layout)
+    if c["unsplit"]:
+        kw["workspace"] = torch.empty(0, dtype=torch.uint8, device="cuda")
+    o, m, l = osattn.fwd(q, k, v, **kw)
+    if c["o16"]:
+        o2, m2, l2 = osattn.fwd(q, k, v, out_dtype=q.dtype, **kw)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attn_fwd(inp.q32, inp.k32, inp.v32, c["scale"], causal=c["causal"],
+                                 cu_seqlens=inp.cu_seqlens)
+    assert_fwd_close(back(host(o)), host(m), host(l), ro, rm, rl, dtype, "random case %d" % idx)
+    if c["o16"]:
+        assert torch.equal(o2, o.to(q.dtype)) and torch.equal(m2, m) and torch.equal(l2, l)
+    if c["bwd"]:
+        do = flip(to_dev(inp.do, dtype))
+        dq, dk, dv = osattn.bwd(q, k, v, o, do, m, l, scale=c["scale"], causal=c["causal"],
+                                cu_seqlens=cu, layout=layout)
+        torch.cuda.synchronize()
+        rdq, rdk, rdv, *_ = oracle.attn_bwd(inp.q32, inp.k32, inp.v32, inp.do32, c["scale"],
+                                            causal=c["causal"], cu_seqlens=inp.cu_seqlens)
+        for name, g, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+            assert_grad_close(back(host(g)), ref, dtype, "random case %d %s" % (idx, name))
