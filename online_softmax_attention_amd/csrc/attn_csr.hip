@@ -8,8 +8,11 @@
 // CSR case the varlen-by-graph-composition section names for compiled
 // streaming.  No MFMA: the work is a gather, bound by memory.
 //
-// One wave per (row, head), head fastest so the waves of one row share its
-// column indices in L2.  Pass 1: the row maximum over the segment's scores
+// One wave per (row, head).  Workgroups go to the 8 XCDs round-robin; when H
+// divides 8 or 8 divides H each XCD takes the rows of one head at a time, so
+// its L2 holds that head's value rows (random gathers over a quarter of the
+// values instead of all of them at H = 4); otherwise the head index varies
+// fastest and the waves of a row share its column indices in L2.  Pass 1: the row maximum over the segment's scores
 // (64 edges per load).  Pass 2: the 64 lanes form 8 edge slots x 8 feature
 // parts; a slot gathers four source rows per step with 16-byte loads (a 128-
 // or 256-byte row split over its 8 lanes), all issued before the first is
@@ -31,10 +34,28 @@ __global__ void __launch_bounds__(64 * kCsrWaves) csr_softmax_kernel(CsrParams p
     constexpr int NCH = CH / 8;        // chunks per lane
     constexpr int EPC = 16 / esz;      // elements per chunk
     static_assert(NCH * 8 == CH, "a value row must split over 8 lanes");
-    const int lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * kCsrWaves + (threadIdx.x >> 6);
-    if (r >= (int64_t)p.H * p.n_dst) return;
-    const int h = (int)(r % p.H), i = (int)(r / p.H);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int h, i;
+    if (p.heads_by_xcd) {
+        const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+        int rb;
+        if (p.H <= 8) {  // 8 / H XCDs per head, row blocks dealt among them
+            const int per = 8 / p.H;
+            h = xcd % p.H;
+            rb = j * per + xcd / p.H;
+        } else {  // H / 8 heads per XCD, one after the other
+            h = xcd + 8 * (j / p.row_blocks);
+            rb = j % p.row_blocks;
+        }
+        if (rb >= p.row_blocks) return;
+        i = rb * kCsrWaves + wave;
+        if (i >= p.n_dst) return;
+    } else {
+        const int64_t r = (int64_t)blockIdx.x * kCsrWaves + wave;
+        if (r >= (int64_t)p.H * p.n_dst) return;
+        h = (int)(r % p.H);
+        i = (int)(r / p.H);
+    }
     const int nnz = p.nnz;
     int lo = p.row_ptr[i], hi = p.row_ptr[i + 1];
     lo = lo < 0 ? 0 : (lo > nnz ? nnz : lo);
@@ -126,9 +147,16 @@ __global__ void __launch_bounds__(64 * kCsrWaves) csr_softmax_kernel(CsrParams p
     }
 }
 
-hipError_t launch_csr_softmax(int dtype, int d, const CsrParams &p, hipStream_t st) {
+hipError_t launch_csr_softmax(int dtype, int d, CsrParams p, hipStream_t st) {
     const int64_t waves = (int64_t)p.H * p.n_dst;
-    const int64_t grid = (waves + kCsrWaves - 1) / kCsrWaves;
+    int64_t grid = (waves + kCsrWaves - 1) / kCsrWaves;
+    const int64_t nb = ((int64_t)p.n_dst + kCsrWaves - 1) / kCsrWaves;
+    p.row_blocks = (int)nb;
+    p.heads_by_xcd = (8 % p.H == 0 || p.H % 8 == 0) ? 1 : 0;
+    if (p.heads_by_xcd) {
+        const int64_t per = p.H <= 8 ? 8 / p.H : 1;
+        grid = p.H <= 8 ? 8 * ((nb + per - 1) / per) : (int64_t)p.H * nb;
+    }
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const dim3 g((unsigned)grid), b(64 * kCsrWaves);

@@ -99,6 +99,8 @@ struct CsrParams {
     int64_t o_sh, o_sn;
     float *m, *l;                      // (H, n_dst)
     int H, n_dst, n_src, nnz;
+    int heads_by_xcd;  // 1: workgroup -> (head, rows) mapped per XCD (H divides 8, or 8 divides H)
+    int row_blocks;    // workgroups of kCsrWaves rows per head
 };
 
 struct ReduceParams {

@@ -18,7 +18,7 @@ hipError_t launch_backward16(int dtype, int d, int mask, BwdParams p, int seqs, 
                              hipStream_t st);
 hipError_t launch_forward_pruned(int dtype, int d, FwdParams p, hipStream_t st);
 int fwd16_block_keys(int d, int waves);
-hipError_t launch_csr_softmax(int dtype, int d, const CsrParams &p, hipStream_t st);
+hipError_t launch_csr_softmax(int dtype, int d, CsrParams p, hipStream_t st);
 }  // namespace osattn
 
 using namespace osattn;

@@ -632,6 +632,23 @@ def test_csr_softmax_parity(osattn, oracle, dtype, D):
                      rl[:, ~empty], dtype, "csr %s D=%d" % (dtype, D))
 
 
+# Head counts for each workgroup mapping: H dividing 8 (heads dealt to XCDs),
+# H a multiple of 8 (XCDs take heads in turn), and the head-fastest fallback.
+@pytest.mark.parametrize("H", [1, 3, 4, 8, 16])
+def test_csr_softmax_head_mappings(osattn, oracle, H):
+    row_ptr, col_idx = W.csr_graph(90 + H, 301, 400, 12, 90, empty_frac=0.05)
+    scores, v, vw = W.csr_inputs(91 + H, H, 400, len(col_idx), 64, "f16")
+    o, m, l = osattn.csr_softmax(torch.tensor(row_ptr, device="cuda"), torch.tensor(col_idx, device="cuda"),
+                                 torch.tensor(scores, device="cuda"), to_dev(v, "f16"))
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.csr_softmax(row_ptr, col_idx, scores, vw)
+    full = np.diff(row_ptr) > 0
+    o, m, l = host(o), host(m), host(l)
+    assert np.all(o[:, ~full] == 0) and np.all(l[:, ~full] == 0)
+    assert_fwd_close(o[:, full], m[:, full], l[:, full], ro[:, full], rm[:, full], rl[:, full], "f16",
+                     "csr H=%d" % H)
+
+
 def test_csr_softmax_causal_relation_matches_attention(osattn, oracle):
     # The causal relation as CSR with q.k scores gives causal attention.
     n, H, D = 200, 2, 64
