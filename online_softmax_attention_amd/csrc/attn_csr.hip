@@ -12,9 +12,9 @@
 // divides 8 or 8 divides H each XCD takes the rows of one head at a time, so
 // its L2 holds that head's value rows (random gathers over a quarter of the
 // values instead of all of them at H = 4); otherwise the head index varies
-// fastest and the waves of a row share its column indices in L2.  Pass 1: the row maximum over the segment's scores
-// (64 edges per load).  Pass 2: the 64 lanes form 8 edge slots x 8 feature
-// parts; a slot gathers four source rows per step with 16-byte loads (a 128-
+// fastest.  Pass 1: the row maximum over the segment's scores (64 edges per
+// load).  Pass 2: the 64 lanes form 8 edge slots x 8 feature parts; a slot
+// gathers kCsrUnroll source rows per step with 16-byte loads (a 128-
 // or 256-byte row split over its 8 lanes), all issued before the first is
 // used, weights them by exp(s - m) and accumulates in f32 in edge order; the
 // slots then reduce across lanes.  The row pointer and
@@ -24,8 +24,11 @@
 
 namespace osattn {
 
-constexpr int kCsrWaves = 4;
-constexpr int kCsrUnroll = 4;  // edges per slot per step (row loads in flight per lane)
+// One-wave workgroups, five edges per slot per step: measured on the 65536-row
+// graph (H=4, D=64 fp16) against four-wave workgroups with four edges per
+// step, 184 -> 170 us (two waves 180 us; eight edges per step spill, 445 us).
+constexpr int kCsrWaves = 1;
+constexpr int kCsrUnroll = 5;  // edges per slot per step (row loads in flight per lane)
 
 template <typename T, int D>
 __global__ void __launch_bounds__(64 * kCsrWaves) csr_softmax_kernel(CsrParams p) {
