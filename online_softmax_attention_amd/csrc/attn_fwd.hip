@@ -715,15 +715,18 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
 // reference m_s) with the rule the recurrence uses between blocks -- a running
 // reference M, rescale by 2^((M_old - M) c) when it grows, add U_s 2^((m_s - M) c)
 // -- then O = U / l, m = the largest exact row maximum, l re-expressed against
-// it.  A workgroup of 256 threads covers 32 rows, 8 threads per row.
-constexpr int kCombineRows = 32;
+// it.  A workgroup of 256 threads covers kCombineRows rows, kCombineTPR threads
+// per row.
+constexpr int kCombineTPR = 8;                   // threads per row
+constexpr int kCombineRows = 256 / kCombineTPR;  // rows per workgroup
 
 // OT: the type of O (f32, or the 16-bit input type).
 template <int D, typename OT>
 __global__ void __launch_bounds__(256) fwd_combine_kernel(FwdParams p) {
-    constexpr int QD = D / 8;  // features per thread
+    constexpr int QD = D / kCombineTPR;  // features per thread
+    static_assert(QD % 4 == 0, "whole float4 per thread");
     const int h = blockIdx.x % p.H, grp = blockIdx.x / p.H;
-    const int row = grp * kCombineRows + (threadIdx.x >> 3), part = threadIdx.x & 7;
+    const int row = grp * kCombineRows + threadIdx.x / kCombineTPR, part = threadIdx.x % kCombineTPR;
     if (row >= p.n_q) return;
     const float c = p.scale_log2;
     const int64_t split_stride = (int64_t)p.H * p.n_q * (D + 4);
