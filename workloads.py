@@ -171,13 +171,18 @@ WORKLOADS = {
 # The order the workloads are listed in (index 0 is the small correctness case).
 ORDER = list(WORKLOADS)
 
-# Extra measurement shape (not one of the five above): the dense relation at the
+# Extra measurement shapes (not among the five above): the dense relation at the
 # causal workload's size, where tile pruning (a dense-only approximation) has
-# enough tiles per query block to act.
+# enough tiles per query block to act, and a decode-like split-KV shape.
 EXTRA = {
     "dense_n4096_h16_d128_bf16": Workload(
         "dense_n4096_h16_d128_bf16", 16, 4096, 4096, 128, "bf16", False, 7,
         description="dense forward, N=4096, H=16, D=128, bf16 (tile-pruning measurement)"),
+    # Few queries against long keys (decode-like): the forward splits the key
+    # range over workgroups and merges the partial states in a second launch.
+    "decode_q128_k16384_h8_d128_bf16": Workload(
+        "decode_q128_k16384_h8_d128_bf16", 8, 128, 16384, 128, "bf16", False, 11,
+        description="dense forward, 128 queries x 16384 keys, H=8, D=128, bf16 (split-KV measurement)"),
 }
 WORKLOADS.update(EXTRA)
 
