@@ -5,8 +5,10 @@
 
 A step is one pass of the attention hot path over one batch of seeded
 synthetic input already resident in HBM: the forward (one fused kernel, plus
-the combine kernel when the key range is split), or forward + backward for the
-workload that includes the backward.  After W untimed steps, K steps are timed
+the combine kernel when the key range is split) and the fused backward (its
+pre-pass, the dK/dV and dQ kernel, and a split reduction where one is used);
+--fwd-only times the forward alone.  The default workload is causal N=4096
+H=16 D=128 bf16, the largest of the named workloads.  After W untimed steps, K steps are timed
 between two device synchronisations, replayed from captured HIP graphs of 20
 steps so host launch overhead does not gate the GPU; value is the algorithmic
 TFLOP/s of the whole step (forward 4 N_q N_k D H, halved for causal, summed per
@@ -20,10 +22,14 @@ sequence for varlen; backward 2.5x the forward).  Rank 0 prints ONE JSON line
                  traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE /
                  WRITE_SIZE counters recorded in profiles/traffic.json, or null
                  when the kernel sources changed since they were recorded;
+  backward     : the same record for the backward's kernels;
   cpu_baseline : the f64 CPU oracle timed on this host's cores on a bounded
-                 row sample of the same workload (a reported baseline only);
+                 row sample of the same workload (a reported baseline only),
+                 with the CPU model and the OpenMP thread setting;
   parity       : max error of sampled output rows against that oracle, taken
-                 eagerly before timing and again after the last replayed step.
+                 eagerly before timing and again after the last replayed step,
+                 and of every gradient of one head (one per sequence, varlen).
+                 A parity failure prints the line with value null and exits 1.
 Only one GPU is used; --gpus above 1 exits with a message.
 """
 import argparse
@@ -42,7 +48,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd/bwd TFLOP/s and % of MFMA peak on 1×MI355X"
-DEFAULT_WORKLOAD = "dense_n1024_h4_d64_f16"
+DEFAULT_WORKLOAD = "causal_n4096_h16_d128_bf16"
 # MI355X dense MFMA peaks (TFLOP/s) by MFMA input type.
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
 TOL = {"f32": 1e-4, "f16": 2e-3, "bf16": 1e-2}
@@ -126,6 +132,17 @@ def admitted_count(w, i, cu):
     return (i + 1) if w.causal else w.n_k
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, inp, oracle, np, budget_s=10.0):
     """Time the oracle forward on row chunks of the workload until ~budget_s."""
     rng = np.random.default_rng(12345)
@@ -151,7 +168,8 @@ def cpu_baseline(w, inp, oracle, np, budget_s=10.0):
             passes += 1
         chunk = min(chunk * 2, 16384)
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS", "unset"),
             "sample": "f64 two-pass oracle forward on %d random (head, query) rows of the "
                       "workload (%d full passes over its %d rows; %.1f s wall on %d threads)"
                       % (rows_done, passes, w.H * w.n_q, spent, oracle.num_threads())}
@@ -167,10 +185,12 @@ def capture(fn, n, torch, stream):
     return g
 
 
-def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True, backward=False):
+def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True, backward=True):
     w = W.WORKLOADS[name]
-    if backward and not w.backward:  # same q, k, v draws; dO drawn after them
-        w = dataclasses.replace(w, backward=True)
+    if w.dtype == "f32" and w.D != 64:
+        backward = False  # the f32 backward serves D = 64
+    if w.backward != backward:  # same q, k, v draws; dO drawn after them
+        w = dataclasses.replace(w, backward=backward)
     inp = W.make_inputs(w)
     q, k, v, do, cu = upload(inp, torch, np)
     max_seqlen = max(w.lengths) if w.lengths else None
@@ -213,10 +233,32 @@ def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True, 
         og = o.reshape(-1, D).cpu().numpy()[rows]
         return float(np.max(np.abs(og - ro)))
 
+    def grad_parity(head):
+        """Largest max|g - g_ref| / max|g_ref| over dq, dk, dv of one head."""
+        torch.cuda.synchronize()
+        got = [t[head].float().cpu().numpy() for t in (dq, dk, dv)]
+        spans = ([(0, w.n_q)] if inp.cu_seqlens is None else
+                 [(int(a), int(b)) for a, b in zip(inp.cu_seqlens[:-1], inp.cu_seqlens[1:]) if b > a])
+        ref = [np.zeros((w.n_q, D)), np.zeros((w.n_k, D)), np.zeros((w.n_k, D))]
+        for a, b in spans:
+            cut = (lambda x: np.ascontiguousarray(x[head:head + 1, a:b])) if inp.cu_seqlens is not None \
+                else (lambda x: np.ascontiguousarray(x[head:head + 1]))
+            r = oracle.attn_bwd(cut(inp.q32), cut(inp.k32), cut(inp.v32), cut(inp.do32),
+                                w.softmax_scale, causal=w.causal)
+            for i in range(3):
+                if inp.cu_seqlens is None:
+                    ref[i] = r[i][0]
+                else:
+                    ref[i][a:b] = r[i][0]
+        return max(float(np.max(np.abs(g - rf)) / max(float(np.max(np.abs(rf))), 1e-2))
+                   for g, rf in zip(got, ref))
+
     stream = torch.cuda.Stream()
+    grad_head = H - 1
     with torch.cuda.stream(stream):
         step()
         err_eager = parity()  # eager parity on sampled rows, before any timing
+        gerr_eager = grad_parity(grad_head) if bw is not None else None
         for _ in range(warmup):
             step()
     torch.cuda.synchronize()
@@ -243,11 +285,18 @@ def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True, 
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     err_graph = parity()  # outputs of the last replayed step
+    gerr_graph = grad_parity(grad_head) if bw is not None else None
     ms_per_step = wall * 1e3 / steps
     step_flops = fwd_flops(w) + (bwd_flops(w) if w.backward else 0.0)
     value = step_flops / (wall / steps) / 1e12
-    parity_rec = {"max_abs_err_o": max(err_eager, err_graph), "tol": TOL[w.dtype],
-                  "rows": int(len(rows)), "ok": bool(max(err_eager, err_graph) <= TOL[w.dtype])}
+    err_o = max(err_eager, err_graph)
+    parity_rec = {"max_abs_err_o": err_o, "tol": TOL[w.dtype], "rows": int(len(rows)),
+                  "ok": bool(err_o <= TOL[w.dtype])}
+    if bw is not None:
+        gerr = max(gerr_eager, gerr_graph)
+        parity_rec.update({"max_rel_err_grad": gerr, "grad_tol": TOL[w.dtype] ,
+                           "grad_head": grad_head,
+                           "ok": bool(parity_rec["ok"] and gerr <= TOL[w.dtype])})
 
     # Roofline of the forward kernel: FLOPs per launch over its average device
     # duration, from HIP events around replays of a graph of back-to-back
@@ -291,6 +340,8 @@ def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True, 
                    "peak": peak, "unit": "TFLOP/s", "frac": bwd_ach / peak,
                    "flops_per_launch": bwd_flops(w), "kernel": bkern,
                    "traffic": recorded_traffic(name + "+bwd", bkern)}
+    if not parity_rec["ok"]:
+        value = None  # a step that computes the wrong result has no throughput
     out = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
            "warmup": warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
@@ -301,7 +352,7 @@ def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True, 
                       "pass": "fwd+bwd" if w.backward else "fwd",
                       "layout": "(H, N, D)", "output": "O f32, m and l f32",
                       "launch": "graphs of %d steps replayed" % G},
-           "pct_of_peak": 100.0 * value / peak,
+           "pct_of_peak": None if value is None else 100.0 * value / peak,
            "event_ms_per_step": e0.elapsed_time(e1) / steps,
            "roofline": roofline, "parity": parity_rec}
     if bwd_rec is not None:
@@ -457,7 +508,9 @@ def main():
     ap.add_argument("--csr", action="store_true",
                     help="time the CSR segment softmax on the synthetic CSR workload")
     ap.add_argument("--backward", action="store_true",
-                    help="time forward + backward for the workload (its step becomes both passes)")
+                    help="time forward + backward (the default; kept for old command lines)")
+    ap.add_argument("--fwd-only", action="store_true",
+                    help="time the forward alone (the step is one forward pass)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run 10 plain device copies of BYTES bytes (calibrates the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters against a known size)")
@@ -495,10 +548,15 @@ def main():
         print(json.dumps(res), flush=True)
         return
     names = W.ORDER if args.all else [args.workload]
+    failed = False
     for name in names:
         res = run_workload(name, args.steps, args.warmup, torch, np, osa, W, oracle,
-                           with_cpu=not args.no_cpu, backward=args.backward)
+                           with_cpu=not args.no_cpu, backward=not args.fwd_only)
         print(json.dumps(res), flush=True)
+        failed |= not res["parity"]["ok"]
+    if failed:
+        sys.stderr.write("parity against the oracle failed: see the parity record\n")
+        sys.exit(1)
 
 
 if __name__ == "__main__":

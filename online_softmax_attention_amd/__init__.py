@@ -27,10 +27,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libosattn.so")
 
 F32, F16, BF16 = 0, 1, 2
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_HIP, ERR_WORKSPACE = range(6)
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_HIP, ERR_WORKSPACE = 0, -1, -2, -3, -4, -5
 EXPORTS = ("osattn_fwd", "osattn_fwd_workspace_bytes", "osattn_fwd_pruned", "osattn_bwd",
            "osattn_bwd_workspace_bytes", "osattn_csr_softmax", "osattn_status_string",
-           "osattn_last_error", "osattn_version")
+           "osattn_last_error_message", "osattn_version")
 
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 _lib = None
@@ -71,8 +71,8 @@ def load(path: Optional[str] = None):
     lib.osattn_bwd.restype = i32
     lib.osattn_status_string.argtypes = [i32]
     lib.osattn_status_string.restype = ctypes.c_char_p
-    lib.osattn_last_error.argtypes = []
-    lib.osattn_last_error.restype = ctypes.c_char_p
+    lib.osattn_last_error_message.argtypes = []
+    lib.osattn_last_error_message.restype = ctypes.c_char_p
     lib.osattn_version.argtypes = []
     lib.osattn_version.restype = i32
     if path is None:
@@ -85,7 +85,7 @@ def status_string(status: int) -> str:
 
 
 def last_error() -> str:
-    return load().osattn_last_error().decode()
+    return load().osattn_last_error_message().decode()
 
 
 def _check(status: int, where: str):
@@ -170,6 +170,13 @@ _fwd_ws = {}
 
 
 def _fwd_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """The cached split-KV / work-list buffer of (device, stream).  Under graph
+    capture every call gets its own buffer instead: torch captures all graphs on
+    one stream, so a cached buffer would be shared by graphs that may replay
+    concurrently, and replacing it would hand memory a graph still uses back to
+    the allocator (the graph's private pool keeps a fresh tensor alive)."""
+    if torch.cuda.is_current_stream_capturing():
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
     key = (device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _fwd_ws.get(key)
     if ws is None or ws.numel() < nbytes:

@@ -333,7 +333,7 @@ const char *osattn_status_string(int status) {
     }
 }
 
-const char *osattn_last_error(void) { return g_err; }
+const char *osattn_last_error_message(void) { return g_err; }
 
 size_t osattn_fwd_workspace_bytes(int dtype, int H, int64_t n_q, int64_t n_k, int d, int causal,
                                   const int32_t *cu_seqlens, int num_seqs, int max_seqlen) {
@@ -515,6 +515,11 @@ int osattn_bwd(int dtype, int o_dtype, int H, int64_t n_q, int64_t n_k, int d, c
     if ((st = check_tensor("dq", dq, q_stride_h, q_stride_n, es))) return st;
     if ((st = check_tensor("dk", dk, kv_stride_h, kv_stride_n, es))) return st;
     if ((st = check_tensor("dv", dv, kv_stride_h, kv_stride_n, es))) return st;
+    // The backward kernels form offsets within a block of rows in 32 bits, as
+    // the forward's do.
+    if (q_stride_n * (int64_t)es > kMaxRowBytes || kv_stride_n * (int64_t)es > kMaxRowBytes)
+        return fail(OSATTN_ERR_UNSUPPORTED, "row strides above %lld bytes are not supported",
+                    (long long)kMaxRowBytes);
     if (!m || !l) return fail(OSATTN_ERR_INVALID_ARG, "m and l must not be NULL");
     const BwdPlan pl = plan_backward(dtype, H, n_q, n_k, d, causal, cu_seqlens, num_seqs, max_seqlen);
     if (!workspace) return fail(OSATTN_ERR_WORKSPACE, "workspace is NULL");

@@ -44,9 +44,13 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(6):
+    codes = (osa.OK, osa.ERR_INVALID_ARG, osa.ERR_UNSUPPORTED, osa.ERR_ALIGNMENT, osa.ERR_HIP,
+             osa.ERR_WORKSPACE)
+    assert codes == (0, -1, -2, -3, -4, -5)  # zero is success, failures are negative
+    for s in codes:
         assert osa.status_string(s).startswith("OSATTN_")
     assert "unknown" in osa.status_string(99)
+    assert "unknown" in osa.status_string(1)
     assert lib.osattn_version() >= 100
 
 
@@ -186,6 +190,59 @@ def test_fwd_rejects_huge_row_stride(lib):
     big = (1 << 22) // 2 + 8  # f16 elements: just above 4 MiB per row
     assert fwd(lib, qs=(big * 128, big)) == osa.ERR_UNSUPPORTED
     assert fwd(lib, kvs=(big * 128, big)) == osa.ERR_UNSUPPORTED
+
+
+def test_bwd_rejects_huge_row_stride(lib):
+    # The backward kernels form in-block row offsets in 32 bits, as the
+    # forward's do: the same 4 MiB limit, checked before the workspace (NULL).
+    def call(qs, kvs, dtype=F16, d=64):
+        return lib.osattn_bwd(dtype, F32, 1, 256, 256, d, A, B, C, O, A + 0x600000, qs[0], qs[1],
+                              kvs[0], kvs[1], 256 * d, d, M, L, 0.125, 0, None, 0, 0,
+                              A + 0x700000, A + 0x800000, A + 0x900000, None, 0, None)
+    big = (1 << 22) // 2 + 8
+    assert call((big * 256, big), (256 * 64, 64)) == osa.ERR_UNSUPPORTED
+    assert call((256 * 64, 64), (big * 256, big)) == osa.ERR_UNSUPPORTED
+    assert call((256 * 64, 64), (256 * 64, 64)) == osa.ERR_WORKSPACE  # the stride check alone
+    assert "workspace" in osa.last_error()
+    f32big = (1 << 22) // 4 + 4
+    assert call((f32big * 256, f32big), (256 * 64, 64), dtype=F32) == osa.ERR_UNSUPPORTED
+
+
+_NO_DEVICE_CALL = r"""
+import ctypes, sys
+sys.path.insert(0, sys.argv[1])
+try:
+    hip = ctypes.CDLL("libamdhip64.so")
+    n = ctypes.c_int(0)
+    if hip.hipGetDeviceCount(ctypes.byref(n)) == 0 and n.value > 0:
+        print("HAS_DEVICE")  # a real device: never launch with fake pointers
+        sys.exit(0)
+except OSError:
+    pass
+import online_softmax_attention_amd as osa
+lib = osa.load()
+A = 0x7F0000000000
+st = lib.osattn_fwd(osa.F16, osa.F32, 2, 128, 128, 64, A, A + 0x100000, A + 0x200000,
+                    128 * 64, 64, 128 * 64, 64, A + 0x300000, 128 * 64, 64, A + 0x400000,
+                    A + 0x500000, 0.125, 0, None, 0, 0, None, 0, None)
+print("STATUS", st, osa.last_error())
+"""
+
+
+def test_valid_call_without_a_device_returns_hip_error():
+    """A call that passes every host check, on a host with no usable GPU,
+    returns OSATTN_ERR_HIP instead of crashing (run in a child process; skipped
+    where a device is visible, since the pointers here are fake)."""
+    import subprocess
+    import sys
+    res = subprocess.run([sys.executable, "-c", _NO_DEVICE_CALL, ROOT], stdout=subprocess.PIPE,
+                         stderr=subprocess.STDOUT, text=True, timeout=120)
+    assert res.returncode == 0, res.stdout
+    if "HAS_DEVICE" in res.stdout:
+        pytest.skip("a HIP device is visible")
+    line = [x for x in res.stdout.splitlines() if x.startswith("STATUS")][0]
+    assert int(line.split()[1]) == osa.ERR_HIP, line
+    assert "device" in line.lower()
 
 
 # Tile-pruned forward: every case fails a host check before any launch.
