@@ -267,6 +267,36 @@ int osattn_bwd(int dtype, int o_dtype, int H, int64_t n_q, int64_t n_k, int d,
                void *workspace, size_t workspace_bytes,
                void *stream);
 
+/*
+ * Backward for callers that cannot allocate: code under HIP graph capture,
+ * serving loops and harnesses that forbid hipMalloc.  Computes exactly what
+ * osattn_bwd computes, with the same kernels and bit-identical results, but
+ * takes no workspace: the library uses a static device array of
+ * OSATTN_NOALLOC_SCRATCH_BYTES (32 MiB), one per GPU, held from the library's
+ * load until the process ends.  Its address is looked up once per device, on
+ * the first call made with that device current.  The call allocates nothing.
+ *
+ * Arguments, layouts and errors as osattn_bwd (without workspace and
+ * workspace_bytes).  A problem whose osattn_bwd_workspace_bytes(...) exceeds
+ * OSATTN_NOALLOC_SCRATCH_BYTES returns OSATTN_ERR_WORKSPACE before any HIP
+ * call.  Every call on one GPU shares that GPU's array (the backward writes
+ * all of it that it reads, so nothing needs clearing between calls), hence
+ * calls that may overlap on one GPU -- on different streams, or from
+ * different threads -- race and must be ordered by the caller.
+ */
+#define OSATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int osattn_bwd_noalloc(int dtype, int o_dtype, int H, int64_t n_q, int64_t n_k, int d,
+                       const void *q, const void *k, const void *v,
+                       const void *o, const void *d_o,
+                       int64_t q_stride_h, int64_t q_stride_n,
+                       int64_t kv_stride_h, int64_t kv_stride_n,
+                       int64_t o_stride_h, int64_t o_stride_n,
+                       const float *m, const float *l,
+                       float scale, int causal,
+                       const int32_t *cu_seqlens, int num_seqs, int max_seqlen,
+                       void *dq, void *dk, void *dv,
+                       void *stream);
+
 /* Static text for a status code (never NULL). */
 const char *osattn_status_string(int status);
 

@@ -29,8 +29,10 @@ LIB_PATH = os.path.join(_HERE, "libosattn.so")
 F32, F16, BF16 = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_HIP, ERR_WORKSPACE = 0, -1, -2, -3, -4, -5
 EXPORTS = ("osattn_fwd", "osattn_fwd_workspace_bytes", "osattn_fwd_pruned", "osattn_bwd",
-           "osattn_bwd_workspace_bytes", "osattn_csr_softmax", "osattn_status_string",
-           "osattn_last_error_message", "osattn_version")
+           "osattn_bwd_workspace_bytes", "osattn_bwd_noalloc", "osattn_csr_softmax",
+           "osattn_status_string", "osattn_last_error_message", "osattn_version")
+# Scratch bytes osattn_bwd_noalloc can use (OSATTN_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 _lib = None
@@ -69,6 +71,8 @@ def load(path: Optional[str] = None):
                                i64, i64, vp, vp, f32, i32, vp, i32, i32, vp, vp, vp, vp,
                                ctypes.c_size_t, vp]
     lib.osattn_bwd.restype = i32
+    lib.osattn_bwd_noalloc.argtypes = lib.osattn_bwd.argtypes[:-3] + [vp]
+    lib.osattn_bwd_noalloc.restype = i32
     lib.osattn_status_string.argtypes = [i32]
     lib.osattn_status_string.restype = ctypes.c_char_p
     lib.osattn_last_error_message.argtypes = []
@@ -332,8 +336,13 @@ def bwd_workspace_bytes(dtype: torch.dtype, H: int, n_q: int, n_k: int, D: int,
 
 def bwd(q, k, v, o, do, m, l, scale: Optional[float] = None, causal: bool = False,
         cu_seqlens=None, max_seqlen: Optional[int] = None, layout: str = "hnd",
-        check: bool = True, workspace: Optional[torch.Tensor] = None, out=None):
-    """Attention backward on the GPU; returns (dq, dk, dv) in the input dtype."""
+        check: bool = True, workspace: Optional[torch.Tensor] = None, out=None,
+        noalloc: bool = False):
+    """Attention backward on the GPU; returns (dq, dk, dv) in the input dtype.
+
+    ``noalloc``: call osattn_bwd_noalloc, which uses the library's static
+    per-device scratch instead of a workspace (nothing is allocated for it;
+    problems needing more than NOALLOC_SCRATCH_BYTES are refused)."""
     lib = load()
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share one dtype of float32/float16/bfloat16")
@@ -364,6 +373,17 @@ def bwd(q, k, v, o, do, m, l, scale: Optional[float] = None, causal: bool = Fals
         _like(dv, k, q.dtype, "dv")
     dev = _one_gpu((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do"), (m, "m"), (l, "l"),
                    (cu, "cu_seqlens"), (dq, "dq"), (dk, "dk"), (dv, "dv"), (workspace, "workspace"))
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc takes no workspace")
+        with torch.cuda.device(dev):
+            st = lib.osattn_bwd_noalloc(
+                _DT[q.dtype], o_code, H, n_q, n_k, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                o.data_ptr(), do.data_ptr(), q_sh, q_sn, kv_sh, kv_sn, o_sh, o_sn, m.data_ptr(),
+                l.data_ptr(), scale, int(bool(causal)), None if cu is None else cu.data_ptr(),
+                num_seqs, max_seqlen, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _stream())
+        _check(st, "osattn_bwd_noalloc")
+        return dq, dk, dv
     with torch.cuda.device(dev):
         need = lib.osattn_bwd_workspace_bytes(_DT[q.dtype], H, n_q, n_k, D, int(bool(causal)),
                                               None if cu is None else cu.data_ptr(), num_seqs,

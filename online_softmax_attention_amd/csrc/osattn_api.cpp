@@ -9,6 +9,7 @@
 #include <cstdio>
 
 #include "../../include/osattn.h"
+#include "api_internal.h"
 #include "attn_params.h"
 
 namespace osattn {
@@ -317,6 +318,92 @@ int check_bwd_supported(int dtype, int d) {
 
 }  // namespace
 
+namespace osattn {
+
+int set_error(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+// Every host check of osattn_bwd that does not involve the workspace.
+int bwd_check_args(int dtype, int o_dtype, int H, int64_t n_q, int64_t n_k, int d, const void *q,
+                   const void *k, const void *v, const void *o, const void *d_o,
+                   int64_t q_stride_h, int64_t q_stride_n, int64_t kv_stride_h,
+                   int64_t kv_stride_n, int64_t o_stride_h, int64_t o_stride_n, const float *m,
+                   const float *l, float scale, int causal, const int32_t *cu_seqlens,
+                   int num_seqs, int max_seqlen, void *dq, void *dk, void *dv) {
+    int st = check_common(dtype, H, n_q, n_k, d, scale, causal, cu_seqlens, num_seqs, max_seqlen);
+    if (st) return st;
+    if ((st = check_bwd_supported(dtype, d))) return st;
+    size_t es_o = 4;
+    if ((st = check_o_dtype(dtype, o_dtype, &es_o))) return st;
+    const size_t es = elem_size(dtype);
+    if ((st = check_tensor("q", q, q_stride_h, q_stride_n, es))) return st;
+    if ((st = check_tensor("k", k, kv_stride_h, kv_stride_n, es))) return st;
+    if ((st = check_tensor("v", v, kv_stride_h, kv_stride_n, es))) return st;
+    if ((st = check_tensor("d_o", d_o, q_stride_h, q_stride_n, es))) return st;
+    if ((st = check_tensor("o", o, o_stride_h, o_stride_n, es_o))) return st;
+    if ((st = check_tensor("dq", dq, q_stride_h, q_stride_n, es))) return st;
+    if ((st = check_tensor("dk", dk, kv_stride_h, kv_stride_n, es))) return st;
+    if ((st = check_tensor("dv", dv, kv_stride_h, kv_stride_n, es))) return st;
+    // The backward kernels form offsets within a block of rows in 32 bits, as
+    // the forward's do.
+    if (q_stride_n * (int64_t)es > kMaxRowBytes || kv_stride_n * (int64_t)es > kMaxRowBytes)
+        return fail(OSATTN_ERR_UNSUPPORTED, "row strides above %lld bytes are not supported",
+                    (long long)kMaxRowBytes);
+    if (!m || !l) return fail(OSATTN_ERR_INVALID_ARG, "m and l must not be NULL");
+    return OSATTN_OK;
+}
+
+}  // namespace osattn
+
+namespace {
+
+// Launches the backward of checked arguments with the planned workspace.
+int bwd_launch(int dtype, size_t es_o, int H, int64_t n_q, int64_t n_k, int d, const void *q,
+               const void *k, const void *v, const void *o, const void *d_o, int64_t q_stride_h,
+               int64_t q_stride_n, int64_t kv_stride_h, int64_t kv_stride_n, int64_t o_stride_h,
+               int64_t o_stride_n, const float *m, const float *l, float scale, int causal,
+               const int32_t *cu_seqlens, int num_seqs, void *dq, void *dk, void *dv,
+               const BwdPlan &pl, char *ws, hipStream_t hs) {
+    BwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.d_o = d_o;
+    p.o = o; p.m = m; p.l = l;
+    p.o16 = es_o == 2;
+    p.dq = dq; p.dk = dk; p.dv = dv;
+    p.q_sh = q_stride_h; p.q_sn = q_stride_n;
+    p.kv_sh = kv_stride_h; p.kv_sn = kv_stride_n;
+    p.o_sh = o_stride_h; p.o_sn = o_stride_n;
+    p.H = H; p.n_q = (int)n_q; p.n_k = (int)n_k;
+    p.num_seqs = cu_seqlens ? num_seqs : 1;
+    p.cu = cu_seqlens;
+    p.scale = scale;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.stat_delta = reinterpret_cast<float *>(ws + pl.off_delta);
+    p.stat_mlog2 = reinterpret_cast<float *>(ws + pl.off_mlog2);
+    p.stat_linv = reinterpret_cast<float *>(ws + pl.off_linv);
+    p.dq_part = reinterpret_cast<float *>(ws + pl.off_dq);
+    p.dk_part = reinterpret_cast<float *>(ws + pl.off_dk);
+    p.dv_part = reinterpret_cast<float *>(ws + pl.off_dv);
+    p.q_tiles = pl.q_tiles; p.k_tiles = pl.k_tiles;
+    p.q_splits = pl.q_splits; p.k_splits = pl.k_splits;
+    if (pl.sched_max > 0) {
+        p.sched = reinterpret_cast<int32_t *>(ws + pl.off_sched);
+        p.sched_max = pl.sched_max;
+    }
+    const int mk = mask_kind(causal, cu_seqlens);
+    const hipError_t e = dtype == OSATTN_F32 ? launch_backward(mk, p, pl.seqs, hs)
+                                             : launch_backward16(dtype, d, mk, p, pl.seqs,
+                                                                 pl.sched_shift, hs);
+    if (e != hipSuccess) return fail(OSATTN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
 extern "C" {
 
 int osattn_version(void) { return 100; }
@@ -501,66 +588,24 @@ int osattn_bwd(int dtype, int o_dtype, int H, int64_t n_q, int64_t n_k, int d, c
                int64_t o_stride_n, const float *m, const float *l, float scale, int causal,
                const int32_t *cu_seqlens, int num_seqs, int max_seqlen, void *dq, void *dk, void *dv,
                void *workspace, size_t workspace_bytes, void *stream) {
-    int st = check_common(dtype, H, n_q, n_k, d, scale, causal, cu_seqlens, num_seqs, max_seqlen);
+    int st = osattn::bwd_check_args(dtype, o_dtype, H, n_q, n_k, d, q, k, v, o, d_o, q_stride_h,
+                                    q_stride_n, kv_stride_h, kv_stride_n, o_stride_h, o_stride_n,
+                                    m, l, scale, causal, cu_seqlens, num_seqs, max_seqlen, dq, dk,
+                                    dv);
     if (st) return st;
-    if ((st = check_bwd_supported(dtype, d))) return st;
     size_t es_o = 4;
-    if ((st = check_o_dtype(dtype, o_dtype, &es_o))) return st;
-    const size_t es = elem_size(dtype);
-    if ((st = check_tensor("q", q, q_stride_h, q_stride_n, es))) return st;
-    if ((st = check_tensor("k", k, kv_stride_h, kv_stride_n, es))) return st;
-    if ((st = check_tensor("v", v, kv_stride_h, kv_stride_n, es))) return st;
-    if ((st = check_tensor("d_o", d_o, q_stride_h, q_stride_n, es))) return st;
-    if ((st = check_tensor("o", o, o_stride_h, o_stride_n, es_o))) return st;
-    if ((st = check_tensor("dq", dq, q_stride_h, q_stride_n, es))) return st;
-    if ((st = check_tensor("dk", dk, kv_stride_h, kv_stride_n, es))) return st;
-    if ((st = check_tensor("dv", dv, kv_stride_h, kv_stride_n, es))) return st;
-    // The backward kernels form offsets within a block of rows in 32 bits, as
-    // the forward's do.
-    if (q_stride_n * (int64_t)es > kMaxRowBytes || kv_stride_n * (int64_t)es > kMaxRowBytes)
-        return fail(OSATTN_ERR_UNSUPPORTED, "row strides above %lld bytes are not supported",
-                    (long long)kMaxRowBytes);
-    if (!m || !l) return fail(OSATTN_ERR_INVALID_ARG, "m and l must not be NULL");
+    check_o_dtype(dtype, o_dtype, &es_o);
     const BwdPlan pl = plan_backward(dtype, H, n_q, n_k, d, causal, cu_seqlens, num_seqs, max_seqlen);
     if (!workspace) return fail(OSATTN_ERR_WORKSPACE, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace) & 255u)
         return fail(OSATTN_ERR_ALIGNMENT, "workspace is not 256-byte aligned");
     if (workspace_bytes < pl.total)
         return fail(OSATTN_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, pl.total);
-
-    char *ws = static_cast<char *>(workspace);
-    BwdParams p{};
-    p.q = q; p.k = k; p.v = v; p.d_o = d_o;
-    p.o = o; p.m = m; p.l = l;
-    p.o16 = es_o == 2;
-    p.dq = dq; p.dk = dk; p.dv = dv;
-    p.q_sh = q_stride_h; p.q_sn = q_stride_n;
-    p.kv_sh = kv_stride_h; p.kv_sn = kv_stride_n;
-    p.o_sh = o_stride_h; p.o_sn = o_stride_n;
-    p.H = H; p.n_q = (int)n_q; p.n_k = (int)n_k;
-    p.num_seqs = cu_seqlens ? num_seqs : 1;
-    p.cu = cu_seqlens;
-    p.scale = scale;
-    p.scale_log2 = scale * 1.4426950408889634f;
-    p.stat_delta = reinterpret_cast<float *>(ws + pl.off_delta);
-    p.stat_mlog2 = reinterpret_cast<float *>(ws + pl.off_mlog2);
-    p.stat_linv = reinterpret_cast<float *>(ws + pl.off_linv);
-    p.dq_part = reinterpret_cast<float *>(ws + pl.off_dq);
-    p.dk_part = reinterpret_cast<float *>(ws + pl.off_dk);
-    p.dv_part = reinterpret_cast<float *>(ws + pl.off_dv);
-    p.q_tiles = pl.q_tiles; p.k_tiles = pl.k_tiles;
-    p.q_splits = pl.q_splits; p.k_splits = pl.k_splits;
-    if (pl.sched_max > 0) {
-        p.sched = reinterpret_cast<int32_t *>(ws + pl.off_sched);
-        p.sched_max = pl.sched_max;
-    }
-    const hipStream_t hs = static_cast<hipStream_t>(stream);
-    const int mk = mask_kind(causal, cu_seqlens);
-    const hipError_t e = dtype == OSATTN_F32 ? launch_backward(mk, p, pl.seqs, hs)
-                                             : launch_backward16(dtype, d, mk, p, pl.seqs,
-                                                                 pl.sched_shift, hs);
-    if (e != hipSuccess) return fail(OSATTN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
-    return ok();
+    return bwd_launch(dtype, es_o, H, n_q, n_k, d, q, k, v, o, d_o, q_stride_h, q_stride_n,
+                      kv_stride_h, kv_stride_n, o_stride_h, o_stride_n, m, l, scale, causal,
+                      cu_seqlens, num_seqs, dq, dk, dv, pl, static_cast<char *>(workspace),
+                      static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
+

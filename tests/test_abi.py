@@ -208,6 +208,25 @@ def test_bwd_rejects_huge_row_stride(lib):
     assert call((f32big * 256, f32big), (256 * 64, 64), dtype=F32) == osa.ERR_UNSUPPORTED
 
 
+def test_bwd_noalloc_refuses_problems_above_its_scratch_before_any_hip_call(lib):
+    # 3 f32 rows of statistics per (head, query): H=64, n=65536 needs 48 MiB > 32 MiB
+    def call(H, n, ptrs=None, scale=0.125):
+        p = dict(q=A, k=B, v=C, o=O, do=A + 0x600000, m=M, l=L, dq=A + 0x700000,
+                 dk=A + 0x800000, dv=A + 0x900000)
+        p.update(ptrs or {})
+        return lib.osattn_bwd_noalloc(F16, F32, H, n, n, 64, p["q"], p["k"], p["v"], p["o"],
+                                      p["do"], n * 64, 64, n * 64, 64, n * 64, 64, p["m"], p["l"],
+                                      scale, 0, None, 0, 0, p["dq"], p["dk"], p["dv"], None)
+    assert lib.osattn_bwd_workspace_bytes(F16, 64, 65536, 65536, 64, 0, None, 0, 0) > osa.NOALLOC_SCRATCH_BYTES
+    assert call(64, 65536) == osa.ERR_WORKSPACE
+    assert "static" in osa.last_error()
+    # argument errors come first, as in osattn_bwd
+    assert call(64, 65536, ptrs={"q": None}) == osa.ERR_INVALID_ARG
+    assert call(64, 65536, ptrs={"dk": A + 4}) == osa.ERR_ALIGNMENT
+    assert call(64, 65536, scale=float("nan")) == osa.ERR_UNSUPPORTED
+    assert call(1, 256, ptrs={"m": None}) == osa.ERR_INVALID_ARG
+
+
 _NO_DEVICE_CALL = r"""
 import ctypes, sys
 sys.path.insert(0, sys.argv[1])
