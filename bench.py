@@ -91,6 +91,23 @@ BWD_KERNELS = {False: "bwd16_pre+bwd16_kernel+bwd16_reduce",
                True: "bwd_pre+bwd_dkdv32+bwd_dq32+reduce_parts_f32"}
 
 
+def fwd_kernel_name(w, torch, split: bool) -> str:
+    """The forward kernel the library's plan picks for workload w: D = 128
+    dense / causal 16-bit problems whose 128-row tiles (causal: tile pairs) fill
+    the device, or that split the keys, run the 64-row-wave kernel."""
+    if w.dtype == "f32":
+        return "fwd32_kernel"
+    if w.D != 128 or w.lengths:
+        return "fwd16_kernel"
+    if split:
+        return "fwd_wide_kernel"
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    t = (w.n_q + 127) // 128
+    pair = w.causal and w.H * t >= cus
+    items = w.H * ((t + 1) // 2 if pair else t)
+    return "fwd_wide_kernel" if items >= cus else "fwd16_kernel"
+
+
 def recorded_traffic(workload: str, kernel: str):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -301,7 +318,7 @@ def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True, 
     # Roofline of the forward kernel: FLOPs per launch over its average device
     # duration, from HIP events around replays of a graph of back-to-back
     # forward launches on the launch stream.
-    kern = "fwd16_kernel" if w.dtype != "f32" else "fwd32_kernel"
+    kern = fwd_kernel_name(w, torch, bool(fws_bytes) and not w.lengths)
     if fws_bytes:  # varlen work list before, or split-KV combine after, the forward
         kern = ("varlen_schedule_kernel+" + kern) if w.lengths else (kern + "+fwd_combine_kernel")
     n_per, reps = 50, 10

@@ -23,6 +23,7 @@
 // H is a multiple of 8; causal tiles are paired (T-1-i, i) for equal work, and
 // varlen tiles can follow a sorted work list (see the schedule kernel).
 #include <type_traits>
+#include <utility>
 
 #include "attn_device.h"
 
@@ -976,6 +977,562 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdPara
 // The varlen work list on its own (the fp16/bf16 backward orders its tile pairs
 // with it): the same kernel and key block as the forward of width d.
 // Key block of the 16-bit forward for width d and NW waves per workgroup.
+// ------------------------------------------------ 64-row waves at D = 128
+// The 128-row tile at D = 128 (dense and causal relations), run by 4 waves,
+// one per SIMD: wave w serves rows 64 (w % 2) .. +64 of the tile (two 32-row
+// halves qh) and key group w / 2, i.e. keys [64 kg, 64 kg + 64) of every
+// 128-key block, as two 32-key chunks.  Every K or V operand read from LDS
+// feeds the MFMAs of both row halves, so the LDS bytes per MFMA are half those
+// of a 32-row wave: with 16-byte operand reads at one per 32-cycle MFMA the LDS
+// port would otherwise be the bound (about 128 bytes per clock per CU).
+//
+// Each wave runs a software pipeline over its chunks s = 0, 1, ...: step s
+// computes the softmax of chunk s on the vector ALU while the same wave's
+// MFMAs compute the next chunk's scores S(s+1) and add the previous chunk's
+// P(s-1) V to U.  The three are independent, so the exponentials issue beside
+// the MFMAs, and every operand is read from LDS three reads (six MFMAs) ahead
+// of its use.
+//
+// K and V blocks use separate two-slot rings.  K(b) is read by the score
+// MFMAs of steps 2b-1 and 2b, V(b) by the P.V MFMAs of steps 2b+1 and 2b+2.
+// At the start of each odd step 2b-1 a wave waits for its own copies of K(b)
+// and V(b-1), meets the others at a barrier, and starts K(b+1) into K(b-1)'s
+// slot and V(b) into V(b-2)'s, one copy instruction per MFMA slot: every wave
+// last read both in step 2b-2, and both copies have two steps to land.  One barrier per block.  The copies are
+// inline assembly: the compiler, which would make any LDS read wait for every
+// LDS copy in flight, then leaves their ordering to the explicit waits and
+// barriers.
+//
+// Exponent reference.  The recurrence rescales U whenever a row maximum grows;
+// here each row's reference is the maximum of its first chunk and never moves,
+// so U is never rescaled and the loop carries no branch that writes it.  The
+// exponentials 2^((s - m_ref) c) <= 2^((m_true - m_ref) c) are exact up to
+// rounding like those of any reference at or below the true maximum, and safe
+// from overflow while (m_true - m_ref) c stays below 64: U and l stay below
+// 2^64 n max|v|.  Every chunk checks that bound; if any row of the tile exceeds
+// it (scores that grow by tens of natural-log units along the keys), the
+// workgroup recomputes the tile with the general routine, whose lazy
+// reference moves.  The two key groups of a row merge through LDS at the end.
+struct Wide128 {
+    static constexpr int D = 128, NW = 4, BC = 128, ROW = 256, KH = 64;
+    static constexpr int KT = BC * ROW;  // bytes of one K (or V) block
+    static constexpr int KS0 = 0, KS1 = KT, VS0 = 2 * KT, VS1 = 3 * KT;  // LDS slots
+    static constexpr int NDMA = KT / (64 * NW * 16);  // 16-byte copies per lane per block
+    static constexpr int STATS = 4 * KT;                // merge statistics, 4 KiB
+    static constexpr int FLAG = STATS + 4096;           // recompute flag
+    static constexpr int LDS = FLAG + 16;
+    static constexpr float kRefLog2 = 64.f;  // largest (m_true - m_ref) c kept on this path
+};
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// f(integral_constant<int, I>) for I = 0, 1, ... in order.
+template <typename F, int... I>
+__device__ __forceinline__ void for_each_index(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+// The four words of a raw buffer resource over [base, base + bytes) (the same
+// descriptor make_rsrc builds): loads at or past the end return zeros.  The
+// caller passes bytes <= 0x7ffffff0.
+__device__ __forceinline__ i32x4 rsrc_words(const void *base, int bytes) {
+    const int n = bytes < 0 ? 0 : bytes;
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    // Wave-uniform by construction; readfirstlane lets the compiler see it,
+    // so the descriptor sits in scalar registers as the instruction requires.
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane(n);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from a raw buffer into LDS bytes [lds + 16 L, +16) of
+// lane L; lds is wave-uniform.  Completion is counted by vmcnt only.
+__device__ __forceinline__ void dma16_asm(i32x4 rsrc, uint32_t lds, int voff) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(lds)
+                 : "memory");
+}
+
+// Returns false when the tile must be recomputed (see above); then nothing
+// of o, m, l (or the partial state) has been written by this call.
+// kv_lo is a multiple of 128 and, for the causal relation, the tile starts
+// at a multiple of 128 with kv_lo = 0, so only the last block can cross the
+// diagonal or the tail.
+template <typename T, int MASK, bool O16>
+__device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, int h, int q_lo,
+                                              int q_hi, int kv_lo, int kv_hi, int split) {
+    typedef Wide128 C;
+    typedef typename Half8<T>::vec vec8;
+    constexpr bool causal = MASK == kCausal;
+    constexpr int D = C::D, NDT = D / 32, NKK = D / 16, esz = (int)sizeof(T);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rg = wave & 1, kg = wave >> 1;  // 64-row group, key group
+    const int c32 = lane & 31, g = lane >> 5;
+    const float c = p.scale_log2;
+    const int nblk = (kv_hi - kv_lo + C::BC - 1) / C::BC;
+    const int wrow_lo = q_lo + 64 * rg;
+
+    const T *kh = static_cast<const T *>(p.k) + (int64_t)h * p.kv_sh;
+    const T *vh = static_cast<const T *>(p.v) + (int64_t)h * p.kv_sh;
+    const int rowb = (int)p.kv_sn * esz;  // bytes between key rows (at most 4 MiB)
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(OSATTN_LDS char *)smem;
+
+    // F1: copy i of this wave fills bytes [(NW i + wave) KiB, +1 KiB) of a
+    // block, i.e. rows 16 i + 4 wave + L / 16, 16-byte chunk L % 16 of each
+    // (stored at its swizzled place); rows at or past kv_hi arrive as zeros.
+    const int drow = 4 * wave + (lane >> 4);
+    const int k_goff = drow * rowb + ((lane & 15) ^ (drow & 15)) * 16;
+    const int v_goff = drow * rowb + ((lane & 15) ^ ((drow & 3) << 2)) * 16;
+    const int max_rows = 0x7ffffff0 / rowb;  // rows one buffer resource may span
+    const auto desc = [&](const T *base, int b) {  // block b of K or V
+        const int k0 = kv_lo + b * C::BC;
+        return rsrc_words(base + (int64_t)k0 * p.kv_sn, min(kv_hi - k0, max_rows) * rowb);
+    };
+    const auto copy_one = [&](const i32x4 &r, uint32_t slot, int goff, int i) {
+        dma16_asm(r, lds0 + slot + (C::NW * i + wave) * 1024, goff + 4 * C::NW * i * rowb);
+    };
+    const auto copy = [&](const T *base, int b, uint32_t slot, int goff) {
+        asm volatile("" : "+v"(goff));  // per-copy offsets are formed here, not hoisted
+        const i32x4 r = desc(base, b);
+#pragma unroll
+        for (int i = 0; i < C::NDMA; ++i) copy_one(r, slot, goff, i);
+    };
+
+    // F0: this lane's two query rows (one per half) as B operands (zero past
+    // the tile end).
+    copy(kh, 0, C::KS0, k_goff);
+    const T *qb = static_cast<const T *>(p.q) + (int64_t)h * p.q_sh + (int64_t)q_lo * p.q_sn;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (int64_t)(q_hi - q_lo) * p.q_sn * esz);
+    vec8 qreg[2][NKK];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+            qreg[qh][kk] = __builtin_bit_cast(
+                vec8, bload16(rq, ((64 * rg + 32 * qh + c32) * (int)p.q_sn + 16 * kk + 8 * g) * esz));
+    if (tid == 0) *reinterpret_cast<int *>(smem + C::FLAG) = 0;  // read after the merge barrier
+    wait_vmcnt<0>();  // Q and K(0)
+    if (nblk > 1) copy(kh, 1, C::KS1, k_goff);
+    copy(vh, 0, C::VS0, v_goff);
+
+    // LDS operand addresses.  K row KH kg + 32 cc + c32 of a slot, 16-byte
+    // chunk 2 kk + g, swizzled with (row & 15) = (c32 & 15): the same place for
+    // both cc.  V: rows r0 = KH kg + 32 cc + 16 hf + 4 g + (L % 16) / 4 and
+    // r0 + 8, feature chunk 4 dt + 2 ((L / 16) & 1) + (L & 3) / 2, swizzled
+    // with (r0 & 3) = (L / 4) & 3.  ka and va hold slot 0 of their ring (the
+    // driver flips the slot bit); cc, hf and the +8 rows are immediate offsets.
+    int ka[NKK], va[NDT];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) ka[kk] = (C::KH * kg + c32) * C::ROW + (((2 * kk + g) ^ (c32 & 15)) * 16);
+    {
+        const int vr = C::KH * kg + 4 * g + ((lane & 15) >> 2);
+        const int cq = lane & 3, hh = (lane >> 4) & 1;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            va[dt] = C::VS0 + vr * C::ROW + (((4 * dt + 2 * hh + (cq >> 1)) ^ (((lane >> 2) & 3) << 2)) * 16) + 8 * (cq & 1);
+    }
+    const auto kread = [&](int kk, int off) {
+        return *reinterpret_cast<const vec8 *>(smem + ka[kk] + off);
+    };
+    const auto vread = [&](int dt, int off) {
+        const i16x4 lo = lds_read_tr16(smem + va[dt] + off);
+        const i16x4 hi = lds_read_tr16(smem + va[dt] + off + 8 * C::ROW);
+        return __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+
+    f32x16 U[2][NDT];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) U[qh][dt] = zero_vec<f32x16>();
+    float m_ref[2] = {0.f, 0.f}, m_true[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
+    float mc[2] = {0.f, 0.f}, thr[2] = {0.f, 0.f};
+    bool bail = false;
+    f32x16 SA[2], SB[2];
+    vec8 PA[2][2], PB[2][2];
+
+    bare_barrier();  // every wave's part of K(0) has landed
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) SA[qh] = zero_vec<f32x16>();
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        const vec8 a = kread(kk, 0);
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) SA[qh] = Half8<T>::mma(a, qreg[qh][kk], SA[qh]);
+    }
+
+    // One pipeline step; its parity fixes the buffers and the 32-key chunk of
+    // the reads at compile time, the slots come from ka and va.  Flags: HS,
+    // S(s+1) exists; HP, P(s-1) exists; MK, chunk s may need masking (only
+    // the last block's chunks can); CK / CV, the block boundary starts
+    // K((s+3)/2) / V((s+1)/2); FIRST, step 0 sets the reference.
+    // (Sc, Pc): chunk s's scores and probabilities; Sn receives S(s+1); Pp
+    // holds P(s-1).  Even steps use (SA, PA), odd ones (SB, PB).
+    const auto step_body = [&](auto ODDc, auto HSc, auto HPc, auto MKc, auto CKc, auto CVc,
+                               auto FIRSTc, int s, f32x16 (&Sc)[2], f32x16 (&Sn)[2],
+                               vec8 (&Pc)[2][2], vec8 (&Pp)[2][2]) {
+        constexpr bool ODD = decltype(ODDc)::value, HS = decltype(HSc)::value;
+        constexpr bool HP = decltype(HPc)::value, MK = decltype(MKc)::value;
+        constexpr bool CK = decltype(CKc)::value, CV = decltype(CVc)::value;
+        constexpr bool FIRST = decltype(FIRSTc)::value;
+        // S(s+1) and P(s-1) V read chunk 0 of their block on odd steps, 1 on even.
+        constexpr int KOFF = ODD ? 0 : 8192;
+        constexpr int VOFF = ODD ? 0 : 8192;
+        // Block boundary (odd steps): K((s+1)/2) and V((s-1)/2) have landed;
+        // the copies of K((s+3)/2) and V((s+1)/2) are issued one per slot in
+        // slots 0 .. 15, beside the MFMAs.
+        i32x4 rk = {0, 0, 0, 0}, rv = {0, 0, 0, 0};
+        uint32_t ksl = 0, vsl = 0;
+        int kgo = k_goff, vgo = v_goff;
+        if constexpr (ODD) {
+            const int b = (s + 1) >> 1;
+            wait_vmcnt<0>();
+            bare_barrier();
+            if constexpr (CK) {
+                rk = desc(kh, b + 1);
+                ksl = ((b + 1) & 1) ? C::KS1 : C::KS0;
+                asm volatile("" : "+v"(kgo));  // per-copy offsets are formed here, not hoisted
+            }
+            if constexpr (CV) {
+                rv = desc(vh, b);
+                vsl = (b & 1) ? C::VS1 : C::VS0;
+                asm volatile("" : "+v"(vgo));
+            }
+        }
+        if constexpr (MK) {  // F3: chunks that cross the tail or the diagonal
+            const int kc0 = kv_lo + (s >> 1) * C::BC + C::KH * kg + 32 * (s & 1);
+#pragma unroll
+            for (int qh = 0; qh < 2; ++qh) {
+                const int r_lo = wrow_lo + 32 * qh;
+                if (kc0 + 32 > kv_hi || (causal && kc0 + 31 > r_lo)) {
+                    f32x16 Sm[1] = {Sc[qh]};
+                    mask_block<1, causal>(Sm, kc0, g, kv_hi, r_lo + c32);
+                    Sc[qh] = Sm[0];
+                }
+            }
+        }
+        // The step's MFMAs in issue order: operand read j feeds MFMAs 2j and
+        // 2j+1 (row halves 0 and 1).  The reads for S(s+1) come first (K, 16
+        // features kk per read), so that S(s+1) is complete long before the
+        // next step reads it, then those for P(s-1) V (V, 32 features dt,
+        // 16-key half hf).  Even slot 2j issues read j + FD; every slot then
+        // issues its MFMA and its share of the softmax; a scheduling fence
+        // after each slot keeps that order (it bounds the operands in flight).
+        constexpr int NRD = (HS ? 8 : 0) + (HP ? 8 : 0);  // operand reads
+        constexpr int FD = 3;                             // reads in flight ahead of use
+        // read code: 0..7 = K with kk, 8 + 4 hf + dt = V of (dt, hf)
+        constexpr auto rdc = [](int j) { return HS ? j : 8 + j; };
+        vec8 opnd[FD + 1];
+        const auto fetch = [&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            if constexpr (j < NRD) {
+                constexpr int o = rdc(j);
+                if constexpr (o < 8) opnd[j % (FD + 1)] = kread(o, KOFF);
+                else opnd[j % (FD + 1)] = vread(o & 3, VOFF + 4096 * ((o - 8) >> 2));
+            }
+        };
+        const auto mma = [&](auto ic) {
+            constexpr int i = decltype(ic)::value, j = i >> 1, qh = i & 1;
+            if constexpr (j < NRD) {
+                constexpr int o = rdc(j);
+                if constexpr (o < 8)
+                    Sn[qh] = Half8<T>::mma(opnd[j % (FD + 1)], qreg[qh][o], o == 0 ? zero_vec<f32x16>() : Sn[qh]);
+                else
+                    U[qh][o & 3] = Half8<T>::mma(opnd[j % (FD + 1)], Pp[qh][(o - 8) >> 2], U[qh][o & 3]);
+            }
+        };
+        const auto dma = [&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (ODD && CK && i < C::NDMA) copy_one(rk, ksl, kgo, i);
+            if constexpr (ODD && CV && i >= C::NDMA && i < 2 * C::NDMA) copy_one(rv, vsl, vgo, i - C::NDMA);
+        };
+        float t[2][4], ps[2][4], y[2][16];
+        f32x8 x[2][2];
+        // Softmax of chunk s in slot-sized pieces, slot i taking piece i / 2
+        // of row half i % 2: F4 (chunk maximum; on step 0 it becomes the
+        // reference), then F5 (probabilities: f32 into l, rounded to T as the
+        // P.V operand).  Each exponential is taken one piece after the
+        // multiply-add that forms its argument.
+        const auto valu = [&](auto ic) {
+            constexpr int i = decltype(ic)::value, qh = i & 1, pc = i >> 1;
+            const f32x16 &S = Sc[qh];
+            if constexpr (pc == 0) {
+                t[qh][0] = vmax(vmax(S[0], S[1]), vmax(S[2], S[3]));
+                t[qh][1] = vmax(vmax(S[4], S[5]), vmax(S[6], S[7]));
+            } else if constexpr (pc == 1) {
+                t[qh][2] = vmax(vmax(S[8], S[9]), vmax(S[10], S[11]));
+                t[qh][3] = vmax(vmax(S[12], S[13]), vmax(S[14], S[15]));
+            } else if constexpr (pc == 2) {
+                const float mx = xor32_max(vmax(vmax(t[qh][0], t[qh][1]), vmax(t[qh][2], t[qh][3])));
+                m_true[qh] = vmax(m_true[qh], mx);
+                if constexpr (FIRST) {
+                    // A row with no admitted key in this chunk (a key group
+                    // above the diagonal of the first tile) takes a finite
+                    // stand-in: its exponentials are 0 and any later admitted
+                    // key exceeds thr, which hands the tile back.
+                    m_ref[qh] = mx == kNegInf ? -1e30f : mx;
+                    mc[qh] = m_ref[qh] * c;
+                    thr[qh] = m_ref[qh] + C::kRefLog2 / c;
+                } else {
+                    bail |= mx > thr[qh];
+                }
+            } else if constexpr (pc >= 3 && pc <= 11) {
+                if constexpr (pc >= 4) {
+                    constexpr int e0 = 2 * (pc - 4);
+                    x[qh][e0 >> 3][e0 & 7] = fast_exp2(y[qh][e0]);
+                    x[qh][e0 >> 3][(e0 & 7) + 1] = fast_exp2(y[qh][e0 + 1]);
+                }
+                if constexpr (pc <= 10) {
+                    constexpr int e1 = 2 * (pc - 3);
+                    y[qh][e1] = fmaf(S[e1], c, -mc[qh]);
+                    y[qh][e1 + 1] = fmaf(S[e1 + 1], c, -mc[qh]);
+                }
+            } else if constexpr (pc == 12 || pc == 13) {
+                constexpr int hf = pc - 12;
+                const f32x8 &v = x[qh][hf];
+                ps[qh][2 * hf] = (v[0] + v[1]) + (v[2] + v[3]);
+                ps[qh][2 * hf + 1] = (v[4] + v[5]) + (v[6] + v[7]);
+                Pc[qh][hf] = __builtin_convertvector(v, vec8);
+            } else if constexpr (pc == 14) {
+                l_run[qh] += (ps[qh][0] + ps[qh][1]) + (ps[qh][2] + ps[qh][3]);
+            }
+        };
+        const auto slot = [&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr ((i & 1) == 0) fetch(std::integral_constant<int, (i >> 1) + FD>{});
+            dma(ic);
+            mma(ic);
+            valu(ic);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        for_each_index(fetch, std::make_integer_sequence<int, FD>{});
+        for_each_index(slot, std::make_integer_sequence<int, 32>{});
+    };
+    using Y = std::true_type;
+    using N = std::false_type;
+    using E = std::false_type;  // even step
+    using O = std::true_type;   // odd step
+    const auto step = [&](auto ODDc, auto HSc, auto HPc, auto MKc, auto CKc, auto CVc, auto FIRSTc,
+                          int s) {
+        if constexpr (!decltype(ODDc)::value)
+            step_body(ODDc, HSc, HPc, MKc, CKc, CVc, FIRSTc, s, SA, SB, PA, PB);
+        else
+            step_body(ODDc, HSc, HPc, MKc, CKc, CVc, FIRSTc, s, SB, SA, PB, PA);
+    };
+    const auto flip_k = [&]() {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) ka[kk] ^= C::KT;
+    };
+    const auto flip_v = [&]() {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) va[dt] ^= C::KT;
+    };
+    // Steps 0 .. 2 nblk - 1, then P(2 nblk - 1) V.  Block b's scores are
+    // computed by steps 2b-1 and 2b (K slot b & 1), its P.V products by steps
+    // 2b+1 and 2b+2 (V slot b & 1): ka flips before each odd step from step 1
+    // on, va after each even step from step 2 on.  Only the last block's
+    // chunks can need a mask; its steps run outside the loop, which is then
+    // free of branches.
+    if (nblk == 1) step(E{}, Y{}, N{}, Y{}, N{}, N{}, Y{}, 0);
+    else step(E{}, Y{}, N{}, N{}, N{}, N{}, Y{}, 0);
+    int b = 1;
+    if (nblk > 2) {
+#pragma unroll 1
+        do {
+            flip_k();
+            step(O{}, Y{}, Y{}, N{}, Y{}, Y{}, N{}, 2 * b - 1);
+            step(E{}, Y{}, Y{}, N{}, N{}, N{}, N{}, 2 * b);
+            flip_v();
+        } while (++b < nblk - 1);
+    }
+    if (nblk > 1) {  // the last block: b = nblk - 1
+        flip_k();
+        step(O{}, Y{}, Y{}, N{}, N{}, Y{}, N{}, 2 * b - 1);
+        step(E{}, Y{}, Y{}, Y{}, N{}, N{}, N{}, 2 * b);
+        flip_v();
+    }
+    step(O{}, N{}, Y{}, Y{}, N{}, N{}, N{}, 2 * nblk - 1);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)  // P(2 nblk - 1) V: chunk 1 of the last block
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const vec8 a = vread(dt, 8192 + 4096 * hf);
+#pragma unroll
+            for (int qh = 0; qh < 2; ++qh) U[qh][dt] = Half8<T>::mma(a, PB[qh][hf], U[qh][dt]);
+        }
+    // F7: merge the two key groups of each row through LDS, into the K
+    // slots: every wave finished its K reads before the last odd step's
+    // barrier.  Wave (rg, kg) finalizes row half qh = kg of its 64 rows; it
+    // hands its partial state of the other half (U, and per row m_ref,
+    // m_true, l) to its partner (rg, 1 - kg) and takes the partner's of its
+    // own.  A wave that saw a row exceed the reference bound raises the flag
+    // before the same barrier, and then every wave hands the tile back.
+    float l_tot[2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) l_tot[qh] = xor32_sum(l_run[qh]);  // the lane halves' keys
+    int *flag = reinterpret_cast<int *>(smem + C::FLAG);
+    if (__any(bail) && lane == 0) *flag = 1;
+    const int give = 1 - kg;  // row half handed to the partner
+    f32x4 *ubuf = reinterpret_cast<f32x4 *>(smem + C::KS0) + (rg * 2) * 16 * 64 + lane;
+    f32x4 *sbuf = reinterpret_cast<f32x4 *>(smem + C::STATS) + (rg * 2) * 64 + lane;
+    const auto give_half = [&](auto qhc) {
+        constexpr int qh = decltype(qhc)::value;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 val = {U[qh][dt][4 * j], U[qh][dt][4 * j + 1], U[qh][dt][4 * j + 2],
+                                   U[qh][dt][4 * j + 3]};
+                ubuf[(qh * 16 + dt * 4 + j) * 64] = val;
+            }
+        const f32x4 st = {m_ref[qh], m_true[qh], l_tot[qh], 0.f};
+        sbuf[qh * 64] = st;
+    };
+    if (give == 0) give_half(std::integral_constant<int, 0>{});
+    else give_half(std::integral_constant<int, 1>{});
+    wait_lgkmcnt0();
+    bare_barrier();
+    if (*flag) {
+        bare_barrier();  // every wave has read the flag before the LDS is reused
+        return false;
+    }
+    const auto finish_half = [&](auto qhc) {
+        constexpr int qh = decltype(qhc)::value;
+        const f32x4 st = sbuf[qh * 64];
+        const float M = vmax(m_ref[qh], st[0]);
+        const float a0 = fast_exp2((m_ref[qh] - M) * c), a1 = fast_exp2((st[0] - M) * c);
+        const float lt = l_tot[qh] * a0 + st[2] * a1;
+        const float mt = vmax(m_true[qh], st[1]);
+        const int qrow = wrow_lo + 32 * qh + c32;
+        if (split >= 0) {
+            if (qrow >= q_hi) return;
+            float *prow = p.part + (((int64_t)split * p.H + h) * p.n_q + qrow) * (D + 4);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 u1 = ubuf[(qh * 16 + dt * 4 + j) * 64];
+                    f32x4 val;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) val[e] = U[qh][dt][4 * j + e] * a0 + u1[e] * a1;
+                    *reinterpret_cast<f32x4 *>(prow + 32 * dt + 8 * j + 4 * g) = val;
+                }
+            if (g == 0) {
+                const f32x4 stv = {M, mt, lt, 0.f};
+                *reinterpret_cast<f32x4 *>(prow + D) = stv;
+            }
+        } else {
+            // O rows go through this wave's own 16 KiB of the merge buffer
+            // (already read above) so that each store covers whole rows: row
+            // c32 of the half, 16-byte chunk 8 dt + 2 j + g, swizzled with
+            // the row's low four bits (16 lanes that write one chunk of 16
+            // rows, or read 16 chunks of one row, hit 16 distinct bank groups).
+            const float b0 = a0 / lt, b1 = a1 / lt;
+            f32x4 val[NDT][4];
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 u1 = ubuf[(qh * 16 + dt * 4 + j) * 64];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) val[dt][j][e] = U[qh][dt][4 * j + e] * b0 + u1[e] * b1;
+                }
+            if (g == 0 && qrow < q_hi) {
+                p.m[(int64_t)h * p.n_q + qrow] = mt * p.scale;
+                p.l[(int64_t)h * p.n_q + qrow] = lt * fast_exp2((M - mt) * c);
+            }
+            wait_lgkmcnt0();  // every read of the region has returned
+            f32x4 *obuf = reinterpret_cast<f32x4 *>(smem + C::KS0) + (rg * 2 + qh) * 16 * 64;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) obuf[c32 * 32 + ((8 * dt + 2 * j + g) ^ (c32 & 15))] = val[dt][j];
+            wait_lgkmcnt0();
+            const int row0 = wrow_lo + 32 * qh;
+            if constexpr (O16) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {  // 4 rows of 16 chunks of 8 values
+                    const int r = 4 * i + (lane >> 4), c8 = lane & 15;
+                    const f32x4 lo = obuf[r * 32 + ((2 * c8) ^ (r & 15))];
+                    const f32x4 hi = obuf[r * 32 + ((2 * c8 + 1) ^ (r & 15))];
+                    if (row0 + r < q_hi) {
+                        T *dst = static_cast<T *>(p.o) + (int64_t)h * p.o_sh + (int64_t)(row0 + r) * p.o_sn + 8 * c8;
+                        store4_16(dst, lo);
+                        store4_16(dst + 4, hi);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {  // 2 rows of 32 chunks of 4 values
+                    const int r = 2 * i + (lane >> 5), ch = lane & 31;
+                    const f32x4 v4 = obuf[r * 32 + (ch ^ (r & 15))];
+                    if (row0 + r < q_hi)
+                        *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + (int64_t)h * p.o_sh +
+                                                   (int64_t)(row0 + r) * p.o_sn + 4 * ch) = v4;
+                }
+            }
+        }
+    };
+    if (kg == 0) finish_half(std::integral_constant<int, 0>{});
+    else finish_half(std::integral_constant<int, 1>{});
+    // The next tile's copies reuse the slots: a barrier without a memory
+    // fence (the stores above need not have landed; every LDS read here has).
+    wait_lgkmcnt0();
+    bare_barrier();
+    return true;
+}
+
+// A tile the wide routine hands back is recomputed by the general 4-wave
+// routine (32-row waves, 64 KiB of the LDS).
+template <typename T, int MASK, bool O16>
+__device__ __forceinline__ void fwd_wide_or_general(const FwdParams &p, char *smem, int h, int q_lo,
+                                                    int q_hi, int kv_lo, int kv_hi, int split) {
+    static_assert(2 * Fwd16Cfg<128, 2, 4>::STAGE <= Wide128::LDS, "both routines fit the LDS");
+    if (!fwd_wide_tile<T, MASK, O16>(p, smem, h, q_lo, q_hi, kv_lo, kv_hi, split))
+        fwd16_tile<T, 128, MASK, 2, 4, false, 4, O16>(p, smem, h, q_lo, q_hi, kv_lo, kv_hi, split);
+}
+
+// The dense and causal 16-bit forward at D = 128 with 128-row tiles: one
+// workgroup of 4 waves per CU.  Work items as in fwd16_kernel: split-KV items
+// (dense), causal tile pairs (T-1-i, i) or single tiles heaviest first, dense
+// tiles.
+template <typename T, int MASK, bool O16>
+__global__ void __launch_bounds__(256, 1) fwd_wide_kernel(FwdParams p) {
+    constexpr bool causal = MASK == kCausal;
+    __shared__ __attribute__((aligned(16))) char smem[Wide128::LDS];
+    const int b = blockIdx.x;
+    if (!causal && p.splits > 1) {
+        const int items = p.H * p.n_tiles;
+        const int split = b / items, r = b % items;
+        const int h = r % p.H, tile = r / p.H;
+        const int q_lo = tile * kBR, q_hi = min(q_lo + kBR, p.n_q);
+        const int k_lo = split * p.split_len, k_hi = min(k_lo + p.split_len, p.n_k);
+        fwd_wide_or_general<T, MASK, O16>(p, smem, h, q_lo, q_hi, k_lo, k_hi, split);
+        return;
+    }
+    const int h = b % p.H, rest = b / p.H;
+    int t0, t1 = -1;
+    if (causal && p.pair) {
+        if (rest >= (p.n_tiles + 1) / 2) return;
+        t0 = p.n_tiles - 1 - rest;
+        t1 = (rest == t0) ? -1 : rest;
+    } else {
+        t0 = causal ? p.n_tiles - 1 - rest : rest;
+    }
+#pragma unroll 1
+    for (int k = 0; k < 2; ++k) {
+        const int tile = k == 0 ? t0 : t1;
+        if (tile < 0) break;
+        const int q_lo = tile * kBR, q_hi = min(q_lo + kBR, p.n_q);
+        fwd_wide_or_general<T, MASK, O16>(p, smem, h, q_lo, q_hi, 0, causal ? q_hi : p.n_k, -1);
+    }
+}
+
 int fwd16_block_keys(int d, int waves) {
     if (d == 64) return waves == 4 ? Fwd16Cfg<64, 2, 4>::BC : Fwd16Cfg<64, 2>::BC;
     return waves == 4 ? Fwd16Cfg<128, 2, 4>::BC : Fwd16Cfg<128, 2>::BC;
@@ -1237,6 +1794,12 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) fwd32_kernel(FwdPar
 template <typename T, int D, int MASK, bool O16>
 static void launch_fwd16_o(const FwdParams &p, int grid, hipStream_t st) {
     const dim3 g(grid), b(kT16);
+    if constexpr (D == 128 && (MASK == kDense || MASK == kCausal)) {
+        if (p.tile_rows == kBR) {  // 64-row waves, one workgroup per CU
+            hipLaunchKernelGGL((fwd_wide_kernel<T, MASK, O16>), g, dim3(256), 0, st, p);
+            return;
+        }
+    }
     if constexpr (MASK == kDense || MASK == kCausal) {
         if (p.tile_rows == 64) {
             hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 2, 8, O16>), g, b, 0, st, p);
