@@ -120,6 +120,14 @@ __device__ __forceinline__ Range16 split16(int lo, int hi, int split, int splits
     return {a, b > a ? b : a};
 }
 
+// x, opaque to the optimizer: an address formed from it is formed where it is
+// used, not hoisted out of the tile loop into a register held for the whole
+// kernel.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // Store a lane's transposed accumulator tiles (feature rows, one position
 // column) as one row of `out`, scaled and rounded to T (or f32 partials).
 template <typename T, int NDT>
@@ -341,8 +349,9 @@ __device__ __forceinline__ void dkdv16_tile(const BwdParams &p, char *smem, int 
                 }
             }
         if (p.k_splits == 1) {
-            store_row16<T, C::NDT>(static_cast<T *>(p.dk) + (int64_t)h * p.kv_sh + (int64_t)key * p.kv_sn, dK, g, p.scale);
-            store_row16<T, C::NDT>(static_cast<T *>(p.dv) + (int64_t)h * p.kv_sh + (int64_t)key * p.kv_sn, dV, g, 1.f);
+            const int64_t koff = (int64_t)h * p.kv_sh + (int64_t)opaque(key) * p.kv_sn;
+            store_row16<T, C::NDT>(static_cast<T *>(p.dk) + koff, dK, g, p.scale);
+            store_row16<T, C::NDT>(static_cast<T *>(p.dv) + koff, dV, g, 1.f);
         } else {
             const int64_t off = (((int64_t)split * p.H + h) * p.n_k + key) * D;
             store_row_part<C::NDT>(p.dk_part + off, dK, g, p.scale);
@@ -536,7 +545,7 @@ __device__ __forceinline__ void dq16_tile(const BwdParams &p, char *smem, int h,
                 for (int e = 0; e < 4; ++e) dQ[dt][4 * jj + e] += a[e];
             }
         if (p.q_splits == 1) {
-            store_row16<T, C::NDT>(static_cast<T *>(p.dq) + (int64_t)h * p.q_sh + (int64_t)qrow * p.q_sn, dQ, g, p.scale);
+            store_row16<T, C::NDT>(static_cast<T *>(p.dq) + (int64_t)h * p.q_sh + (int64_t)opaque(qrow) * p.q_sn, dQ, g, p.scale);
         } else {
             const int64_t off = (((int64_t)split * p.H + h) * p.n_q + qrow) * D;
             store_row_part<C::NDT>(p.dq_part + off, dQ, g, p.scale);

@@ -1008,11 +1008,14 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdPara
 // so U is never rescaled and the loop carries no branch that writes it.  The
 // exponentials 2^((s - m_ref) c) <= 2^((m_true - m_ref) c) are exact up to
 // rounding like those of any reference at or below the true maximum, and safe
-// from overflow while (m_true - m_ref) c stays below 64: U and l stay below
-// 2^64 n max|v|.  Every chunk checks that bound; if any row of the tile exceeds
-// it (scores that grow by tens of natural-log units along the keys), the
-// workgroup recomputes the tile with the general routine, whose lazy
-// reference moves.  The two key groups of a row merge through LDS at the end.
+// from overflow while (m_true - m_ref) c stays below a bound B: the P operand
+// is at most 2^B, and U and l stay below 2^B n max|v|.  B = 64 for bf16 (whose
+// exponent range is f32's) and 15 for fp16 (largest finite value 65504, just
+// under 2^16).  Every chunk checks that bound; if any row of the tile exceeds
+// it (scores that grow by 10 or more natural-log units along the keys), the
+// workgroup recomputes the tile with each row's exact maximum as its reference,
+// found first by a pass of score MFMAs alone.  The two key groups of a row
+// merge through LDS at the end.
 struct Wide128 {
     static constexpr int D = 128, NW = 4, BC = 128, ROW = 256, KH = 64;
     static constexpr int KT = BC * ROW;  // bytes of one K (or V) block
@@ -1021,7 +1024,8 @@ struct Wide128 {
     static constexpr int STATS = 4 * KT;                // merge statistics, 4 KiB
     static constexpr int FLAG = STATS + 4096;           // recompute flag
     static constexpr int LDS = FLAG + 16;
-    static constexpr float kRefLog2 = 64.f;  // largest (m_true - m_ref) c kept on this path
+    // largest (m_true - m_ref) c kept on this path, by input type
+    template <typename T> static constexpr float kRefLog2 = std::is_same<T, _Float16>::value ? 15.f : 64.f;
 };
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -1058,13 +1062,15 @@ __device__ __forceinline__ void dma16_asm(i32x4 rsrc, uint32_t lds, int voff) {
 }
 
 // Returns false when the tile must be recomputed (see above); then nothing
-// of o, m, l (or the partial state) has been written by this call.
-// kv_lo is a multiple of 128 and, for the causal relation, the tile starts
-// at a multiple of 128 with kv_lo = 0, so only the last block can cross the
-// diagonal or the tail.
+// of o, m, l (or the partial state) has been written by this call.  With
+// exact_ref the reference of each row is its exact maximum, and the call
+// always succeeds.  kv_lo is a multiple of 128 and, for the causal relation,
+// the tile starts at a multiple of 128 with kv_lo = 0, so only the last block
+// can cross the diagonal or the tail.
 template <typename T, int MASK, bool O16>
 __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, int h, int q_lo,
-                                              int q_hi, int kv_lo, int kv_hi, int split) {
+                                              int q_hi, int kv_lo, int kv_hi, int split,
+                                              bool exact_ref) {
     typedef Wide128 C;
     typedef typename Half8<T>::vec vec8;
     constexpr bool causal = MASK == kCausal;
@@ -1117,6 +1123,33 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
                 vec8, bload16(rq, ((64 * rg + 32 * qh + c32) * (int)p.q_sn + 16 * kk + 8 * g) * esz));
     if (tid == 0) *reinterpret_cast<int *>(smem + C::FLAG) = 0;  // read after the merge barrier
     wait_vmcnt<0>();  // Q and K(0)
+    float m_init[2] = {kNegInf, kNegInf};
+    if (exact_ref) {
+        // F2-F4 alone: each row's exact maximum over its admitted keys, from
+        // the same MFMA products (K read straight from memory in the A
+        // operand layout) as the pass below computes.
+        for (int k0 = kv_lo; k0 < kv_hi; k0 += 32) {
+            if (causal && k0 > wrow_lo + 63) break;
+            const __amdgpu_buffer_rsrc_t rk =
+                make_rsrc(kh + (int64_t)k0 * p.kv_sn, (int64_t)(kv_hi - k0) * rowb);
+            f32x16 S[2] = {zero_vec<f32x16>(), zero_vec<f32x16>()};
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                const vec8 a = __builtin_bit_cast(vec8, bload16(rk, c32 * rowb + (16 * kk + 8 * g) * esz));
+#pragma unroll
+                for (int qh = 0; qh < 2; ++qh) S[qh] = Half8<T>::mma(a, qreg[qh][kk], S[qh]);
+            }
+#pragma unroll
+            for (int qh = 0; qh < 2; ++qh) {
+                f32x16 Sm[1] = {S[qh]};
+                mask_block<1, causal>(Sm, k0, g, kv_hi, wrow_lo + 32 * qh + c32);
+                float mx = kNegInf;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = vmax(mx, Sm[0][r]);
+                m_init[qh] = vmax(m_init[qh], xor32_max(mx));
+            }
+        }
+    }
     if (nblk > 1) copy(kh, 1, C::KS1, k_goff);
     copy(vh, 0, C::VS0, v_goff);
 
@@ -1275,9 +1308,10 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
                     // above the diagonal of the first tile) takes a finite
                     // stand-in: its exponentials are 0 and any later admitted
                     // key exceeds thr, which hands the tile back.
-                    m_ref[qh] = mx == kNegInf ? -1e30f : mx;
+                    const float base = exact_ref ? m_init[qh] : mx;
+                    m_ref[qh] = base == kNegInf ? -1e30f : base;
                     mc[qh] = m_ref[qh] * c;
-                    thr[qh] = m_ref[qh] + C::kRefLog2 / c;
+                    thr[qh] = exact_ref ? __builtin_inff() : m_ref[qh] + C::template kRefLog2<T> / c;
                 } else {
                     bail |= mx > thr[qh];
                 }
@@ -1487,14 +1521,14 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
     return true;
 }
 
-// A tile the wide routine hands back is recomputed by the general 4-wave
-// routine (32-row waves, 64 KiB of the LDS).
+// A tile the wide routine hands back is run again with exact references (one
+// body of the routine in the kernel: the retry is the loop's second pass).
 template <typename T, int MASK, bool O16>
-__device__ __forceinline__ void fwd_wide_or_general(const FwdParams &p, char *smem, int h, int q_lo,
-                                                    int q_hi, int kv_lo, int kv_hi, int split) {
-    static_assert(2 * Fwd16Cfg<128, 2, 4>::STAGE <= Wide128::LDS, "both routines fit the LDS");
-    if (!fwd_wide_tile<T, MASK, O16>(p, smem, h, q_lo, q_hi, kv_lo, kv_hi, split))
-        fwd16_tile<T, 128, MASK, 2, 4, false, 4, O16>(p, smem, h, q_lo, q_hi, kv_lo, kv_hi, split);
+__device__ __forceinline__ void fwd_wide_or_retry(const FwdParams &p, char *smem, int h, int q_lo,
+                                                  int q_hi, int kv_lo, int kv_hi, int split) {
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass)
+        if (fwd_wide_tile<T, MASK, O16>(p, smem, h, q_lo, q_hi, kv_lo, kv_hi, split, pass == 1)) break;
 }
 
 // The dense and causal 16-bit forward at D = 128 with 128-row tiles: one
@@ -1512,7 +1546,7 @@ __global__ void __launch_bounds__(256, 1) fwd_wide_kernel(FwdParams p) {
         const int h = r % p.H, tile = r / p.H;
         const int q_lo = tile * kBR, q_hi = min(q_lo + kBR, p.n_q);
         const int k_lo = split * p.split_len, k_hi = min(k_lo + p.split_len, p.n_k);
-        fwd_wide_or_general<T, MASK, O16>(p, smem, h, q_lo, q_hi, k_lo, k_hi, split);
+        fwd_wide_or_retry<T, MASK, O16>(p, smem, h, q_lo, q_hi, k_lo, k_hi, split);
         return;
     }
     const int h = b % p.H, rest = b / p.H;
@@ -1529,7 +1563,7 @@ __global__ void __launch_bounds__(256, 1) fwd_wide_kernel(FwdParams p) {
         const int tile = k == 0 ? t0 : t1;
         if (tile < 0) break;
         const int q_lo = tile * kBR, q_hi = min(q_lo + kBR, p.n_q);
-        fwd_wide_or_general<T, MASK, O16>(p, smem, h, q_lo, q_hi, 0, causal ? q_hi : p.n_k, -1);
+        fwd_wide_or_retry<T, MASK, O16>(p, smem, h, q_lo, q_hi, 0, causal ? q_hi : p.n_k, -1);
     }
 }
 
