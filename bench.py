@@ -531,6 +531,11 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run 10 plain device copies of BYTES bytes (calibrates the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters against a known size)")
+    ap.add_argument("--read-probe", type=int, default=0, metavar="BYTES",
+                    help="only run 10 reads of BYTES bytes with 16-byte buffer loads "
+                         "(libosattn_probe.so), to calibrate FETCH_SIZE for those loads")
+    ap.add_argument("--probe-lds", action="store_true",
+                    help="with --read-probe: the loads go to LDS (buffer_load ... lds)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -554,6 +559,25 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n * 4, "copies": 10}), flush=True)
+        return
+    if args.read_probe:
+        import ctypes
+        probe = ctypes.CDLL(os.path.join(ROOT, "online_softmax_attention_amd", "libosattn_probe.so"))
+        probe.osattn_probe_read16.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                              ctypes.c_void_p, ctypes.c_void_p]
+        probe.osattn_probe_read16.restype = ctypes.c_int
+        src = torch.arange(args.read_probe // 4, dtype=torch.int32, device="cuda")
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+        for _ in range(10):
+            rc = probe.osattn_probe_read16(src.data_ptr(), args.read_probe, int(args.probe_lds),
+                                           sink.data_ptr(), stream)
+            if rc != 0:
+                sys.stderr.write("read probe failed: %d\n" % rc)
+                sys.exit(1)
+        torch.cuda.synchronize()
+        print(json.dumps({"read_probe_bytes": args.read_probe, "to_lds": bool(args.probe_lds),
+                          "reads": 10}), flush=True)
         return
     osa.load()
     if args.csr:

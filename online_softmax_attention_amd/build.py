@@ -3,8 +3,10 @@
     python -m online_softmax_attention_amd.build      # or build() from Python
 
 Every source under csrc/ is compiled by hipcc into _build/ and linked into
-online_softmax_attention_amd/libosattn.so.  Packed-FP32 VALU instructions are
-disabled for all device code (-packed-fp32-ops).
+online_softmax_attention_amd/libosattn.so.  The counter-calibration probe
+(probe/read_probe.hip) becomes libosattn_probe.so beside it; nothing in the
+library uses it.  Packed-FP32 VALU instructions are disabled for all device
+code (-packed-fp32-ops).
 """
 from __future__ import annotations
 
@@ -18,6 +20,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libosattn.so")
+PROBE_SRC = os.path.join(HERE, "probe", "read_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libosattn_probe.so")
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
@@ -55,8 +59,14 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stdout)
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [_hipcc()] + COMMON + ["-shared", "-o", tmp, PROBE_SRC]
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("probe build failed:\n" + res.stdout)
+    os.replace(tmp, PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 
