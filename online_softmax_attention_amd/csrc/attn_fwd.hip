@@ -218,262 +218,19 @@ __device__ __forceinline__ void wait_dma_blocks(int blocks) {
     else wait_vmcnt<0>();
 }
 
-// The NW waves of a workgroup form RG row groups of 32 query rows (a tile of
-// 32 RG rows) times KG = NW / RG key groups; key group kg takes keys
-// [kg KH, (kg + 1) KH) of every block, and the KG partial states of a row are
-// merged through LDS at the end.  Launches use RG = 4 (128-row tiles) unless
-// such tiles are too few to occupy the device.
-// split < 0: write O, m, l.  split >= 0: write this key range's partial state.
-// PRUNE: tile-pruned dense forward (each block is one 128 x BC tile); smem then
-// carries 8 extra floats past the stages for the tile-maximum exchange.
-// O16: O is written in T (the same f32 values rounded once) instead of f32.
-template <typename T, int D, int MASK, int NST, int RG, bool PRUNE = false, int NW = 8,
-          bool O16 = false>
-__device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h, int q_lo,
-                                           int q_hi, int kv_lo, int kv_hi, int split) {
+// F7 for every 16-bit tile: merge the KG = NW / RG key groups of each row
+// through LDS, then O = U / l (or the split's partial state), m and l.  Every
+// wave calls it after its last block; it begins and ends with a workgroup
+// barrier (the stages' LDS is reused for the merge, and then by the next tile).
+template <typename T, int D, int NST, int RG, int NW, bool O16>
+__device__ __forceinline__ void fwd16_finish(const FwdParams &p, char *smem, int h, int q_hi,
+                                             int split, int wave, int lane, int qrow,
+                                             f32x16 (&U)[D / 32], float m_ref, float m_true,
+                                             float l_run, float c) {
     typedef Fwd16Cfg<D, NST, NW> C;
-    typedef typename Half8<T>::vec vec8;
-    constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
-    constexpr int KG = NW / RG, KH = C::BC / KG, NS = KH / 32;  // keys, 32-key chunks per wave
-    static_assert(RG * KG == NW && NS * 32 == KH && NS >= 1, "wave layout must tile the block");
-    static_assert(8192 + (NW - RG) * (D / 8) * 64 * 16 <= NST * C::STAGE, "merge buffers fit in LDS");
-    static_assert(!PRUNE || NW == 8, "the pruned tile exchange assumes 8 waves");
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int KG = NW / RG;
     const int rg = wave % RG, kg = wave / RG;
-    const int c32 = lane & 31, g = lane >> 5;
-    constexpr int esz = (int)sizeof(T);
-
-    // F0: this lane's query row as the B operand (zero past the tile end).
-    const int qrow = q_lo + 32 * rg + c32;
-    const T *qb = static_cast<const T *>(p.q) + (int64_t)h * p.q_sh + (int64_t)q_lo * p.q_sn;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (int64_t)(q_hi - q_lo) * p.q_sn * esz);
-    vec8 qreg[C::NKK];
-#pragma unroll
-    for (int kk = 0; kk < C::NKK; ++kk)
-        qreg[kk] = __builtin_bit_cast(vec8, bload16(rq, ((32 * rg + c32) * (int)p.q_sn + 16 * kk + 8 * g) * esz));
-
-    const T *kh = static_cast<const T *>(p.k) + (int64_t)h * p.kv_sh;
-    const T *vh = static_cast<const T *>(p.v) + (int64_t)h * p.kv_sh;
-    const int kv_sn = (int)p.kv_sn;
-
-    // F1: DMA block [k0, k0 + BC) of K and V into stage `buf`.  DMA
-    // instruction i of this wave fills LDS bytes [(NW i + wave) 1 KiB, +1 KiB)
-    // of each tile; each lane fetches the global chunk its swizzled LDS slot
-    // holds.  Rows at or past kv_hi arrive as zeros.
-    int dma_off[C::NDMA];
-#pragma unroll
-    for (int i = 0; i < C::NDMA; ++i) {
-        const int byte = (NW * i + wave) * 1024 + 16 * lane;
-        const int row = byte / C::ROW, pch = (byte % C::ROW) / 16;
-        (void)pch;
-        dma_off[i] = row * kv_sn * esz;  // + logical chunk, per tile below
-    }
-    auto issue = [&](int k0, int buf) {
-        const int64_t bytes = (int64_t)(kv_hi - k0) * kv_sn * esz;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh + (int64_t)k0 * kv_sn, bytes);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh + (int64_t)k0 * kv_sn, bytes);
-        char *sk = smem + buf * C::STAGE;
-        char *sv = sk + C::TILE;
-#pragma unroll
-        for (int i = 0; i < C::NDMA; ++i) {
-            const int byte = (NW * i + wave) * 1024 + 16 * lane;
-            const int row = byte / C::ROW, pch = (byte % C::ROW) / 16;
-            dma16(rk, sk + (NW * i + wave) * 1024, dma_off[i] + swz_k<C::ROW>(row, pch) * 16);
-            dma16(rv, sv + (NW * i + wave) * 1024, dma_off[i] + swz_vt<C::ROW>(row, pch) * 16);
-        }
-    };
-
-    f32x16 U[C::NDT];
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) U[dt] = zero_vec<f32x16>();
-    float m_ref = kNegInf, m_true = kNegInf, l_run = 0.f;
-    const float c = p.scale_log2;
-    const int nblk = (kv_hi - kv_lo + C::BC - 1) / C::BC;
-    const int wrow_lo = q_lo + 32 * rg, wrow_hi = wrow_lo + 31;
-    float m_blk = kNegInf;  // PRUNE: running maximum of the query block (raw score units)
-
-    // Prefetch distance NST - 1 blocks.
-    for (int j = 0; j < NST - 1 && j < nblk; ++j) issue(kv_lo + j * C::BC, j);
-    for (int j = 0; j < nblk; ++j) {
-        // Block j has landed (this thread's DMA) and, after the barrier, for
-        // every thread; every wave has also finished reading block j-1, so
-        // its stage can take block j + NST - 1.
-        wait_dma_blocks<C::NDMA_BLOCK, NST>(min(NST - 2, nblk - 1 - j));
-        bare_barrier();
-        if (j + NST - 1 < nblk) issue(kv_lo + (j + NST - 1) * C::BC, (j + NST - 1) % NST);
-
-        const int k0 = kv_lo + j * C::BC;
-        const int kw0 = k0 + kg * KH;  // first key of this wave's group
-        const char *sk = smem + (j % NST) * C::STAGE;
-        const char *sv = sk + C::TILE;
-        if constexpr (PRUNE) {
-            // Tile pruning (TIGA-lang "tile-pruned sparse attention", the
-            // admission rule): the block is one (128-row, BC-key) tile.  Every
-            // wave scores its keys for its rows, the 8 waves' maxima meet in
-            // LDS, and the tile is admitted iff its maximum reaches the
-            // block's running maximum plus ln(rho) (p.prune_thr = ln(rho) /
-            // scale in raw score units).  A pruned tile skips the
-            // exponentials and the P.V product; its V block was prefetched.
-            const bool act = kw0 < kv_hi;
-            f32x16 S[NS];
-            float mxc[NS];
-            float wmax = kNegInf;
-            if (act) {
-#pragma unroll
-                for (int cc = 0; cc < NS; ++cc) {
-                    const int row = kg * KH + 32 * cc + c32;
-                    const char *krow = sk + row * C::ROW;
-                    S[cc] = zero_vec<f32x16>();
-#pragma unroll
-                    for (int kk = 0; kk < C::NKK; ++kk) {
-                        const vec8 a = *reinterpret_cast<const vec8 *>(krow + swz_k<C::ROW>(row, 2 * kk + g) * 16);
-                        S[cc] = Half8<T>::mma(a, qreg[kk], S[cc]);
-                    }
-                    const int kc0 = kw0 + 32 * cc;
-                    if (kc0 + 32 > kv_hi) {
-                        f32x16 Sm[1] = {S[cc]};
-                        mask_block<1, false>(Sm, kc0, g, kv_hi, qrow);
-                        S[cc] = Sm[0];
-                    }
-                    float t[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        t[i] = vmax(vmax(S[cc][4 * i], S[cc][4 * i + 1]), vmax(S[cc][4 * i + 2], S[cc][4 * i + 3]));
-                    mxc[cc] = xor32_max(vmax(vmax(t[0], t[1]), vmax(t[2], t[3])));
-                    wmax = vmax(wmax, mxc[cc]);
-                }
-                if (qrow >= q_hi) wmax = kNegInf;  // rows past the tile end do not count
-            }
-#pragma unroll
-            for (int off = 16; off >= 1; off >>= 1) wmax = vmax(wmax, __shfl_xor(wmax, off));
-            float *slot = reinterpret_cast<float *>(smem + NST * C::STAGE);
-            if (lane == 0) slot[wave] = wmax;
-            wait_lgkmcnt0();
-            bare_barrier();
-            float m_tile = slot[0];
-#pragma unroll
-            for (int w = 1; w < NW; ++w) m_tile = vmax(m_tile, slot[w]);
-            if (m_tile >= m_blk + p.prune_thr) {
-                m_blk = vmax(m_blk, m_tile);
-                if (act) {
-#pragma unroll
-                    for (int cc = 0; cc < NS; ++cc) {
-                        const float mx = mxc[cc];
-                        m_true = vmax(m_true, mx);
-                        if (__any((mx - m_ref) * c > kLazyLog2)) {
-                            const float m_new = vmax(m_ref, mx);
-                            const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_ref - m_new) * c);
-#pragma unroll
-                            for (int dt = 0; dt < C::NDT; ++dt) U[dt] *= alpha;
-                            l_run *= alpha;
-                            m_ref = m_new;
-                        }
-                        const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
-                        vec8 P[2];
-                        float ps = 0.f;
-#pragma unroll
-                        for (int hf = 0; hf < 2; ++hf) {
-                            f32x8 x;
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) x[e] = fast_exp2(fmaf(S[cc][8 * hf + e], c, -mc));
-                            ps += ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
-                            P[hf] = __builtin_convertvector(x, vec8);
-                        }
-                        l_run += ps;
-#pragma unroll
-                        for (int hf = 0; hf < 2; ++hf) {
-                            const int r0 = kg * KH + 32 * cc + 16 * hf + 4 * g + ((lane & 15) >> 2);
-                            const int cq = lane & 3, hh = (lane >> 4) & 1;
-#pragma unroll
-                            for (int dt = 0; dt < C::NDT; ++dt) {
-                                const int ch = 4 * dt + 2 * hh + (cq >> 1);
-                                const i16x4 lo = lds_read_tr16(sv + r0 * C::ROW + swz_vt<C::ROW>(r0, ch) * 16 + 8 * (cq & 1));
-                                const i16x4 hi = lds_read_tr16(sv + (r0 + 8) * C::ROW + swz_vt<C::ROW>(r0 + 8, ch) * 16 + 8 * (cq & 1));
-                                const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                                U[dt] = Half8<T>::mma(a, P[hf], U[dt]);
-                            }
-                        }
-                    }
-                }
-            }
-            continue;
-        }
-        if (kw0 < kv_hi && (!causal || kw0 <= wrow_hi)) {
-            // The wave's KH keys are processed as 32-key chunks, software
-            // pipelined: chunk cc+1's S^T MFMAs are issued before chunk cc's
-            // exponentials so the two overlap in the same scheduling region.
-            auto qk = [&](int cc) {  // F2: S^T = K Q^T for one 32-key chunk
-                f32x16 S = zero_vec<f32x16>();
-                const int row = kg * KH + 32 * cc + c32;
-                const char *krow = sk + row * C::ROW;
-#pragma unroll
-                for (int kk = 0; kk < C::NKK; ++kk) {
-                    const vec8 a = *reinterpret_cast<const vec8 *>(krow + swz_k<C::ROW>(row, 2 * kk + g) * 16);
-                    S = Half8<T>::mma(a, qreg[kk], S);
-                }
-                return S;
-            };
-            f32x16 S = qk(0);
-#pragma unroll
-            for (int cc = 0; cc < NS; ++cc) {
-                const int kc0 = kw0 + 32 * cc;
-                // F3: mask chunks that cross the tail or the diagonal.
-                if (kc0 + 32 > kv_hi || (causal && kc0 + 31 > wrow_lo)) {
-                    f32x16 Sm[1] = {S};
-                    mask_block<1, causal>(Sm, kc0, g, kv_hi, qrow);
-                    S = Sm[0];
-                }
-                // F4: chunk row maximum (in-lane, then the other lane half).
-                float t[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    t[i] = vmax(vmax(S[4 * i], S[4 * i + 1]), vmax(S[4 * i + 2], S[4 * i + 3]));
-                float mx = vmax(vmax(t[0], t[1]), vmax(t[2], t[3]));
-                mx = xor32_max(mx);
-                m_true = vmax(m_true, mx);
-                // F5 (lazy): move the exponent reference only on a large increase.
-                if (__any((mx - m_ref) * c > kLazyLog2)) {
-                    const float m_new = vmax(m_ref, mx);
-                    const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_ref - m_new) * c);
-#pragma unroll
-                    for (int dt = 0; dt < C::NDT; ++dt) U[dt] *= alpha;
-                    l_run *= alpha;
-                    m_ref = m_new;
-                }
-                const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
-                f32x16 Sn;
-                if (cc + 1 < NS) Sn = qk(cc + 1);
-                float ps[4];
-                vec8 P[2];
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    f32x8 x;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = fast_exp2(fmaf(S[8 * hf + e], c, -mc));
-                    ps[2 * hf] = (x[0] + x[1]) + (x[2] + x[3]);
-                    ps[2 * hf + 1] = (x[4] + x[5]) + (x[6] + x[7]);
-                    P[hf] = __builtin_convertvector(x, vec8);
-                }
-                l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-                // F6: U += V^T P^T over the chunk's two 16-key slices; slice hf
-                // holds keys 32 cc + 16 hf + 8 x + 4 g + 0..3 (x = 0, 1).
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const int r0 = kg * KH + 32 * cc + 16 * hf + 4 * g + ((lane & 15) >> 2);
-                    const int cq = lane & 3, hh = (lane >> 4) & 1;
-#pragma unroll
-                    for (int dt = 0; dt < C::NDT; ++dt) {
-                        const int ch = 4 * dt + 2 * hh + (cq >> 1);
-                        const i16x4 lo = lds_read_tr16(sv + r0 * C::ROW + swz_vt<C::ROW>(r0, ch) * 16 + 8 * (cq & 1));
-                        const i16x4 hi = lds_read_tr16(sv + (r0 + 8) * C::ROW + swz_vt<C::ROW>(r0 + 8, ch) * 16 + 8 * (cq & 1));
-                        const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                        U[dt] = Half8<T>::mma(a, P[hf], U[dt]);
-                    }
-                }
-                if (cc + 1 < NS) S = Sn;
-            }
-        }
-    }
+    const int g = lane >> 5;
     __syncthreads();  // every wave is done with the last stage
 
     // F7: merge the KG key groups of each row, then O = U / l.
@@ -712,6 +469,170 @@ __device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h
     __syncthreads();  // the next tile's prologue reuses this LDS
 }
 
+// The NW waves of a workgroup form RG row groups of 32 query rows (a tile of
+// 32 RG rows) times KG = NW / RG key groups; key group kg takes keys
+// [kg KH, (kg + 1) KH) of every block, and the KG partial states of a row are
+// merged through LDS at the end.  Launches use RG = 4 (128-row tiles) unless
+// such tiles are too few to occupy the device.
+// split < 0: write O, m, l.  split >= 0: write this key range's partial state.
+// O16: O is written in T (the same f32 values rounded once) instead of f32.
+template <typename T, int D, int MASK, int NST, int RG, int NW = 8,
+          bool O16 = false>
+__device__ __forceinline__ void fwd16_tile(const FwdParams &p, char *smem, int h, int q_lo,
+                                           int q_hi, int kv_lo, int kv_hi, int split) {
+    typedef Fwd16Cfg<D, NST, NW> C;
+    typedef typename Half8<T>::vec vec8;
+    constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
+    constexpr int KG = NW / RG, KH = C::BC / KG, NS = KH / 32;  // keys, 32-key chunks per wave
+    static_assert(RG * KG == NW && NS * 32 == KH && NS >= 1, "wave layout must tile the block");
+    static_assert(8192 + (NW - RG) * (D / 8) * 64 * 16 <= NST * C::STAGE, "merge buffers fit in LDS");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rg = wave % RG, kg = wave / RG;
+    const int c32 = lane & 31, g = lane >> 5;
+    constexpr int esz = (int)sizeof(T);
+
+    // F0: this lane's query row as the B operand (zero past the tile end).
+    const int qrow = q_lo + 32 * rg + c32;
+    const T *qb = static_cast<const T *>(p.q) + (int64_t)h * p.q_sh + (int64_t)q_lo * p.q_sn;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (int64_t)(q_hi - q_lo) * p.q_sn * esz);
+    vec8 qreg[C::NKK];
+#pragma unroll
+    for (int kk = 0; kk < C::NKK; ++kk)
+        qreg[kk] = __builtin_bit_cast(vec8, bload16(rq, ((32 * rg + c32) * (int)p.q_sn + 16 * kk + 8 * g) * esz));
+
+    const T *kh = static_cast<const T *>(p.k) + (int64_t)h * p.kv_sh;
+    const T *vh = static_cast<const T *>(p.v) + (int64_t)h * p.kv_sh;
+    const int kv_sn = (int)p.kv_sn;
+
+    // F1: DMA block [k0, k0 + BC) of K and V into stage `buf`.  DMA
+    // instruction i of this wave fills LDS bytes [(NW i + wave) 1 KiB, +1 KiB)
+    // of each tile; each lane fetches the global chunk its swizzled LDS slot
+    // holds.  Rows at or past kv_hi arrive as zeros.
+    int dma_off[C::NDMA];
+#pragma unroll
+    for (int i = 0; i < C::NDMA; ++i) {
+        const int byte = (NW * i + wave) * 1024 + 16 * lane;
+        const int row = byte / C::ROW, pch = (byte % C::ROW) / 16;
+        (void)pch;
+        dma_off[i] = row * kv_sn * esz;  // + logical chunk, per tile below
+    }
+    auto issue = [&](int k0, int buf) {
+        const int64_t bytes = (int64_t)(kv_hi - k0) * kv_sn * esz;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh + (int64_t)k0 * kv_sn, bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh + (int64_t)k0 * kv_sn, bytes);
+        char *sk = smem + buf * C::STAGE;
+        char *sv = sk + C::TILE;
+#pragma unroll
+        for (int i = 0; i < C::NDMA; ++i) {
+            const int byte = (NW * i + wave) * 1024 + 16 * lane;
+            const int row = byte / C::ROW, pch = (byte % C::ROW) / 16;
+            dma16(rk, sk + (NW * i + wave) * 1024, dma_off[i] + swz_k<C::ROW>(row, pch) * 16);
+            dma16(rv, sv + (NW * i + wave) * 1024, dma_off[i] + swz_vt<C::ROW>(row, pch) * 16);
+        }
+    };
+
+    f32x16 U[C::NDT];
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) U[dt] = zero_vec<f32x16>();
+    float m_ref = kNegInf, m_true = kNegInf, l_run = 0.f;
+    const float c = p.scale_log2;
+    const int nblk = (kv_hi - kv_lo + C::BC - 1) / C::BC;
+    const int wrow_lo = q_lo + 32 * rg, wrow_hi = wrow_lo + 31;
+
+    // Prefetch distance NST - 1 blocks.
+    for (int j = 0; j < NST - 1 && j < nblk; ++j) issue(kv_lo + j * C::BC, j);
+    for (int j = 0; j < nblk; ++j) {
+        // Block j has landed (this thread's DMA) and, after the barrier, for
+        // every thread; every wave has also finished reading block j-1, so
+        // its stage can take block j + NST - 1.
+        wait_dma_blocks<C::NDMA_BLOCK, NST>(min(NST - 2, nblk - 1 - j));
+        bare_barrier();
+        if (j + NST - 1 < nblk) issue(kv_lo + (j + NST - 1) * C::BC, (j + NST - 1) % NST);
+
+        const int k0 = kv_lo + j * C::BC;
+        const int kw0 = k0 + kg * KH;  // first key of this wave's group
+        const char *sk = smem + (j % NST) * C::STAGE;
+        const char *sv = sk + C::TILE;
+        if (kw0 < kv_hi && (!causal || kw0 <= wrow_hi)) {
+            // The wave's KH keys are processed as 32-key chunks, software
+            // pipelined: chunk cc+1's S^T MFMAs are issued before chunk cc's
+            // exponentials so the two overlap in the same scheduling region.
+            auto qk = [&](int cc) {  // F2: S^T = K Q^T for one 32-key chunk
+                f32x16 S = zero_vec<f32x16>();
+                const int row = kg * KH + 32 * cc + c32;
+                const char *krow = sk + row * C::ROW;
+#pragma unroll
+                for (int kk = 0; kk < C::NKK; ++kk) {
+                    const vec8 a = *reinterpret_cast<const vec8 *>(krow + swz_k<C::ROW>(row, 2 * kk + g) * 16);
+                    S = Half8<T>::mma(a, qreg[kk], S);
+                }
+                return S;
+            };
+            f32x16 S = qk(0);
+#pragma unroll
+            for (int cc = 0; cc < NS; ++cc) {
+                const int kc0 = kw0 + 32 * cc;
+                // F3: mask chunks that cross the tail or the diagonal.
+                if (kc0 + 32 > kv_hi || (causal && kc0 + 31 > wrow_lo)) {
+                    f32x16 Sm[1] = {S};
+                    mask_block<1, causal>(Sm, kc0, g, kv_hi, qrow);
+                    S = Sm[0];
+                }
+                // F4: chunk row maximum (in-lane, then the other lane half).
+                float t[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    t[i] = vmax(vmax(S[4 * i], S[4 * i + 1]), vmax(S[4 * i + 2], S[4 * i + 3]));
+                float mx = vmax(vmax(t[0], t[1]), vmax(t[2], t[3]));
+                mx = xor32_max(mx);
+                m_true = vmax(m_true, mx);
+                // F5 (lazy): move the exponent reference only on a large increase.
+                if (__any((mx - m_ref) * c > kLazyLog2)) {
+                    const float m_new = vmax(m_ref, mx);
+                    const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_ref - m_new) * c);
+#pragma unroll
+                    for (int dt = 0; dt < C::NDT; ++dt) U[dt] *= alpha;
+                    l_run *= alpha;
+                    m_ref = m_new;
+                }
+                const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
+                f32x16 Sn;
+                if (cc + 1 < NS) Sn = qk(cc + 1);
+                float ps[4];
+                vec8 P[2];
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    f32x8 x;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = fast_exp2(fmaf(S[8 * hf + e], c, -mc));
+                    ps[2 * hf] = (x[0] + x[1]) + (x[2] + x[3]);
+                    ps[2 * hf + 1] = (x[4] + x[5]) + (x[6] + x[7]);
+                    P[hf] = __builtin_convertvector(x, vec8);
+                }
+                l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+                // F6: U += V^T P^T over the chunk's two 16-key slices; slice hf
+                // holds keys 32 cc + 16 hf + 8 x + 4 g + 0..3 (x = 0, 1).
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int r0 = kg * KH + 32 * cc + 16 * hf + 4 * g + ((lane & 15) >> 2);
+                    const int cq = lane & 3, hh = (lane >> 4) & 1;
+#pragma unroll
+                    for (int dt = 0; dt < C::NDT; ++dt) {
+                        const int ch = 4 * dt + 2 * hh + (cq >> 1);
+                        const i16x4 lo = lds_read_tr16(sv + r0 * C::ROW + swz_vt<C::ROW>(r0, ch) * 16 + 8 * (cq & 1));
+                        const i16x4 hi = lds_read_tr16(sv + (r0 + 8) * C::ROW + swz_vt<C::ROW>(r0 + 8, ch) * 16 + 8 * (cq & 1));
+                        const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                        U[dt] = Half8<T>::mma(a, P[hf], U[dt]);
+                    }
+                }
+                if (cc + 1 < NS) S = Sn;
+            }
+        }
+    }
+    fwd16_finish<T, D, NST, RG, NW, O16>(p, smem, h, q_hi, split, wave, lane, qrow, U, m_ref,
+                                         m_true, l_run, c);
+}
+
 // Split-KV combine: one pass over a row's partial states (U_s, l_s against
 // reference m_s) with the rule the recurrence uses between blocks -- a running
 // reference M, rescale by 2^((M_old - M) c) when it grows, add U_s 2^((m_s - M) c)
@@ -885,7 +806,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdPara
         const int h = r % p.H, tile = r / p.H;
         const int q_lo = tile * TR, q_hi = min(q_lo + TR, p.n_q);
         const int k_lo = split * p.split_len, k_hi = min(k_lo + p.split_len, p.n_k);
-        fwd16_tile<T, D, MASK, NST, RG, false, NW, O16>(p, smem, h, q_lo, q_hi, k_lo, k_hi, split);
+        fwd16_tile<T, D, MASK, NST, RG, NW, O16>(p, smem, h, q_lo, q_hi, k_lo, k_hi, split);
         return;
     }
     const int h = b % p.H;
@@ -922,7 +843,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdPara
             const int tile = k == 0 ? ta : tb;
             if (tile < 0) break;
             const int q_lo = s_lo + tile * TR, q_hi = min(q_lo + TR, s_hi);
-            fwd16_tile<T, D, MASK, NST, RG, false, NW, O16>(p, smem, h, q_lo, q_hi, s_lo, causal ? q_hi : s_hi, -1);
+            fwd16_tile<T, D, MASK, NST, RG, NW, O16>(p, smem, h, q_lo, q_hi, s_lo, causal ? q_hi : s_hi, -1);
         }
         return;
     }
@@ -934,7 +855,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdPara
             if (tile < 0) break;
             const int q_lo = it.x + tile * TR, q_hi = min(q_lo + TR, it.y);
             if (q_lo >= q_hi) break;
-            fwd16_tile<T, D, MASK, NST, RG, false, NW, O16>(p, smem, h, q_lo, q_hi, it.x, causal ? q_hi : it.y, -1);
+            fwd16_tile<T, D, MASK, NST, RG, NW, O16>(p, smem, h, q_lo, q_hi, it.x, causal ? q_hi : it.y, -1);
         }
         return;
     }
@@ -970,7 +891,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdPara
         if (tile < 0) break;
         const int q_lo = seq_lo + tile * TR, q_hi = min(q_lo + TR, seq_hi);
         const int kv_hi = causal ? q_hi : (varlen ? seq_hi : p.n_k);
-        fwd16_tile<T, D, MASK, NST, RG, false, NW, O16>(p, smem, h, q_lo, q_hi, seq_lo, kv_hi, -1);
+        fwd16_tile<T, D, MASK, NST, RG, NW, O16>(p, smem, h, q_lo, q_hi, seq_lo, kv_hi, -1);
     }
 }
 
@@ -1600,9 +1521,209 @@ hipError_t launch_varlen_schedule(int d, int causal, const int32_t *cu, int num_
     return hipGetLastError();
 }
 
-// Tile-pruned dense forward: one 128-row tile per workgroup, key blocks of 128
-// (D = 64 uses four stages of 128 keys so that both widths prune 128 x 128
-// tiles).
+// ------------------------------------------------ tile-pruned forward
+// TIGA-lang "tile-pruned sparse attention", admission rule: a (128-row,
+// 128-key) tile of the dense relation is admitted iff its maximum score reaches
+// the query block's running maximum (over admitted tiles) plus ln(rho), with
+// p.prune_thr = ln(rho) / scale in raw score units; a pruned tile contributes
+// nothing and its V block is never read.
+//
+// The 8 waves (4 row groups of 32 rows x 2 key groups of 64 keys) run a
+// pipeline with one block of lag: in iteration j they score block j+1 and
+// exchange the tile maxima through LDS, start V(j+1) only if that tile is
+// admitted, and then run the softmax and P.V of block j (if admitted) from the
+// scores kept in registers.  K is copied two blocks ahead, V one; each has two
+// LDS slots, and one barrier at the top of the iteration (after the copies
+// that block j needs have landed) frees the slots the iteration refills.
+template <typename T, int D, bool O16>
+__device__ __forceinline__ void fwd16_pruned_tile(const FwdParams &p, char *smem, int h, int q_lo,
+                                                  int q_hi) {
+    constexpr int NST = D == 64 ? 4 : 2;  // the finish routine's view of the LDS
+    constexpr int NW = 8, RG = 4, KG = 2, BC = 128, KH = BC / KG, NS = KH / 32;
+    static_assert(Fwd16Cfg<D, NST>::BC == BC, "pruning tiles are 128 keys");
+    constexpr int ROW = D * 2, TILE = BC * ROW, NKK = D / 16, NDT = D / 32;
+    constexpr int NDMA = TILE / (64 * NW * 16);  // 16-byte copies per lane per block
+    constexpr int KS = 0, VS = 2 * TILE, XCH = 4 * TILE;  // K slots, V slots, tile maxima
+    typedef typename Half8<T>::vec vec8;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rg = wave % RG, kg = wave / RG;
+    const int c32 = lane & 31, g = lane >> 5;
+    constexpr int esz = (int)sizeof(T);
+    const int kv_hi = p.n_k;
+    const float c = p.scale_log2;
+
+    // F0: this lane's query row as the B operand (zero past the tile end).
+    const int qrow = q_lo + 32 * rg + c32;
+    const T *qb = static_cast<const T *>(p.q) + (int64_t)h * p.q_sh + (int64_t)q_lo * p.q_sn;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (int64_t)(q_hi - q_lo) * p.q_sn * esz);
+    vec8 qreg[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+        qreg[kk] = __builtin_bit_cast(vec8, bload16(rq, ((32 * rg + c32) * (int)p.q_sn + 16 * kk + 8 * g) * esz));
+
+    // F1: copy i of this wave fills bytes [(NW i + wave) KiB, +1 KiB) of a
+    // slot; each lane fetches the global chunk its swizzled LDS place holds.
+    // Rows at or past kv_hi arrive as zeros.
+    const T *kh = static_cast<const T *>(p.k) + (int64_t)h * p.kv_sh;
+    const T *vh = static_cast<const T *>(p.v) + (int64_t)h * p.kv_sh;
+    const int kv_sn = (int)p.kv_sn;
+    const auto copy_block = [&](const T *base, int b, int slot, bool is_v) {
+        const int k0 = b * BC;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (int64_t)k0 * kv_sn, (int64_t)(kv_hi - k0) * kv_sn * esz);
+        char *dst = smem + slot;
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            const int byte = (NW * i + wave) * 1024 + 16 * lane;
+            const int row = byte / ROW, pch = (byte % ROW) / 16;
+            const int ch = is_v ? swz_vt<ROW>(row, pch) : swz_k<ROW>(row, pch);
+            dma16(r, dst + (NW * i + wave) * 1024, row * kv_sn * esz + ch * 16);
+        }
+    };
+
+    // F2-F3 for block b: this wave's NS chunks of S^T = K Q^T (tail keys -inf),
+    // each chunk's row maximum, and the wave's maximum over its admitted rows.
+    const auto scores = [&](int b, f32x16 (&S)[NS], float (&mxc)[NS]) {
+        const int kw0 = b * BC + kg * KH;
+        const char *sk = smem + KS + (b & 1) * TILE;
+        float wmax = kNegInf;
+#pragma unroll
+        for (int cc = 0; cc < NS; ++cc) {
+            mxc[cc] = kNegInf;
+            S[cc] = zero_vec<f32x16>();
+        }
+        if (kw0 < kv_hi) {
+#pragma unroll
+            for (int cc = 0; cc < NS; ++cc) {
+                const int row = kg * KH + 32 * cc + c32;
+                const char *krow = sk + row * ROW;
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const vec8 a = *reinterpret_cast<const vec8 *>(krow + swz_k<ROW>(row, 2 * kk + g) * 16);
+                    S[cc] = Half8<T>::mma(a, qreg[kk], S[cc]);
+                }
+                const int kc0 = kw0 + 32 * cc;
+                if (kc0 + 32 > kv_hi) {
+                    f32x16 Sm[1] = {S[cc]};
+                    mask_block<1, false>(Sm, kc0, g, kv_hi, qrow);
+                    S[cc] = Sm[0];
+                }
+                float t[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    t[i] = vmax(vmax(S[cc][4 * i], S[cc][4 * i + 1]), vmax(S[cc][4 * i + 2], S[cc][4 * i + 3]));
+                mxc[cc] = xor32_max(vmax(vmax(t[0], t[1]), vmax(t[2], t[3])));
+                wmax = vmax(wmax, mxc[cc]);
+            }
+            if (qrow >= q_hi) wmax = kNegInf;  // rows past the tile end do not count
+        }
+        return wmax;
+    };
+    // The tile maximum (all 8 waves' maxima through LDS, one barrier) and the
+    // admission decision, the same in every wave.
+    float m_blk = kNegInf;  // running maximum of the query block (raw score units)
+    const auto admit = [&](float wmax) {
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) wmax = vmax(wmax, __shfl_xor(wmax, off));
+        float *slot = reinterpret_cast<float *>(smem + XCH);
+        if (lane == 0) slot[wave] = wmax;
+        wait_lgkmcnt0();
+        bare_barrier();
+        float m_tile = slot[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) m_tile = vmax(m_tile, slot[w]);
+        const bool ok = m_tile >= m_blk + p.prune_thr;
+        if (ok) m_blk = vmax(m_blk, m_tile);
+        return ok;
+    };
+
+    f32x16 U[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) U[dt] = zero_vec<f32x16>();
+    float m_ref = kNegInf, m_true = kNegInf, l_run = 0.f;
+    // F4-F6 for an admitted block: lazy reference, probabilities, U += V^T P^T.
+    const auto accumulate = [&](int b, const f32x16 (&S)[NS], const float (&mxc)[NS]) {
+        const char *sv = smem + VS + (b & 1) * TILE;
+#pragma unroll
+        for (int cc = 0; cc < NS; ++cc) {
+            const float mx = mxc[cc];
+            m_true = vmax(m_true, mx);
+            if (__any((mx - m_ref) * c > kLazyLog2)) {
+                const float m_new = vmax(m_ref, mx);
+                const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_ref - m_new) * c);
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) U[dt] *= alpha;
+                l_run *= alpha;
+                m_ref = m_new;
+            }
+            const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
+            vec8 P[2];
+            float ps = 0.f;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                f32x8 x;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = fast_exp2(fmaf(S[cc][8 * hf + e], c, -mc));
+                ps += ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+                P[hf] = __builtin_convertvector(x, vec8);
+            }
+            l_run += ps;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int r0 = kg * KH + 32 * cc + 16 * hf + 4 * g + ((lane & 15) >> 2);
+                const int cq = lane & 3, hh = (lane >> 4) & 1;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    const int ch = 4 * dt + 2 * hh + (cq >> 1);
+                    const i16x4 lo = lds_read_tr16(sv + r0 * ROW + swz_vt<ROW>(r0, ch) * 16 + 8 * (cq & 1));
+                    const i16x4 hi = lds_read_tr16(sv + (r0 + 8) * ROW + swz_vt<ROW>(r0 + 8, ch) * 16 + 8 * (cq & 1));
+                    const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    U[dt] = Half8<T>::mma(a, P[hf], U[dt]);
+                }
+            }
+        }
+    };
+
+    const int nblk = (kv_hi + BC - 1) / BC;
+    copy_block(kh, 0, KS, false);
+    if (nblk > 1) copy_block(kh, 1, KS + TILE, false);
+    if (nblk > 1) wait_vmcnt<NDMA>();  // K(0) (copies complete in order)
+    else wait_vmcnt<0>();
+    bare_barrier();
+    f32x16 Sc[NS];
+    float mxc[NS];
+    bool adm = admit(scores(0, Sc, mxc));
+    if (adm) copy_block(vh, 0, VS, true);
+#pragma unroll 1
+    for (int j = 0; j < nblk; ++j) {
+        // K(j+1) and, if block j is admitted, V(j) have landed for every
+        // wave; every wave is past its reads of K(j) and V(j-1).
+        wait_vmcnt<0>();
+        bare_barrier();
+        bool adm_n = false;
+        f32x16 Sn[NS];
+        float mxn[NS];
+        if (j + 1 < nblk) {
+            if (j + 2 < nblk) copy_block(kh, j + 2, KS + (j & 1) * TILE, false);
+            adm_n = admit(scores(j + 1, Sn, mxn));
+            if (adm_n) copy_block(vh, j + 1, VS + ((j + 1) & 1) * TILE, true);
+        }
+        if (adm && kg * KH + j * BC < kv_hi) accumulate(j, Sc, mxc);
+        if (j + 1 < nblk) {
+#pragma unroll
+            for (int cc = 0; cc < NS; ++cc) {
+                Sc[cc] = Sn[cc];
+                mxc[cc] = mxn[cc];
+            }
+        }
+        adm = adm_n;
+    }
+    fwd16_finish<T, D, NST, RG, NW, O16>(p, smem, h, q_hi, -1, wave, lane, qrow, U, m_ref, m_true,
+                                         l_run, c);
+}
+
+// Tile-pruned dense forward: one 128-row tile per workgroup, 128 x 128 tiles at
+// both widths.  The LDS holds the rings of fwd16_pruned_tile and, at the end,
+// the key-group merge of the finish routine (which sees it as NST stages).
 template <typename T, int D, bool O16>
 __global__ void __launch_bounds__(kT16) fwd16_pruned_kernel(FwdParams p) {
     constexpr int NST = D == 64 ? 4 : 2;
@@ -1610,7 +1731,7 @@ __global__ void __launch_bounds__(kT16) fwd16_pruned_kernel(FwdParams p) {
     __shared__ __attribute__((aligned(16))) char smem[NST * Fwd16Cfg<D, NST>::STAGE + 256];
     const int h = blockIdx.x % p.H, tile = blockIdx.x / p.H;
     const int q_lo = tile * kBR, q_hi = min(q_lo + kBR, p.n_q);
-    fwd16_tile<T, D, kDense, NST, 4, true, 8, O16>(p, smem, h, q_lo, q_hi, 0, p.n_k, -1);
+    fwd16_pruned_tile<T, D, O16>(p, smem, h, q_lo, q_hi);
 }
 
 hipError_t launch_forward_pruned(int dtype, int d, FwdParams p, hipStream_t st) {
