@@ -108,6 +108,68 @@ def fwd_kernel_name(w, torch, split: bool) -> str:
     return "fwd_wide_kernel" if items >= cus else "fwd16_kernel"
 
 
+# FETCH_SIZE and WRITE_SIZE scale factors to true bytes, from the calibration
+# runs in profiles/hbm_counter_calibration.md (a 256 MiB copy: 262144 KiB moved,
+# FETCH_SIZE 131084.0 KiB, WRITE_SIZE 262144.0 KiB per dispatch).
+FETCH_SCALE = 262144.0 / 131084.0
+WRITE_SCALE = 1.0
+
+
+def kernel_identifiers(name: str) -> set:
+    """The identifiers in a kernel name as rocprofv3 prints it, mangled
+    (_ZN6osattn12bwd16_kernelI...: length-prefixed) or demangled."""
+    if name.startswith("_Z"):
+        out, i = set(), 0
+        while i < len(name):
+            m = re.match(r"\d+", name[i:])
+            if not m:
+                i += 1
+                continue
+            n, j = int(m.group(0)), i + len(m.group(0))
+            out.add(name[j:j + n])
+            i = j + n
+        return out
+    return set(re.findall(r"[A-Za-z_][A-Za-z0-9_]*", name))
+
+
+def counter_kib_per_launch(csv_path: str, kernels: str, counter: str) -> float:
+    """Sum over the '+'-separated kernel names of a launch of the counter's
+    average per dispatch (KiB), from a rocprofv3 counter_collection CSV."""
+    import csv
+    per = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            idents = kernel_identifiers(r["Kernel_Name"])
+            for k in kernels.split("+"):
+                if k in idents or k + "_kernel" in idents:
+                    per.setdefault(k, []).append(float(r["Counter_Value"]))
+    missing = [k for k in kernels.split("+") if k not in per]
+    if missing:
+        raise SystemExit("no %s dispatches of %s in %s" % (counter, ", ".join(missing), csv_path))
+    return sum(sum(v) / len(v) for v in per.values())
+
+
+def record_traffic(key: str, kernels: str, fetch_csv: str, write_csv: str) -> dict:
+    """Write profiles/traffic.json[key] from a FETCH_SIZE and a WRITE_SIZE pass."""
+    fetch = counter_kib_per_launch(fetch_csv, kernels, "FETCH_SIZE")
+    write = counter_kib_per_launch(write_csv, kernels, "WRITE_SIZE")
+    rec = {"kernel": kernels, "fetch_kib": fetch, "write_kib": write, "fetch_scale": FETCH_SCALE,
+           "write_scale": WRITE_SCALE, "source_sha": kernel_source_sha(),
+           "traffic_bytes": (fetch * FETCH_SCALE + write * WRITE_SCALE) * 1024.0}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    allrec = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            allrec = json.load(f)
+    allrec[key] = rec
+    with open(path, "w") as f:
+        json.dump(allrec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return rec
+
+
 def recorded_traffic(workload: str, kernel: str):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -536,7 +598,13 @@ def main():
                          "(libosattn_probe.so), to calibrate FETCH_SIZE for those loads")
     ap.add_argument("--probe-lds", action="store_true",
                     help="with --read-probe: the loads go to LDS (buffer_load ... lds)")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("KEY", "KERNELS", "FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json[KEY] from rocprofv3 FETCH_SIZE and WRITE_SIZE "
+                         "counter_collection CSVs, summed over the '+'-separated KERNELS (no GPU)")
     args = ap.parse_args()
+    if args.record_traffic:
+        print(json.dumps(record_traffic(*args.record_traffic)), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path "
                          "(--gpus %d requested)\n" % args.gpus)

@@ -187,15 +187,18 @@ FwdPlan plan_forward(int dtype, int H, int64_t n_q, int64_t n_k, int d, int caus
         // f32: 128-row tiles of 4 waves; split the keys until there is about one
         // workgroup per CU.  Measured on MI355X (SQ=8192 SK=2048 H=1 D=64): 149 us
         // unsplit (64 workgroups), 52 us in 4 splits, 55 us in 8 (two per CU).
-        // Keys too few to split (under 512) at d = 64 take 32-row tiles whose
+        // At d = 64, keys too few to split (under 512) take 32-row tiles whose
         // four waves share every key block instead: four times the workgroups
-        // (N=128 H=1: 12.6 -> 6.6 us).  Where the keys can be split, the split
-        // ran faster (SQ=8192 SK=2048 H=1: 48.9 us split vs 50.5 us in 32-row
-        // tiles; N=1024 H=4: 23.2 vs 26.7 us).
+        // (N=128 H=1: 12.6 -> 6.6 us).  So do problems whose 32-row tiles alone
+        // give every CU a workgroup: no partial states are written and read
+        // back, for a little time (SQ=8192 SK=2048 H=1: 50.5 us against 48.9 us
+        // split, 8.9 MB of partials gone).  Smaller grids split the keys
+        // (N=1024 H=4: 23.2 us split vs 26.7 us in 32-row tiles).
         const int64_t items = (int64_t)H * pl.n_tiles;
         const int64_t target = device_cus();
         const int64_t units = (n_k + 127) / 128;
-        if (d == 64 && items < target && units < 4) {
+        const int64_t items32 = (int64_t)H * ((n_q + 31) / 32);
+        if (d == 64 && items < target && (units < 4 || items32 >= target)) {
             pl.f32_groups = 4;
         } else if (items < target && units >= 4) {
             int64_t splits = (target + items - 1) / items;

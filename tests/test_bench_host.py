@@ -71,3 +71,34 @@ def test_recorded_traffic_needs_the_same_workload_kernel_and_sources(tmp_path, m
     assert bench.recorded_traffic("w2", "k") is None
     monkeypatch.setattr(bench, "kernel_source_sha", lambda: "changed")
     assert bench.recorded_traffic("w", "k") is None
+
+
+def test_kernel_identifiers_read_mangled_and_demangled_names():
+    ids = bench.kernel_identifiers("_ZN6osattn12bwd16_kernelIDF16bLi128ELi1ELb0EEEvNS_9BwdParamsE")
+    assert "bwd16_kernel" in ids and "osattn" in ids and "BwdParams" in ids
+    ids = bench.kernel_identifiers("void osattn::fwd_wide_kernel<__bf16, 1, false>(osattn::FwdParams)")
+    assert "fwd_wide_kernel" in ids
+
+
+def test_record_traffic_sums_each_kernels_average_and_scales(tmp_path, monkeypatch):
+    # Two kernels of one launch, two dispatches each: per kernel the average per
+    # dispatch, summed; FETCH_SIZE scaled by the calibration factor, WRITE_SIZE 1x.
+    head = '"Kernel_Name","Counter_Name","Counter_Value"\n'
+    rows = [("_ZN6osattn16bwd16_pre_kernelIDF16bLi128EEEvNS_9BwdParamsE", 10.0, 14.0),
+            ("_ZN6osattn12bwd16_kernelIDF16bLi128ELi1ELb0EEEvNS_9BwdParamsE", 100.0, 300.0),
+            ("void at::native::vectorized_elementwise_kernel<4>", 5000.0, 5000.0)]
+    fetch = tmp_path / "fetch.csv"
+    write = tmp_path / "write.csv"
+    fetch.write_text(head + "".join('"%s","FETCH_SIZE",%f\n"%s","FETCH_SIZE",%f\n' % (n, a, n, b)
+                                    for n, a, b in rows))
+    write.write_text(head + "".join('"%s","WRITE_SIZE",%f\n"%s","WRITE_SIZE",%f\n' % (n, a, n, b)
+                                    for n, a, b in rows))
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_sha", lambda: "abc")
+    rec = bench.record_traffic("w+bwd", "bwd16_pre+bwd16_kernel", str(fetch), str(write))
+    assert rec["fetch_kib"] == 12.0 + 200.0 and rec["write_kib"] == 12.0 + 200.0
+    assert abs(rec["traffic_bytes"] - (212.0 * bench.FETCH_SCALE + 212.0) * 1024) < 1e-6
+    stored = json.loads((tmp_path / "profiles" / "traffic.json").read_text())
+    assert stored["w+bwd"]["source_sha"] == "abc"
+    assert bench.recorded_traffic("w+bwd", "bwd16_pre+bwd16_kernel") == rec["traffic_bytes"]
