@@ -147,10 +147,15 @@ def test_fwd_workspace_bytes(lib):
     assert lib.osattn_fwd_workspace_bytes(F16, 4, 1024, 1024, 64, 1, None, 0, 0) == 0
     assert lib.osattn_fwd_workspace_bytes(F32, 4, 1024, 1024, 64, 1, None, 0, 0) == 0
     assert lib.osattn_fwd_workspace_bytes(F16, 4, 1024, 1024, 96, 0, None, 0, 0) == 0
-    # f32 dense splits whenever its 128-row tiles cannot fill the device and the
-    # keys span at least 512: (splits, H, n_q, D + 4) f32 partial states
-    n = lib.osattn_fwd_workspace_bytes(F32, 1, 8192, 2048, 64, 0, None, 0, 0)
-    assert n > 0 and n % 256 == 0 and n % (8192 * 68 * 4) == 0
+    # f32 dense splits when its 128-row tiles cannot fill the device, the keys
+    # span at least 512 and (d = 64) 32-row tiles cannot fill it either:
+    # (splits, H, n_q, D + 4) f32 partial states
+    n = lib.osattn_fwd_workspace_bytes(F32, 1, 1024, 2048, 64, 0, None, 0, 0)
+    assert n > 0 and n % 256 == 0 and n % (1024 * 68 * 4) == 0
+    n = lib.osattn_fwd_workspace_bytes(F32, 1, 8192, 2048, 128, 0, None, 0, 0)
+    assert n > 0 and n % 256 == 0 and n % (8192 * 132 * 4) == 0
+    # 8192 / 32 = 256 tiles of 32 rows fill the device at d = 64: no partials
+    assert lib.osattn_fwd_workspace_bytes(F32, 1, 8192, 2048, 64, 0, None, 0, 0) == 0
     assert lib.osattn_fwd_workspace_bytes(F32, 4, 1024, 384, 64, 0, None, 0, 0) == 0
     assert lib.osattn_fwd_workspace_bytes(F32, 1, 128, 128, 64, 0, None, 0, 0) == 0
     # enough tiles to fill the device: no split

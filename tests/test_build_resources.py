@@ -20,8 +20,9 @@ BUNDLE_MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 def kernel_private_segments(lib: str, tmp: str) -> dict:
     """{kernel symbol: private segment bytes per lane} for the gfx950 code."""
     sec = os.path.join(tmp, "fatbin.bin")
-    subprocess.run(["objcopy", "--dump-section", ".hip_fatbin=" + sec, lib], check=True,
-                   capture_output=True)
+    # An explicit output file: without one objcopy rewrites its input in place.
+    subprocess.run(["objcopy", "--dump-section", ".hip_fatbin=" + sec, lib,
+                    os.path.join(tmp, "lib_copy.so")], check=True, capture_output=True)
     data = open(sec, "rb").read()
     starts = [m.start() for m in re.finditer(re.escape(BUNDLE_MAGIC), data)]
     out = {}
