@@ -949,39 +949,6 @@ struct Wide128 {
     template <typename T> static constexpr float kRefLog2 = std::is_same<T, _Float16>::value ? 15.f : 64.f;
 };
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// f(integral_constant<int, I>) for I = 0, 1, ... in order.
-template <typename F, int... I>
-__device__ __forceinline__ void for_each_index(F &&f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-
-// The four words of a raw buffer resource over [base, base + bytes) (the same
-// descriptor make_rsrc builds): loads at or past the end return zeros.  The
-// caller passes bytes <= 0x7ffffff0.
-__device__ __forceinline__ i32x4 rsrc_words(const void *base, int bytes) {
-    const int n = bytes < 0 ? 0 : bytes;
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    // Wave-uniform by construction; readfirstlane lets the compiler see it,
-    // so the descriptor sits in scalar registers as the instruction requires.
-    i32x4 r;
-    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
-    r[2] = __builtin_amdgcn_readfirstlane(n);
-    r[3] = 0x00020000;
-    return r;
-}
-
-// 16 bytes per lane from a raw buffer into LDS bytes [lds + 16 L, +16) of
-// lane L; lds is wave-uniform.  Completion is counted by vmcnt only.
-__device__ __forceinline__ void dma16_asm(i32x4 rsrc, uint32_t lds, int voff) {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :
-                 : "v"(voff), "s"(rsrc), "{m0}"(lds)
-                 : "memory");
-}
-
 // Returns false when the tile must be recomputed (see above); then nothing
 // of o, m, l (or the partial state) has been written by this call.  With
 // exact_ref the reference of each row is its exact maximum, and the call
