@@ -87,6 +87,8 @@ def kernel_source_sha() -> str:
 
 
 # The backward's kernels (fp16/bf16, f32), as named in profiles/traffic.json.
+# The varlen backward writes its work list first; the reductions run only when
+# the plan splits keys or queries over partial sums.
 BWD_KERNELS = {False: "bwd16_pre+bwd16_kernel+bwd16_reduce",
                True: "bwd_pre+bwd_dkdv32+bwd_dq32+reduce_parts_f32"}
 
@@ -132,9 +134,12 @@ def kernel_identifiers(name: str) -> set:
     return set(re.findall(r"[A-Za-z_][A-Za-z0-9_]*", name))
 
 
-def counter_kib_per_launch(csv_path: str, kernels: str, counter: str) -> float:
-    """Sum over the '+'-separated kernel names of a launch of the counter's
-    average per dispatch (KiB), from a rocprofv3 counter_collection CSV."""
+def counter_kib_per_launch(csv_path: str, kernels: str, counter: str):
+    """The counter's KiB per launch of the '+'-separated kernels, from a rocprofv3
+    counter_collection CSV: the sum over every dispatch of those kernels divided
+    by the launch count (the fewest dispatches of any kernel present), with the
+    dispatches per launch of each kernel. A launch may run a listed kernel more
+    than once (one reduction per gradient) or not at all (no split partials)."""
     import csv
     per = {}
     with open(csv_path) as f:
@@ -145,17 +150,19 @@ def counter_kib_per_launch(csv_path: str, kernels: str, counter: str) -> float:
             for k in kernels.split("+"):
                 if k in idents or k + "_kernel" in idents:
                     per.setdefault(k, []).append(float(r["Counter_Value"]))
-    missing = [k for k in kernels.split("+") if k not in per]
-    if missing:
-        raise SystemExit("no %s dispatches of %s in %s" % (counter, ", ".join(missing), csv_path))
-    return sum(sum(v) / len(v) for v in per.values())
+    if not per:
+        raise SystemExit("no %s dispatches of %s in %s" % (counter, kernels, csv_path))
+    launches = min(len(v) for v in per.values())
+    counts = {k: len(per.get(k, [])) / launches for k in kernels.split("+")}
+    return sum(sum(v) for v in per.values()) / launches, counts
 
 
 def record_traffic(key: str, kernels: str, fetch_csv: str, write_csv: str) -> dict:
     """Write profiles/traffic.json[key] from a FETCH_SIZE and a WRITE_SIZE pass."""
-    fetch = counter_kib_per_launch(fetch_csv, kernels, "FETCH_SIZE")
-    write = counter_kib_per_launch(write_csv, kernels, "WRITE_SIZE")
-    rec = {"kernel": kernels, "fetch_kib": fetch, "write_kib": write, "fetch_scale": FETCH_SCALE,
+    fetch, counts = counter_kib_per_launch(fetch_csv, kernels, "FETCH_SIZE")
+    write, _ = counter_kib_per_launch(write_csv, kernels, "WRITE_SIZE")
+    rec = {"kernel": kernels, "dispatches_per_launch": counts,
+           "fetch_kib": fetch, "write_kib": write, "fetch_scale": FETCH_SCALE,
            "write_scale": WRITE_SCALE, "source_sha": kernel_source_sha(),
            "traffic_bytes": (fetch * FETCH_SCALE + write * WRITE_SCALE) * 1024.0}
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -415,6 +422,8 @@ def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True, 
         bwd_ms = b0.elapsed_time(b1) / (n_per * reps)
         bwd_ach = bwd_flops(w) / (bwd_ms * 1e-3) / 1e12
         bkern = BWD_KERNELS[w.dtype == "f32"]
+        if w.lengths:
+            bkern = "varlen_schedule_kernel+" + bkern
         bwd_rec = {"bound": "mfma", "launch_us_avg": bwd_ms * 1e3, "achieved": bwd_ach,
                    "peak": peak, "unit": "TFLOP/s", "frac": bwd_ach / peak,
                    "flops_per_launch": bwd_flops(w), "kernel": bkern,
@@ -471,8 +480,8 @@ def run_pruned(name, rho, steps, warmup, torch, np, osa, W, oracle):
             exact()
     torch.cuda.synchronize()
     err = float(np.max(np.abs(o[:hs].cpu().numpy() - ro)))
-    n_per = 20
-    reps = max(1, steps // n_per) if steps > 0 else 10
+    n_per = 50  # the launch protocol of the exact forward's roofline
+    reps = max(10, steps // n_per)
     times = {}
     for tag, fn in (("pruned", pruned), ("exact", exact)):
         g = capture(fn, n_per, torch, stream)
@@ -542,8 +551,8 @@ def run_csr(steps, warmup, torch, np, osa, W, oracle):
     ro, rm, rl = oracle.csr_softmax(row_ptr, col_idx, scores, vw)
     nonempty = np.diff(row_ptr) > 0
     err = float(np.max(np.abs(o.cpu().numpy()[:, nonempty] - ro[:, nonempty])))
-    n_per = 20
-    reps = max(1, steps // n_per) if steps > 0 else 20
+    n_per = 50
+    reps = max(10, steps // n_per)
     g = capture(run, n_per, torch, stream)
     with torch.cuda.stream(stream):
         g.replay()

@@ -8,6 +8,7 @@ import subprocess
 import sys
 
 import numpy as np
+import pytest
 
 import bench
 import workloads as W
@@ -102,3 +103,21 @@ def test_record_traffic_sums_each_kernels_average_and_scales(tmp_path, monkeypat
     stored = json.loads((tmp_path / "profiles" / "traffic.json").read_text())
     assert stored["w+bwd"]["source_sha"] == "abc"
     assert bench.recorded_traffic("w+bwd", "bwd16_pre+bwd16_kernel") == rec["traffic_bytes"]
+
+
+def test_counter_per_launch_counts_repeated_and_absent_kernels(tmp_path):
+    # Two launches: the reduction runs three times per launch, the schedule
+    # kernel not at all; the sum over every dispatch is divided by two.
+    head = '"Kernel_Name","Counter_Name","Counter_Value"\n'
+    body = ""
+    for _ in range(2):
+        body += '"_ZN6osattn12bwd16_kernelIDF16_Li64ELi0ELb0EEEvNS_9BwdParamsE","FETCH_SIZE",100\n'
+        body += '"_ZN6osattn19bwd16_reduce_kernelIDF16_Li64EEEvNS_12ReduceParamsE","FETCH_SIZE",7\n' * 3
+    path = tmp_path / "fetch.csv"
+    path.write_text(head + body)
+    kib, counts = bench.counter_kib_per_launch(
+        str(path), "varlen_schedule_kernel+bwd16_kernel+bwd16_reduce", "FETCH_SIZE")
+    assert kib == 100.0 + 21.0
+    assert counts == {"varlen_schedule_kernel": 0.0, "bwd16_kernel": 1.0, "bwd16_reduce": 3.0}
+    with pytest.raises(SystemExit):
+        bench.counter_kib_per_launch(str(path), "fwd16_kernel", "FETCH_SIZE")
