@@ -273,8 +273,6 @@ def capture(fn, n, torch, stream):
 
 def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True, backward=True):
     w = W.WORKLOADS[name]
-    if w.dtype == "f32" and w.D != 64:
-        backward = False  # the f32 backward serves D = 64
     if w.backward != backward:  # same q, k, v draws; dO drawn after them
         w = dataclasses.replace(w, backward=backward)
     inp = W.make_inputs(w)

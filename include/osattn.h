@@ -46,9 +46,8 @@
  *    f32); otherwise OSATTN_ERR_ALIGNMENT.
  *  - Row strides: stride_n * element size must be <= 4 MiB for q and k/v
  *    (OSATTN_ERR_UNSUPPORTED otherwise).
- *  - Supported feature widths: d = 64 or 128 for the forward (any dtype);
- *    for the backward d = 64 or 128 with fp16/bf16 and d = 64 with f32.
- *    Other combinations return OSATTN_ERR_UNSUPPORTED.
+ *  - Supported feature widths: d = 64 or 128, forward and backward, every
+ *    dtype.  Other widths return OSATTN_ERR_UNSUPPORTED.
  *  - scale must be finite and > 0 (OSATTN_ERR_UNSUPPORTED otherwise).
  *  - causal != 0 selects j <= i; without cu_seqlens it needs n_q == n_k.
  *  - Varlen: cu_seqlens != NULL selects block-diagonal attention over

@@ -1,4 +1,4 @@
-// Backward attention kernels for gfx950 (f32, feature width 64).
+// Backward attention kernels for gfx950 (f32, feature width 64 or 128).
 //
 // Method: OCANNL "Module Ir.Online_softmax", third rewrite bullet (the fused
 // backward): a per-row D = sum(dO * O), then nests that recompute each pair's
@@ -92,6 +92,22 @@ __device__ __forceinline__ void store_rows_f32(float *rowp, const f32x16 (&acc)[
                        acc[dt][4 * j + 2] * scale, acc[dt][4 * j + 3] * scale};
             *reinterpret_cast<f32x4 *>(rowp + 32 * dt + 8 * j + 4 * g) = v;
         }
+}
+
+// Element (acc_row(r, g) + row0, 32 dt + c32) of a swizzled f32 tile of KCH
+// 16-byte chunks per row, split as rowoff[r & 3] (per lane) + tile_elem (a
+// compile-time constant for unrolled r, dt and row0 a multiple of 8): the
+// swizzle XORs the chunk with row & 7 = 4 g + (r & 3), which leaves the 8 dt
+// part of the chunk and the rows' multiple of 8 untouched.
+template <int KCH>
+__device__ __forceinline__ void lane_row_offsets(int (&rowoff)[4], int c32, int g) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        rowoff[j] = ((4 * g + j) * KCH + ((c32 >> 2) ^ (4 * g + j))) * 4 + (c32 & 3);
+}
+template <int KCH>
+__device__ __forceinline__ constexpr int tile_elem(int row0, int r, int dt) {
+    return ((row0 + 8 * (r >> 2)) * KCH + 8 * dt) * 4;
 }
 
 // ---------------------------------------------------------------- B1
@@ -194,6 +210,8 @@ __global__ void __launch_bounds__(kBThreads, 1) bwd_dkdv32_kernel(BwdParams p) {
     const float *sQf = reinterpret_cast<const float *>(sQ);
     const float *sDOf = reinterpret_cast<const float *>(sDO);
     const int nblk = (qr.hi - qr.lo + kBQ - 1) / kBQ;
+    int rowoff[4];
+    lane_row_offsets<KCH>(rowoff, c32, g);
 
     if (nblk > 0) gload(qr.lo);
     for (int qb = 0; qb < nblk; ++qb) {
@@ -224,14 +242,10 @@ __global__ void __launch_bounds__(kBThreads, 1) bwd_dkdv32_kernel(BwdParams p) {
             }
             // dV^T += dO^T P
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int ql = 32 * qs + acc_row(r, g);
+            for (int r = 0; r < 16; ++r)
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    const int d = 32 * dt + c32;
-                    dV[dt] = mma_f32(sDOf[(ql * KCH + swz(ql, d >> 2)) * 4 + (d & 3)], P[r], dV[dt]);
-                }
-            }
+                for (int dt = 0; dt < NDT; ++dt)
+                    dV[dt] = mma_f32(sDOf[rowoff[r & 3] + tile_elem<KCH>(32 * qs, r, dt)], P[r], dV[dt]);
             // dP = dO V^T
             f32x16 dP = zero_vec<f32x16>();
             const u32x4 *dorow = &sDO[(32 * qs + c32) * KCH];
@@ -247,10 +261,8 @@ __global__ void __launch_bounds__(kBThreads, 1) bwd_dkdv32_kernel(BwdParams p) {
                 const int ql = 32 * qs + acc_row(r, g);
                 const float ds = P[r] * (dP[r] - sDl[ql]);
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    const int d = 32 * dt + c32;
-                    dK[dt] = mma_f32(sQf[(ql * KCH + swz(ql, d >> 2)) * 4 + (d & 3)], ds, dK[dt]);
-                }
+                for (int dt = 0; dt < NDT; ++dt)
+                    dK[dt] = mma_f32(sQf[rowoff[r & 3] + tile_elem<KCH>(32 * qs, r, dt)], ds, dK[dt]);
             }
         }
     }
@@ -348,6 +360,8 @@ __global__ void __launch_bounds__(kBThreads, 1) bwd_dq32_kernel(BwdParams p) {
     const float c = p.scale_log2;
     const float *sKf = reinterpret_cast<const float *>(sK);
     const int nblk = (kr.hi - kr.lo + kBCk - 1) / kBCk;
+    int rowoff[4];
+    lane_row_offsets<KCH>(rowoff, c32, g);
 
     if (nblk > 0) gload(kr.lo);
     for (int kb = 0; kb < nblk; ++kb) {
@@ -382,10 +396,8 @@ __global__ void __launch_bounds__(kBThreads, 1) bwd_dq32_kernel(BwdParams p) {
                 if (kk >= kr.hi || (causal && kk > qrow)) pv = 0.f;
                 const float ds = pv * (dP[r] - dl);
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    const int d = 32 * dt + c32;
-                    dQ[dt] = mma_f32(sKf[(kl * KCH + swz(kl, d >> 2)) * 4 + (d & 3)], ds, dQ[dt]);
-                }
+                for (int dt = 0; dt < NDT; ++dt)
+                    dQ[dt] = mma_f32(sKf[rowoff[r & 3] + tile_elem<KCH>(32 * s, r, dt)], ds, dQ[dt]);
             }
         }
     }
@@ -433,53 +445,63 @@ __global__ void __launch_bounds__(kBThreads) reduce_parts_f32_kernel(Reduce3 q) 
 }
 
 // ------------------------------------------------------------------ launch
-template <int MASK>
+template <int D, int MASK>
 static void launch_bwd_mask(const BwdParams &p, int grid_k, int grid_q, hipStream_t st) {
     if (grid_k > 0)
-        hipLaunchKernelGGL((bwd_dkdv32_kernel<64, MASK>), dim3(grid_k), dim3(kBThreads), 0, st, p);
+        hipLaunchKernelGGL((bwd_dkdv32_kernel<D, MASK>), dim3(grid_k), dim3(kBThreads), 0, st, p);
     if (grid_q > 0)
-        hipLaunchKernelGGL((bwd_dq32_kernel<64, MASK>), dim3(grid_q), dim3(kBThreads), 0, st, p);
+        hipLaunchKernelGGL((bwd_dq32_kernel<D, MASK>), dim3(grid_q), dim3(kBThreads), 0, st, p);
 }
 
 // Adds one reduction to the combined launch.
 static void add_reduce(Reduce3 &q, const float *part, void *out, int64_t sh, int64_t sn, int H,
-                       int n, int splits) {
-    const int64_t grid = ((int64_t)H * n * 64 / 4 + kBThreads - 1) / kBThreads;
+                       int n, int d, int splits) {
+    const int64_t grid = ((int64_t)H * n * d / 4 + kBThreads - 1) / kBThreads;
     if (grid <= 0) return;
     q.r[q.count] = ReduceParams{part, out, sh, sn, H, n, splits};
     q.end[q.count] = (q.count ? q.end[q.count - 1] : 0) + grid;
     ++q.count;
 }
 
+template <int D>
+static void launch_bwd_width(int mask, const BwdParams &p, int grid_k, int grid_q, hipStream_t st) {
+    switch (mask) {
+        case kDense: launch_bwd_mask<D, kDense>(p, grid_k, grid_q, st); break;
+        case kCausal: launch_bwd_mask<D, kCausal>(p, grid_k, grid_q, st); break;
+        case kVarlen: launch_bwd_mask<D, kVarlen>(p, grid_k, grid_q, st); break;
+        default: launch_bwd_mask<D, kVarlenCausal>(p, grid_k, grid_q, st); break;
+    }
+}
+
 // Host entry used by the C ABI (arguments and workspace already validated;
-// p carries the workspace views and the split plan).
-hipError_t launch_backward(int mask, BwdParams p, int seqs, hipStream_t st) {
+// p carries the workspace views and the split plan), d = 64 or 128.
+hipError_t launch_backward(int d, int mask, BwdParams p, int seqs, hipStream_t st) {
     const int64_t rows = (int64_t)p.H * p.n_q;
     const int64_t grid_pre = (rows + (kBThreads / 16) - 1) / (kBThreads / 16);
-    hipLaunchKernelGGL((bwd_pre_kernel<float, 64>), dim3((unsigned)grid_pre), dim3(kBThreads), 0, st, p);
+    if (d == 64)
+        hipLaunchKernelGGL((bwd_pre_kernel<float, 64>), dim3((unsigned)grid_pre), dim3(kBThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL((bwd_pre_kernel<float, 128>), dim3((unsigned)grid_pre), dim3(kBThreads), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t grid_k = (int64_t)p.H * p.k_splits * seqs * p.k_tiles;
     const int64_t grid_q = (int64_t)p.H * p.q_splits * seqs * p.q_tiles;
     if (grid_k > 0x7fffffffLL || grid_q > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    switch (mask) {
-        case kDense: launch_bwd_mask<kDense>(p, (int)grid_k, (int)grid_q, st); break;
-        case kCausal: launch_bwd_mask<kCausal>(p, (int)grid_k, (int)grid_q, st); break;
-        case kVarlen: launch_bwd_mask<kVarlen>(p, (int)grid_k, (int)grid_q, st); break;
-        default: launch_bwd_mask<kVarlenCausal>(p, (int)grid_k, (int)grid_q, st); break;
-    }
+    if (d == 64) launch_bwd_width<64>(mask, p, (int)grid_k, (int)grid_q, st);
+    else launch_bwd_width<128>(mask, p, (int)grid_k, (int)grid_q, st);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     Reduce3 q{};
     if (p.k_splits > 1) {
-        add_reduce(q, p.dk_part, p.dk, p.kv_sh, p.kv_sn, p.H, p.n_k, p.k_splits);
-        add_reduce(q, p.dv_part, p.dv, p.kv_sh, p.kv_sn, p.H, p.n_k, p.k_splits);
+        add_reduce(q, p.dk_part, p.dk, p.kv_sh, p.kv_sn, p.H, p.n_k, d, p.k_splits);
+        add_reduce(q, p.dv_part, p.dv, p.kv_sh, p.kv_sn, p.H, p.n_k, d, p.k_splits);
     }
-    if (p.q_splits > 1) add_reduce(q, p.dq_part, p.dq, p.q_sh, p.q_sn, p.H, p.n_q, p.q_splits);
+    if (p.q_splits > 1) add_reduce(q, p.dq_part, p.dq, p.q_sh, p.q_sn, p.H, p.n_q, d, p.q_splits);
     if (q.count > 0) {
         if (q.end[q.count - 1] > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((reduce_parts_f32_kernel<64>), dim3((unsigned)q.end[q.count - 1]),
-                           dim3(kBThreads), 0, st, q);
+        const dim3 grid((unsigned)q.end[q.count - 1]);
+        if (d == 64) hipLaunchKernelGGL((reduce_parts_f32_kernel<64>), grid, dim3(kBThreads), 0, st, q);
+        else hipLaunchKernelGGL((reduce_parts_f32_kernel<128>), grid, dim3(kBThreads), 0, st, q);
         e = hipGetLastError();
     }
     return e;

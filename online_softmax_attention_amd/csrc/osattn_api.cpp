@@ -14,7 +14,7 @@
 
 namespace osattn {
 hipError_t launch_forward(int dtype, int d, int mask, FwdParams p, int max_seqlen, hipStream_t st);
-hipError_t launch_backward(int mask, BwdParams p, int seqs, hipStream_t st);
+hipError_t launch_backward(int d, int mask, BwdParams p, int seqs, hipStream_t st);
 hipError_t launch_backward16(int dtype, int d, int mask, BwdParams p, int seqs, int sched_shift,
                              hipStream_t st);
 hipError_t launch_forward_pruned(int dtype, int d, FwdParams p, hipStream_t st);
@@ -310,12 +310,9 @@ BwdPlan plan_backward(int dtype, int H, int64_t n_q, int64_t n_k, int d, int cau
     return pl;
 }
 
-int check_bwd_supported(int dtype, int d) {
-    const bool ok = dtype == OSATTN_F32 ? d == 64 : (d == 64 || d == 128);
-    if (!ok)
-        return fail(OSATTN_ERR_UNSUPPORTED,
-                    "backward supports f32 with d = 64 and fp16/bf16 with d = 64 or 128 "
-                    "(got dtype %d, d %d)", dtype, d);
+int check_bwd_supported(int d) {
+    if (d != 64 && d != 128)
+        return fail(OSATTN_ERR_UNSUPPORTED, "backward supports d = 64 or 128 (got %d)", d);
     return OSATTN_OK;
 }
 
@@ -340,7 +337,7 @@ int bwd_check_args(int dtype, int o_dtype, int H, int64_t n_q, int64_t n_k, int 
                    int num_seqs, int max_seqlen, void *dq, void *dk, void *dv) {
     int st = check_common(dtype, H, n_q, n_k, d, scale, causal, cu_seqlens, num_seqs, max_seqlen);
     if (st) return st;
-    if ((st = check_bwd_supported(dtype, d))) return st;
+    if ((st = check_bwd_supported(d))) return st;
     size_t es_o = 4;
     if ((st = check_o_dtype(dtype, o_dtype, &es_o))) return st;
     const size_t es = elem_size(dtype);
@@ -398,7 +395,7 @@ int bwd_launch(int dtype, size_t es_o, int H, int64_t n_q, int64_t n_k, int d, c
         p.sched_max = pl.sched_max;
     }
     const int mk = mask_kind(causal, cu_seqlens);
-    const hipError_t e = dtype == OSATTN_F32 ? launch_backward(mk, p, pl.seqs, hs)
+    const hipError_t e = dtype == OSATTN_F32 ? launch_backward(d, mk, p, pl.seqs, hs)
                                              : launch_backward16(dtype, d, mk, p, pl.seqs,
                                                                  pl.sched_shift, hs);
     if (e != hipSuccess) return fail(OSATTN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
@@ -581,7 +578,7 @@ int osattn_csr_softmax(int dtype, int H, int64_t n_dst, int64_t n_src, int d,
 size_t osattn_bwd_workspace_bytes(int dtype, int H, int64_t n_q, int64_t n_k, int d, int causal,
                                   const int32_t *cu_seqlens, int num_seqs, int max_seqlen) {
     if (check_common(dtype, H, n_q, n_k, d, 1.f, causal, cu_seqlens, num_seqs, max_seqlen)) return 0;
-    if (check_bwd_supported(dtype, d)) return 0;
+    if (check_bwd_supported(d)) return 0;
     return plan_backward(dtype, H, n_q, n_k, d, causal, cu_seqlens, num_seqs, max_seqlen).total;
 }
 

@@ -122,7 +122,8 @@ def bwd(lib, dtype=F32, H=1, n_q=256, n_k=128, d=64, ptrs=None, ws=None, ws_byte
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=F16, d=96), osa.ERR_UNSUPPORTED),
-    (dict(d=128), osa.ERR_UNSUPPORTED),  # f32 backward: d = 64 only
+    (dict(d=32), osa.ERR_UNSUPPORTED),
+    (dict(d=128, ws=None), osa.ERR_WORKSPACE),  # f32 d = 128 passes the width checks
     (dict(ws=None), osa.ERR_WORKSPACE),
     (dict(dtype=F16, ws=None), osa.ERR_WORKSPACE),  # fp16 d = 64 passes the dtype checks
     (dict(dtype=BF16, d=128, ws=None), osa.ERR_WORKSPACE),
@@ -187,7 +188,10 @@ def test_bwd_workspace_bytes(lib):
     assert lib.osattn_bwd_workspace_bytes(F16, 1, 8192, 2048, 64, 0, None, 0, 0) >= 3 * 8192 * 4
     assert lib.osattn_bwd_workspace_bytes(BF16, 1, 8192, 2048, 128, 0, None, 0, 0) >= 3 * 8192 * 4
     assert lib.osattn_bwd_workspace_bytes(F16, 1, 8192, 2048, 96, 0, None, 0, 0) == 0
-    assert lib.osattn_bwd_workspace_bytes(F32, 1, 8192, 2048, 128, 0, None, 0, 0) == 0
+    # f32 at d = 128: the same plan (dK/dV split over queries) with partials twice as wide
+    n128 = lib.osattn_bwd_workspace_bytes(F32, 1, 8192, 2048, 128, 0, None, 0, 0)
+    assert n128 > n and n128 % 256 == 0
+    assert lib.osattn_bwd_workspace_bytes(F32, 1, 8192, 2048, 32, 0, None, 0, 0) == 0
     assert lib.osattn_bwd_workspace_bytes(F32, 0, 8192, 2048, 64, 0, None, 0, 0) == 0
 
 

@@ -329,11 +329,13 @@ BWD_CASES = [
 ]
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal,n_q,n_k,H,lengths", BWD_CASES)
-def test_bwd_parity_f32(osattn, oracle, causal, n_q, n_k, H, lengths):
+def test_bwd_parity_f32(osattn, oracle, D, causal, n_q, n_k, H, lengths):
     if lengths is not None:
         n_q = n_k = sum(lengths)
-    w = small("b", H, n_q, n_k, 64, "f32", causal, 3000 + n_q, lengths=lengths, backward=True)
+    w = small("b", H, n_q, n_k, D, "f32", causal, 3000 + n_q + (D - 64), lengths=lengths,
+              backward=True)
     inp = W.make_inputs(w)
     q, k, v, do = (to_dev(x, "f32") for x in (inp.q, inp.k, inp.v, inp.do))
     cu = cu_dev(inp.cu_seqlens)
@@ -346,7 +348,7 @@ def test_bwd_parity_f32(osattn, oracle, causal, n_q, n_k, H, lengths):
     rdq, rdk, rdv, *_ = oracle.attn_bwd(inp.q32, inp.k32, inp.v32, inp.do32, w.softmax_scale,
                                         causal=causal, cu_seqlens=inp.cu_seqlens)
     for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
-        assert_grad_close(host(g), r, "f32", name)
+        assert_grad_close(host(g), r, "f32", "%s D=%d" % (name, D))
     for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):  # no atomics: bit-identical reruns
         assert torch.equal(a, b)
 
@@ -749,6 +751,7 @@ SHARP_CASES = [
     ("bf16", 128, True, 1024, 2, None), ("bf16", 64, False, 700, 2, None),
     ("f16", 128, False, 513, 2, None), ("f16", 64, True, 0, 4, [300, 1, 700, 129]),
     ("bf16", 128, True, 0, 2, [1000, 37, 400]), ("f32", 64, False, 600, 2, None),
+    ("f32", 128, True, 600, 2, None),
 ]
 
 
@@ -811,7 +814,7 @@ def random_case(idx):
     return dict(dtype=dtype, D=D, causal=mode in ("causal", "varlen_causal"), H=H, n_q=n_q, n_k=n_k,
                 lengths=lengths, scale=D ** -0.5 * fac, layout=r.choice(["hnd", "hnd", "nhd"]),
                 o16=dtype != "f32" and r.random() < 0.3, unsplit=r.random() < 0.25,
-                bwd=(dtype != "f32" or D == 64) and r.random() < 0.6, sharp=sharp)
+                bwd=r.random() < 0.6, sharp=sharp)
 
 
 @pytest.mark.parametrize("idx", range(60))
