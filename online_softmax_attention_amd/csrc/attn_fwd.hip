@@ -898,21 +898,23 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdPara
 // The varlen work list on its own (the fp16/bf16 backward orders its tile pairs
 // with it): the same kernel and key block as the forward of width d.
 // Key block of the 16-bit forward for width d and NW waves per workgroup.
-// ------------------------------------------------ 64-row waves at D = 128
-// The 128-row tile at D = 128 (dense and causal relations), run by 4 waves,
-// one per SIMD: wave w serves rows 64 (w % 2) .. +64 of the tile (two 32-row
-// halves qh) and key group w / 2, i.e. keys [64 kg, 64 kg + 64) of every
-// 128-key block, as two 32-key chunks.  Every K or V operand read from LDS
-// feeds the MFMAs of both row halves, so the LDS bytes per MFMA are half those
-// of a 32-row wave: with 16-byte operand reads at one per 32-cycle MFMA the LDS
-// port would otherwise be the bound (about 128 bytes per clock per CU).
+// ------------------------------------------------ pipelined waves at D = 128
+// The 128-row tile at D = 128 (dense and causal relations), run by 8 waves,
+// two per SIMD: wave w serves rows 32 (w % 4) .. +32 of the tile and key group
+// w / 4, i.e. keys [64 kg, 64 kg + 64) of every 128-key block, as two 32-key
+// chunks.
 //
 // Each wave runs a software pipeline over its chunks s = 0, 1, ...: step s
 // computes the softmax of chunk s on the vector ALU while the same wave's
 // MFMAs compute the next chunk's scores S(s+1) and add the previous chunk's
 // P(s-1) V to U.  The three are independent, so the exponentials issue beside
-// the MFMAs, and every operand is read from LDS three reads (six MFMAs) ahead
-// of its use.
+// the MFMAs, and every operand is read from LDS four reads ahead of its use.
+// A wave overlaps its own vector ALU work with its MFMAs, but one wave issues
+// that work at about one instruction per 5 clocks (measured: 16 MFMAs with 8
+// FMAs each take 43 clocks per MFMA in one wave, 32 alone); the second wave of
+// the SIMD fills the issue gaps (two such waves: both MFMA streams at full
+// rate).  The waves of a SIMD that split the phases instead -- one all MFMA,
+// the other all vector ALU -- do not overlap at all (77 clocks per pair).
 //
 // K and V blocks use separate two-slot rings.  K(b) is read by the score
 // MFMAs of steps 2b-1 and 2b, V(b) by the P.V MFMAs of steps 2b+1 and 2b+2.
@@ -937,13 +939,20 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdPara
 // workgroup recomputes the tile with each row's exact maximum as its reference,
 // found first by a pass of score MFMAs alone.  The two key groups of a row
 // merge through LDS at the end.
+//
+// The steps below are written for RH 32-row halves per wave, RH = 1.  With
+// RH = 2 (4 waves, one per SIMD, 64 rows each) every K or V operand read feeds
+// two MFMAs, half the LDS bytes per MFMA, but the one wave per SIMD issues all
+// of the vector ALU work: 3-5 % slower (causal N=4096 H=16 bf16 77.0 against
+// 73.9 us).
 struct Wide128 {
-    static constexpr int D = 128, NW = 4, BC = 128, ROW = 256, KH = 64;
+    static constexpr int D = 128, BC = 128, ROW = 256, KH = 64, RH = 1;
+    static constexpr int NW = 8 / RH, RGN = NW / 2;   // waves; row groups (x 2 key groups)
     static constexpr int KT = BC * ROW;  // bytes of one K (or V) block
     static constexpr int KS0 = 0, KS1 = KT, VS0 = 2 * KT, VS1 = 3 * KT;  // LDS slots
     static constexpr int NDMA = KT / (64 * NW * 16);  // 16-byte copies per lane per block
-    static constexpr int STATS = 4 * KT;                // merge statistics, 4 KiB
-    static constexpr int FLAG = STATS + 4096;           // recompute flag
+    static constexpr int STATS = 4 * KT;                // merge statistics, 8 KiB
+    static constexpr int FLAG = STATS + 8192;           // recompute flag
     static constexpr int LDS = FLAG + 16;
     // largest (m_true - m_ref) c kept on this path, by input type
     template <typename T> static constexpr float kRefLog2 = std::is_same<T, _Float16>::value ? 15.f : 64.f;
@@ -955,21 +964,144 @@ struct Wide128 {
 // always succeeds.  kv_lo is a multiple of 128 and, for the causal relation,
 // the tile starts at a multiple of 128 with kv_lo = 0, so only the last block
 // can cross the diagonal or the tail.
+// The key groups' merge of a tile whose waves own 32 rows each (8 waves):
+// wave (rg, kg) finalizes the feature tiles 2 kg and 2 kg + 1 of its rows.  It
+// hands its other two tiles, and per row m_ref, m_true and l, to its partner
+// (rg, 1 - kg) through region (rg, 1 - kg) of the merge buffer (8 KiB each)
+// and takes the partner's from region (rg, kg), which it then reuses to turn
+// its O tiles into whole-row stores.  Returns false (nothing written) when a
+// wave raised the recompute flag.
+template <typename T, bool O16>
+__device__ __forceinline__ bool wide_merge_rows32(const FwdParams &p, char *mbuf, char *stats,
+                                                  int *flag, int h, int q_hi, int split,
+                                                  int wrow_lo, int rg, int kg, int lane,
+                                                  f32x16 (&U)[4], float m_ref, float m_true,
+                                                  float l_tot, float c) {
+    constexpr int D = 128;
+    const int c32 = lane & 31, g = lane >> 5;
+    f32x4 *give = reinterpret_cast<f32x4 *>(mbuf) + (rg * 2 + 1 - kg) * 8 * 64 + lane;
+    const f32x4 *take = reinterpret_cast<const f32x4 *>(mbuf) + (rg * 2 + kg) * 8 * 64 + lane;
+    f32x4 *sb = reinterpret_cast<f32x4 *>(stats) + lane;
+    const auto hand = [&](auto d0c) {
+        constexpr int d0 = decltype(d0c)::value;
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 val = {U[d0 + t2][4 * j], U[d0 + t2][4 * j + 1], U[d0 + t2][4 * j + 2],
+                                   U[d0 + t2][4 * j + 3]};
+                give[(t2 * 4 + j) * 64] = val;
+            }
+    };
+    if (kg == 0) hand(std::integral_constant<int, 2>{});
+    else hand(std::integral_constant<int, 0>{});
+    const f32x4 mine = {m_ref, m_true, l_tot, 0.f};
+    sb[(rg * 2 + kg) * 64] = mine;
+    wait_lgkmcnt0();
+    bare_barrier();
+    if (*flag) {
+        bare_barrier();  // every wave has read the flag before the LDS is reused
+        return false;
+    }
+    const f32x4 st = sb[(rg * 2 + 1 - kg) * 64];
+    const float M = vmax(m_ref, st[0]);
+    const float a0 = fast_exp2((m_ref - M) * c), a1 = fast_exp2((st[0] - M) * c);
+    const float lt = l_tot * a0 + st[2] * a1;
+    const float mt = vmax(m_true, st[1]);
+    const int qrow = wrow_lo + c32;
+    const auto finish = [&](auto d0c) {
+        constexpr int d0 = decltype(d0c)::value;
+        if (split >= 0) {
+            if (qrow >= q_hi) return;
+            float *prow = p.part + (((int64_t)split * p.H + h) * p.n_q + qrow) * (D + 4);
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 u1 = take[(t2 * 4 + j) * 64];
+                    f32x4 val;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) val[e] = U[d0 + t2][4 * j + e] * a0 + u1[e] * a1;
+                    *reinterpret_cast<f32x4 *>(prow + 32 * (d0 + t2) + 8 * j + 4 * g) = val;
+                }
+            if (kg == 0 && g == 0) {
+                const f32x4 stv = {M, mt, lt, 0.f};
+                *reinterpret_cast<f32x4 *>(prow + D) = stv;
+            }
+            return;
+        }
+        const float b0 = a0 / lt, b1 = a1 / lt;
+        f32x4 val[2][4];
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 u1 = take[(t2 * 4 + j) * 64];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) val[t2][j][e] = U[d0 + t2][4 * j + e] * b0 + u1[e] * b1;
+            }
+        if (kg == 0 && g == 0 && qrow < q_hi) {
+            p.m[(int64_t)h * p.n_q + qrow] = mt * p.scale;
+            p.l[(int64_t)h * p.n_q + qrow] = lt * fast_exp2((M - mt) * c);
+        }
+        // Row c32 of the region: 16 chunks of 4 features (this wave's 64),
+        // chunk 8 t2 + 2 j + g at (chunk ^ (row & 15)).
+        wait_lgkmcnt0();  // every read of the region has returned
+        f32x4 *obuf = reinterpret_cast<f32x4 *>(mbuf) + (rg * 2 + kg) * 8 * 64;
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) obuf[c32 * 16 + ((8 * t2 + 2 * j + g) ^ (c32 & 15))] = val[t2][j];
+        wait_lgkmcnt0();
+        if constexpr (O16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {  // 8 rows of 8 chunks of 8 values
+                const int r = 8 * i + (lane >> 3), c8 = lane & 7;
+                const f32x4 lo = obuf[r * 16 + ((2 * c8) ^ (r & 15))];
+                const f32x4 hi = obuf[r * 16 + ((2 * c8 + 1) ^ (r & 15))];
+                if (wrow_lo + r < q_hi) {
+                    T *dst = static_cast<T *>(p.o) + (int64_t)h * p.o_sh + (int64_t)(wrow_lo + r) * p.o_sn +
+                             64 * kg + 8 * c8;
+                    store4_16(dst, lo);
+                    store4_16(dst + 4, hi);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {  // 4 rows of 16 chunks of 4 values
+                const int r = 4 * i + (lane >> 4), ch = lane & 15;
+                const f32x4 v4 = obuf[r * 16 + (ch ^ (r & 15))];
+                if (wrow_lo + r < q_hi)
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + (int64_t)h * p.o_sh +
+                                               (int64_t)(wrow_lo + r) * p.o_sn + 64 * kg + 4 * ch) = v4;
+            }
+        }
+    };
+    if (kg == 0) finish(std::integral_constant<int, 0>{});
+    else finish(std::integral_constant<int, 2>{});
+    // The next tile's copies reuse the slots: a barrier without a memory
+    // fence (the stores above need not have landed; every LDS read here has).
+    wait_lgkmcnt0();
+    bare_barrier();
+    return true;
+}
+
 template <typename T, int MASK, bool O16>
 __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, int h, int q_lo,
                                               int q_hi, int kv_lo, int kv_hi, int split,
                                               bool exact_ref) {
     typedef Wide128 C;
+    constexpr int RH = C::RH;
     typedef typename Half8<T>::vec vec8;
     constexpr bool causal = MASK == kCausal;
     constexpr int D = C::D, NDT = D / 32, NKK = D / 16, esz = (int)sizeof(T);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rg = wave & 1, kg = wave >> 1;  // 64-row group, key group
+    const int rg = wave % C::RGN, kg = wave / C::RGN;  // row group of 32 RH rows, key group
     const int c32 = lane & 31, g = lane >> 5;
     const float c = p.scale_log2;
     const int nblk = (kv_hi - kv_lo + C::BC - 1) / C::BC;
-    const int wrow_lo = q_lo + 64 * rg;
+    const int wrow_lo = q_lo + 32 * RH * rg;
 
     const T *kh = static_cast<const T *>(p.k) + (int64_t)h * p.kv_sh;
     const T *vh = static_cast<const T *>(p.v) + (int64_t)h * p.kv_sh;
@@ -997,38 +1129,42 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
         for (int i = 0; i < C::NDMA; ++i) copy_one(r, slot, goff, i);
     };
 
-    // F0: this lane's two query rows (one per half) as B operands (zero past
-    // the tile end).
+    // F0: this lane's query rows (one per half) as B operands (zero past the
+    // tile end).
     copy(kh, 0, C::KS0, k_goff);
     const T *qb = static_cast<const T *>(p.q) + (int64_t)h * p.q_sh + (int64_t)q_lo * p.q_sn;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (int64_t)(q_hi - q_lo) * p.q_sn * esz);
-    vec8 qreg[2][NKK];
+    vec8 qreg[RH][NKK];
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh)
+    for (int qh = 0; qh < RH; ++qh)
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk)
             qreg[qh][kk] = __builtin_bit_cast(
-                vec8, bload16(rq, ((64 * rg + 32 * qh + c32) * (int)p.q_sn + 16 * kk + 8 * g) * esz));
+                vec8, bload16(rq, ((32 * RH * rg + 32 * qh + c32) * (int)p.q_sn + 16 * kk + 8 * g) * esz));
     if (tid == 0) *reinterpret_cast<int *>(smem + C::FLAG) = 0;  // read after the merge barrier
     wait_vmcnt<0>();  // Q and K(0)
-    float m_init[2] = {kNegInf, kNegInf};
+    float m_init[RH];
+#pragma unroll
+    for (int qh = 0; qh < RH; ++qh) m_init[qh] = kNegInf;
     if (exact_ref) {
         // F2-F4 alone: each row's exact maximum over its admitted keys, from
         // the same MFMA products (K read straight from memory in the A
         // operand layout) as the pass below computes.
         for (int k0 = kv_lo; k0 < kv_hi; k0 += 32) {
-            if (causal && k0 > wrow_lo + 63) break;
+            if (causal && k0 > wrow_lo + 32 * RH - 1) break;
             const __amdgpu_buffer_rsrc_t rk =
                 make_rsrc(kh + (int64_t)k0 * p.kv_sn, (int64_t)(kv_hi - k0) * rowb);
-            f32x16 S[2] = {zero_vec<f32x16>(), zero_vec<f32x16>()};
+            f32x16 S[RH];
+#pragma unroll
+            for (int qh = 0; qh < RH; ++qh) S[qh] = zero_vec<f32x16>();
 #pragma unroll
             for (int kk = 0; kk < NKK; ++kk) {
                 const vec8 a = __builtin_bit_cast(vec8, bload16(rk, c32 * rowb + (16 * kk + 8 * g) * esz));
 #pragma unroll
-                for (int qh = 0; qh < 2; ++qh) S[qh] = Half8<T>::mma(a, qreg[qh][kk], S[qh]);
+                for (int qh = 0; qh < RH; ++qh) S[qh] = Half8<T>::mma(a, qreg[qh][kk], S[qh]);
             }
 #pragma unroll
-            for (int qh = 0; qh < 2; ++qh) {
+            for (int qh = 0; qh < RH; ++qh) {
                 f32x16 Sm[1] = {S[qh]};
                 mask_block<1, causal>(Sm, k0, g, kv_hi, wrow_lo + 32 * qh + c32);
                 float mx = kNegInf;
@@ -1066,25 +1202,32 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
         return __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
-    f32x16 U[2][NDT];
+    f32x16 U[RH][NDT];
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh)
+    for (int qh = 0; qh < RH; ++qh)
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) U[qh][dt] = zero_vec<f32x16>();
-    float m_ref[2] = {0.f, 0.f}, m_true[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
-    float mc[2] = {0.f, 0.f}, thr[2] = {0.f, 0.f};
+    float m_ref[RH], m_true[RH], l_run[RH], mc[RH], thr[RH];
+#pragma unroll
+    for (int qh = 0; qh < RH; ++qh) {
+        m_ref[qh] = 0.f;
+        m_true[qh] = kNegInf;
+        l_run[qh] = 0.f;
+        mc[qh] = 0.f;
+        thr[qh] = 0.f;
+    }
     bool bail = false;
-    f32x16 SA[2], SB[2];
-    vec8 PA[2][2], PB[2][2];
+    f32x16 SA[RH], SB[RH];
+    vec8 PA[RH][2], PB[RH][2];
 
     bare_barrier();  // every wave's part of K(0) has landed
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh) SA[qh] = zero_vec<f32x16>();
+    for (int qh = 0; qh < RH; ++qh) SA[qh] = zero_vec<f32x16>();
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
         const vec8 a = kread(kk, 0);
 #pragma unroll
-        for (int qh = 0; qh < 2; ++qh) SA[qh] = Half8<T>::mma(a, qreg[qh][kk], SA[qh]);
+        for (int qh = 0; qh < RH; ++qh) SA[qh] = Half8<T>::mma(a, qreg[qh][kk], SA[qh]);
     }
 
     // One pipeline step; its parity fixes the buffers and the 32-key chunk of
@@ -1095,8 +1238,8 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
     // (Sc, Pc): chunk s's scores and probabilities; Sn receives S(s+1); Pp
     // holds P(s-1).  Even steps use (SA, PA), odd ones (SB, PB).
     const auto step_body = [&](auto ODDc, auto HSc, auto HPc, auto MKc, auto CKc, auto CVc,
-                               auto FIRSTc, int s, f32x16 (&Sc)[2], f32x16 (&Sn)[2],
-                               vec8 (&Pc)[2][2], vec8 (&Pp)[2][2]) {
+                               auto FIRSTc, int s, f32x16 (&Sc)[RH], f32x16 (&Sn)[RH],
+                               vec8 (&Pc)[RH][2], vec8 (&Pp)[RH][2]) {
         constexpr bool ODD = decltype(ODDc)::value, HS = decltype(HSc)::value;
         constexpr bool HP = decltype(HPc)::value, MK = decltype(MKc)::value;
         constexpr bool CK = decltype(CKc)::value, CV = decltype(CVc)::value;
@@ -1128,7 +1271,7 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
         if constexpr (MK) {  // F3: chunks that cross the tail or the diagonal
             const int kc0 = kv_lo + (s >> 1) * C::BC + C::KH * kg + 32 * (s & 1);
 #pragma unroll
-            for (int qh = 0; qh < 2; ++qh) {
+            for (int qh = 0; qh < RH; ++qh) {
                 const int r_lo = wrow_lo + 32 * qh;
                 if (kc0 + 32 > kv_hi || (causal && kc0 + 31 > r_lo)) {
                     f32x16 Sm[1] = {Sc[qh]};
@@ -1137,15 +1280,15 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
                 }
             }
         }
-        // The step's MFMAs in issue order: operand read j feeds MFMAs 2j and
-        // 2j+1 (row halves 0 and 1).  The reads for S(s+1) come first (K, 16
+        // The step's MFMAs in issue order: operand read j feeds MFMAs RH j ..
+        // RH j + RH - 1 (one per row half).  The reads for S(s+1) come first (K, 16
         // features kk per read), so that S(s+1) is complete long before the
         // next step reads it, then those for P(s-1) V (V, 32 features dt,
         // 16-key half hf).  Even slot 2j issues read j + FD; every slot then
         // issues its MFMA and its share of the softmax; a scheduling fence
         // after each slot keeps that order (it bounds the operands in flight).
         constexpr int NRD = (HS ? 8 : 0) + (HP ? 8 : 0);  // operand reads
-        constexpr int FD = 3;                             // reads in flight ahead of use
+        constexpr int FD = 4;                             // reads in flight ahead of use
         // read code: 0..7 = K with kk, 8 + 4 hf + dt = V of (dt, hf)
         constexpr auto rdc = [](int j) { return HS ? j : 8 + j; };
         vec8 opnd[FD + 1];
@@ -1158,7 +1301,7 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
             }
         };
         const auto mma = [&](auto ic) {
-            constexpr int i = decltype(ic)::value, j = i >> 1, qh = i & 1;
+            constexpr int i = decltype(ic)::value, j = i / RH, qh = i % RH;
             if constexpr (j < NRD) {
                 constexpr int o = rdc(j);
                 if constexpr (o < 8)
@@ -1172,15 +1315,15 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
             if constexpr (ODD && CK && i < C::NDMA) copy_one(rk, ksl, kgo, i);
             if constexpr (ODD && CV && i >= C::NDMA && i < 2 * C::NDMA) copy_one(rv, vsl, vgo, i - C::NDMA);
         };
-        float t[2][4], ps[2][4], y[2][16];
-        f32x8 x[2][2];
-        // Softmax of chunk s in slot-sized pieces, slot i taking piece i / 2
-        // of row half i % 2: F4 (chunk maximum; on step 0 it becomes the
+        float t[RH][4], ps[RH][4], y[RH][16];
+        f32x8 x[RH][2];
+        // Softmax of chunk s in slot-sized pieces, slot i taking piece i / RH
+        // of row half i % RH: F4 (chunk maximum; on step 0 it becomes the
         // reference), then F5 (probabilities: f32 into l, rounded to T as the
         // P.V operand).  Each exponential is taken one piece after the
         // multiply-add that forms its argument.
         const auto valu = [&](auto ic) {
-            constexpr int i = decltype(ic)::value, qh = i & 1, pc = i >> 1;
+            constexpr int i = decltype(ic)::value, qh = i % RH, pc = i / RH;
             const f32x16 &S = Sc[qh];
             if constexpr (pc == 0) {
                 t[qh][0] = vmax(vmax(S[0], S[1]), vmax(S[2], S[3]));
@@ -1226,14 +1369,14 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
         };
         const auto slot = [&](auto ic) {
             constexpr int i = decltype(ic)::value;
-            if constexpr ((i & 1) == 0) fetch(std::integral_constant<int, (i >> 1) + FD>{});
+            if constexpr (i % RH == 0) fetch(std::integral_constant<int, i / RH + FD>{});
             dma(ic);
             mma(ic);
             valu(ic);
             __builtin_amdgcn_sched_barrier(0);
         };
         for_each_index(fetch, std::make_integer_sequence<int, FD>{});
-        for_each_index(slot, std::make_integer_sequence<int, 32>{});
+        for_each_index(slot, std::make_integer_sequence<int, 16 * RH>{});
     };
     using Y = std::true_type;
     using N = std::false_type;
@@ -1285,128 +1428,19 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
         for (int dt = 0; dt < NDT; ++dt) {
             const vec8 a = vread(dt, 8192 + 4096 * hf);
 #pragma unroll
-            for (int qh = 0; qh < 2; ++qh) U[qh][dt] = Half8<T>::mma(a, PB[qh][hf], U[qh][dt]);
+            for (int qh = 0; qh < RH; ++qh) U[qh][dt] = Half8<T>::mma(a, PB[qh][hf], U[qh][dt]);
         }
     // F7: merge the two key groups of each row through LDS, into the K
     // slots: every wave finished its K reads before the last odd step's
-    // barrier.  Wave (rg, kg) finalizes row half qh = kg of its 64 rows; it
-    // hands its partial state of the other half (U, and per row m_ref,
-    // m_true, l) to its partner (rg, 1 - kg) and takes the partner's of its
-    // own.  A wave that saw a row exceed the reference bound raises the flag
-    // before the same barrier, and then every wave hands the tile back.
-    float l_tot[2];
+    // barrier.  A wave that saw a row exceed the reference bound raises the
+    // flag before the merge barrier, and then every wave hands the tile back.
+    float l_tot[RH];
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh) l_tot[qh] = xor32_sum(l_run[qh]);  // the lane halves' keys
+    for (int qh = 0; qh < RH; ++qh) l_tot[qh] = xor32_sum(l_run[qh]);  // the lane halves' keys
     int *flag = reinterpret_cast<int *>(smem + C::FLAG);
     if (__any(bail) && lane == 0) *flag = 1;
-    const int give = 1 - kg;  // row half handed to the partner
-    f32x4 *ubuf = reinterpret_cast<f32x4 *>(smem + C::KS0) + (rg * 2) * 16 * 64 + lane;
-    f32x4 *sbuf = reinterpret_cast<f32x4 *>(smem + C::STATS) + (rg * 2) * 64 + lane;
-    const auto give_half = [&](auto qhc) {
-        constexpr int qh = decltype(qhc)::value;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const f32x4 val = {U[qh][dt][4 * j], U[qh][dt][4 * j + 1], U[qh][dt][4 * j + 2],
-                                   U[qh][dt][4 * j + 3]};
-                ubuf[(qh * 16 + dt * 4 + j) * 64] = val;
-            }
-        const f32x4 st = {m_ref[qh], m_true[qh], l_tot[qh], 0.f};
-        sbuf[qh * 64] = st;
-    };
-    if (give == 0) give_half(std::integral_constant<int, 0>{});
-    else give_half(std::integral_constant<int, 1>{});
-    wait_lgkmcnt0();
-    bare_barrier();
-    if (*flag) {
-        bare_barrier();  // every wave has read the flag before the LDS is reused
-        return false;
-    }
-    const auto finish_half = [&](auto qhc) {
-        constexpr int qh = decltype(qhc)::value;
-        const f32x4 st = sbuf[qh * 64];
-        const float M = vmax(m_ref[qh], st[0]);
-        const float a0 = fast_exp2((m_ref[qh] - M) * c), a1 = fast_exp2((st[0] - M) * c);
-        const float lt = l_tot[qh] * a0 + st[2] * a1;
-        const float mt = vmax(m_true[qh], st[1]);
-        const int qrow = wrow_lo + 32 * qh + c32;
-        if (split >= 0) {
-            if (qrow >= q_hi) return;
-            float *prow = p.part + (((int64_t)split * p.H + h) * p.n_q + qrow) * (D + 4);
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const f32x4 u1 = ubuf[(qh * 16 + dt * 4 + j) * 64];
-                    f32x4 val;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) val[e] = U[qh][dt][4 * j + e] * a0 + u1[e] * a1;
-                    *reinterpret_cast<f32x4 *>(prow + 32 * dt + 8 * j + 4 * g) = val;
-                }
-            if (g == 0) {
-                const f32x4 stv = {M, mt, lt, 0.f};
-                *reinterpret_cast<f32x4 *>(prow + D) = stv;
-            }
-        } else {
-            // O rows go through this wave's own 16 KiB of the merge buffer
-            // (already read above) so that each store covers whole rows: row
-            // c32 of the half, 16-byte chunk 8 dt + 2 j + g, swizzled with
-            // the row's low four bits (16 lanes that write one chunk of 16
-            // rows, or read 16 chunks of one row, hit 16 distinct bank groups).
-            const float b0 = a0 / lt, b1 = a1 / lt;
-            f32x4 val[NDT][4];
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const f32x4 u1 = ubuf[(qh * 16 + dt * 4 + j) * 64];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) val[dt][j][e] = U[qh][dt][4 * j + e] * b0 + u1[e] * b1;
-                }
-            if (g == 0 && qrow < q_hi) {
-                p.m[(int64_t)h * p.n_q + qrow] = mt * p.scale;
-                p.l[(int64_t)h * p.n_q + qrow] = lt * fast_exp2((M - mt) * c);
-            }
-            wait_lgkmcnt0();  // every read of the region has returned
-            f32x4 *obuf = reinterpret_cast<f32x4 *>(smem + C::KS0) + (rg * 2 + qh) * 16 * 64;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) obuf[c32 * 32 + ((8 * dt + 2 * j + g) ^ (c32 & 15))] = val[dt][j];
-            wait_lgkmcnt0();
-            const int row0 = wrow_lo + 32 * qh;
-            if constexpr (O16) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {  // 4 rows of 16 chunks of 8 values
-                    const int r = 4 * i + (lane >> 4), c8 = lane & 15;
-                    const f32x4 lo = obuf[r * 32 + ((2 * c8) ^ (r & 15))];
-                    const f32x4 hi = obuf[r * 32 + ((2 * c8 + 1) ^ (r & 15))];
-                    if (row0 + r < q_hi) {
-                        T *dst = static_cast<T *>(p.o) + (int64_t)h * p.o_sh + (int64_t)(row0 + r) * p.o_sn + 8 * c8;
-                        store4_16(dst, lo);
-                        store4_16(dst + 4, hi);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {  // 2 rows of 32 chunks of 4 values
-                    const int r = 2 * i + (lane >> 5), ch = lane & 31;
-                    const f32x4 v4 = obuf[r * 32 + (ch ^ (r & 15))];
-                    if (row0 + r < q_hi)
-                        *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + (int64_t)h * p.o_sh +
-                                                   (int64_t)(row0 + r) * p.o_sn + 4 * ch) = v4;
-                }
-            }
-        }
-    };
-    if (kg == 0) finish_half(std::integral_constant<int, 0>{});
-    else finish_half(std::integral_constant<int, 1>{});
-    // The next tile's copies reuse the slots: a barrier without a memory
-    // fence (the stores above need not have landed; every LDS read here has).
-    wait_lgkmcnt0();
-    bare_barrier();
-    return true;
+    return wide_merge_rows32<T, O16>(p, smem + C::KS0, smem + C::STATS, flag, h, q_hi, split, wrow_lo,
+                                     rg, kg, lane, U[0], m_ref[0], m_true[0], l_tot[0], c);
 }
 
 // A tile the wide routine hands back is run again with exact references (one
@@ -1420,11 +1454,11 @@ __device__ __forceinline__ void fwd_wide_or_retry(const FwdParams &p, char *smem
 }
 
 // The dense and causal 16-bit forward at D = 128 with 128-row tiles: one
-// workgroup of 4 waves per CU.  Work items as in fwd16_kernel: split-KV items
+// workgroup of 8 waves per CU.  Work items as in fwd16_kernel: split-KV items
 // (dense), causal tile pairs (T-1-i, i) or single tiles heaviest first, dense
 // tiles.
 template <typename T, int MASK, bool O16>
-__global__ void __launch_bounds__(256, 1) fwd_wide_kernel(FwdParams p) {
+__global__ void __launch_bounds__(64 * Wide128::NW, 1) fwd_wide_kernel(FwdParams p) {
     constexpr bool causal = MASK == kCausal;
     __shared__ __attribute__((aligned(16))) char smem[Wide128::LDS];
     const int b = blockIdx.x;
@@ -1917,8 +1951,8 @@ template <typename T, int D, int MASK, bool O16>
 static void launch_fwd16_o(const FwdParams &p, int grid, hipStream_t st) {
     const dim3 g(grid), b(kT16);
     if constexpr (D == 128 && (MASK == kDense || MASK == kCausal)) {
-        if (p.tile_rows == kBR) {  // 64-row waves, one workgroup per CU
-            hipLaunchKernelGGL((fwd_wide_kernel<T, MASK, O16>), g, dim3(256), 0, st, p);
+        if (p.tile_rows == kBR) {  // 8 waves of 32 rows, one workgroup per CU
+            hipLaunchKernelGGL((fwd_wide_kernel<T, MASK, O16>), g, dim3(64 * Wide128::NW), 0, st, p);
             return;
         }
     }
