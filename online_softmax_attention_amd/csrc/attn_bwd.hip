@@ -412,22 +412,14 @@ __global__ void __launch_bounds__(kBThreads, 1) bwd_dq32_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- reduce
-// Up to three split reductions (dK, dV, dQ) in one launch: workgroup b serves
-// reduction k while b < end[k].  Each thread sums one float4 of its output over
-// the splits in a fixed order (deterministic), four loads in flight.
-struct Reduce3 {
-    ReduceParams r[3];
-    int64_t end[3];  // cumulative workgroup counts
-    int count;
-};
+// Up to three split reductions (dK, dV, dQ) in one launch (Reduce3): each
+// thread sums one float4 of its output over the splits in a fixed order
+// (deterministic), eight loads in flight.
 
 template <int D>
 __global__ void __launch_bounds__(kBThreads) reduce_parts_f32_kernel(Reduce3 q) {
-    int k = 0;
     int64_t b = blockIdx.x;
-    while (k + 1 < q.count && b >= q.end[k]) ++k;
-    if (k > 0) b -= q.end[k - 1];
-    const ReduceParams &r = q.r[k];
+    const ReduceParams &r = q.r[q.which(b)];
     const int64_t total4 = (int64_t)r.H * r.n * D / 4;
     const int64_t i4 = (int64_t)b * kBThreads + threadIdx.x;
     if (i4 >= total4) return;

@@ -610,11 +610,15 @@ __global__ void __launch_bounds__(kB16T) bwd16_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- reduce
+// Up to three split reductions in one launch (Reduce3), each thread one float4
+// of its output summed over the splits in a fixed order, rounded once.
 template <typename T, int D>
-__global__ void __launch_bounds__(256) bwd16_reduce_kernel(ReduceParams r) {
+__global__ void __launch_bounds__(256) bwd16_reduce_kernel(Reduce3 q) {
     typedef T t4 __attribute__((ext_vector_type(4)));
+    int64_t b = blockIdx.x;
+    const ReduceParams &r = q.r[q.which(b)];
     const int64_t total4 = (int64_t)r.H * r.n * D / 4;
-    const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t i4 = b * 256 + threadIdx.x;
     if (i4 >= total4) return;
     const int64_t e = i4 * 4;
     const int64_t plane = (int64_t)r.n * D;
@@ -623,6 +627,7 @@ __global__ void __launch_bounds__(256) bwd16_reduce_kernel(ReduceParams r) {
     const int i = (int)(rem / D), d = (int)(rem % D);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const int64_t stride = (int64_t)r.H * plane;
+#pragma unroll 8
     for (int s = 0; s < r.splits; ++s) acc += *reinterpret_cast<const f32x4 *>(r.part + s * stride + e);
     *reinterpret_cast<t4 *>(static_cast<T *>(r.out) + (int64_t)h * r.out_sh + (int64_t)i * r.out_sn + d) =
         __builtin_convertvector(acc, t4);
@@ -663,16 +668,24 @@ static hipError_t launch_bwd16_typed(int mask, const BwdParams &p, int seqs, hip
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    auto reduce = [&](const float *part, void *out, int64_t sh, int64_t sn, int n, int splits) {
-        ReduceParams r{part, out, sh, sn, p.H, n, splits};
+    // One launch for every split reduction, not one per gradient.
+    Reduce3 q{};
+    const auto add = [&](const float *part, void *out, int64_t sh, int64_t sn, int n, int splits) {
         const int64_t grid = ((int64_t)p.H * n * D / 4 + 255) / 256;
-        if (grid > 0) hipLaunchKernelGGL((bwd16_reduce_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, st, r);
+        if (grid <= 0) return;
+        q.r[q.count] = ReduceParams{part, out, sh, sn, p.H, n, splits};
+        q.end[q.count] = (q.count ? q.end[q.count - 1] : 0) + grid;
+        ++q.count;
     };
     if (p.k_splits > 1) {
-        reduce(p.dk_part, p.dk, p.kv_sh, p.kv_sn, p.n_k, p.k_splits);
-        reduce(p.dv_part, p.dv, p.kv_sh, p.kv_sn, p.n_k, p.k_splits);
+        add(p.dk_part, p.dk, p.kv_sh, p.kv_sn, p.n_k, p.k_splits);
+        add(p.dv_part, p.dv, p.kv_sh, p.kv_sn, p.n_k, p.k_splits);
     }
-    if (p.q_splits > 1) reduce(p.dq_part, p.dq, p.q_sh, p.q_sn, p.n_q, p.q_splits);
+    if (p.q_splits > 1) add(p.dq_part, p.dq, p.q_sh, p.q_sn, p.n_q, p.q_splits);
+    if (q.count > 0) {
+        if (q.end[q.count - 1] > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((bwd16_reduce_kernel<T, D>), dim3((unsigned)q.end[q.count - 1]), dim3(256), 0, st, q);
+    }
     return hipGetLastError();
 }
 

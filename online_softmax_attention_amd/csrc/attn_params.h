@@ -110,4 +110,19 @@ struct ReduceParams {
     int H, n, splits;
 };
 
+// Up to three split reductions (dK, dV, dQ) in one launch: workgroup b serves
+// reduction k while b < end[k].
+struct Reduce3 {
+    ReduceParams r[3];
+    int64_t end[3];  // cumulative workgroup counts
+    int count;
+    // The reduction of workgroup b; b becomes its index within that reduction.
+    __device__ int which(int64_t &b) const {
+        int k = 0;
+        while (k + 1 < count && b >= end[k]) ++k;
+        if (k > 0) b -= end[k - 1];
+        return k;
+    }
+};
+
 }  // namespace osattn
