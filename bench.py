@@ -94,13 +94,14 @@ BWD_KERNELS = {False: "bwd16_pre+bwd16_kernel+bwd16_reduce",
 
 
 def fwd_kernel_name(w, torch, split: bool) -> str:
-    """The forward kernel the library's plan picks for workload w: D = 128
-    dense / causal 16-bit problems whose 128-row tiles (causal: tile pairs) fill
-    the device, or that split the keys, run the 64-row-wave kernel."""
+    """The forward kernel the library's plan picks for workload w: 16-bit
+    dense / causal problems whose 128-row tiles (causal: tile pairs) fill the
+    device, or that split the keys, and varlen problems whose sequences average
+    2048 rows or more run the 8-wave pipelined kernel; the rest the tiled one."""
     if w.dtype == "f32":
         return "fwd32_kernel"
-    if w.D != 128 or w.lengths:
-        return "fwd16_kernel"
+    if w.lengths:
+        return "fwd_wide_kernel" if w.n_q >= 2048 * len(w.lengths) else "fwd16_kernel"
     if split:
         return "fwd_wide_kernel"
     cus = torch.cuda.get_device_properties(0).multi_processor_count

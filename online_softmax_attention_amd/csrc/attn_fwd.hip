@@ -9,9 +9,13 @@
 // tail whose scores are -inf.  Relations: TIGA-lang "Attention and dense
 // relations" (dense, causal j <= i, varlen block-diagonal with cu_seqlens).
 //
-// Work decomposition (MI355X).  fp16/bf16: a workgroup of 8 or 4 waves owns a tile
-// of 32 RG query rows of one head (RG row groups x 8/RG key groups, 128 rows by
-// default).  Each wave computes the transposed score tile S^T = K Q^T on MFMA so
+// Work decomposition (MI355X).  fp16/bf16: 128-row tiles of dense and causal
+// problems (and of varlen problems of long sequences) run on fwd_wide_kernel,
+// 8 waves per CU, each wave software-pipelined over its key chunks (see
+// there).  The tiled kernel fwd16_kernel takes the rest: a workgroup of 8 or 4
+// waves owns a tile of 32 RG query rows of one head (RG row groups x 8/RG key
+// groups: 64- and 32-row tiles of small grids, and 128-row varlen tiles with
+// two 4-wave workgroups per CU).  Each wave computes the transposed score tile S^T = K Q^T on MFMA so
 // that every lane owns ONE query row: the row maximum and row sum are in-lane
 // reductions plus one exchange between the two lane halves, and the rescale of U
 // is a per-lane multiply.  Q lives in registers for the whole scan; K and V
@@ -31,6 +35,7 @@ namespace osattn {
 
 constexpr int kThreads = 256;
 constexpr int kBR = 128;  // query rows per workgroup
+constexpr int kWideVarlenRows = 2048;  // varlen average rows per sequence for the 8-wave kernel
 
 struct FwdWork {
     int h;
@@ -789,6 +794,65 @@ __global__ void __launch_bounds__(kSchedThreads) varlen_schedule_kernel(FwdParam
     for (int i = count + tid; i < p.sched_max; i += kSchedThreads) items[i] = make_int4(0, 0, -1, -1);
 }
 
+// A varlen work item: sequence rows [lo, hi) and its tiles t0, t1 (t1 < 0:
+// one tile; t0 < 0: no work) of kBR rows.
+struct VarlenItem {
+    int lo, hi, t0, t1;
+};
+
+// Varlen item `rest` of one head: from the sorted work list (p.sched), from a
+// ranking done here (p.sched_inline: up to 64 sequences), or from the natural
+// (sequence, pair) grid.  Uniform across the workgroup: the result is taken
+// into scalar registers.
+__device__ __forceinline__ VarlenItem varlen_item_lanes(const FwdParams &p, int rest);
+__device__ __forceinline__ VarlenItem varlen_item(const FwdParams &p, int rest) {
+    const VarlenItem it = varlen_item_lanes(p, rest);
+    return {__builtin_amdgcn_readfirstlane(it.lo), __builtin_amdgcn_readfirstlane(it.hi),
+            __builtin_amdgcn_readfirstlane(it.t0), __builtin_amdgcn_readfirstlane(it.t1)};
+}
+__device__ __forceinline__ VarlenItem varlen_item_lanes(const FwdParams &p, int rest) {
+    if (p.sched_inline) {
+        // Item `rest` in a list of the tile pairs (T-1-i, i) that takes the
+        // sequences by tile count, most first (ties: lower index first), and
+        // each sequence's pairs in order of i; a pair scans about T + 1 key
+        // blocks, so this is the sorted work list without a separate launch.
+        // Lane s < num_seqs (at most 64) holds sequence s; every wave computes
+        // the same answer.
+        const int lane = threadIdx.x & 63, S = p.num_seqs;
+        int lo = 0, hi = 0;
+        if (lane < S) {
+            const Span sp = seq_bounds(p.cu, lane, p.n_q);
+            lo = sp.lo;
+            hi = sp.hi;
+        }
+        const int nt = (hi - lo + kBR - 1) / kBR, npair = (nt + 1) / 2;
+        const int key = (nt << 6) | (63 - lane);  // distinct per lane; nt < 2^24
+        int before = 0;                          // pairs listed ahead of this sequence's
+        for (int s2 = 0; s2 < S; ++s2) {
+            const int ks = __shfl(key, s2), ns = __shfl(npair, s2);
+            before += ks > key ? ns : 0;
+        }
+        const uint64_t own = __ballot(lane < S && rest >= before && rest < before + npair);
+        if (own == 0) return {0, 0, -1, -1};  // past the last item
+        const int src = __ffsll((unsigned long long)own) - 1;
+        const int s_nt = __shfl(nt, src), i = rest - __shfl(before, src);
+        const int ta = s_nt - 1 - i;
+        return {__shfl(lo, src), __shfl(hi, src), ta, (i == ta) ? -1 : i};
+    }
+    if (p.sched) {  // item `rest` of the sorted work list
+        const int4 it = reinterpret_cast<const int4 *>(p.sched + 4)[rest];
+        return {it.x, it.y, it.z, it.w};
+    }
+    // pair (T-1-i, i) of sequence rest % num_seqs; the grid walks i downwards
+    // from the middle tiles of the longest sequence
+    const Span sq = seq_bounds(p.cu, rest % p.num_seqs, p.n_q);
+    const int ntile = (sq.hi - sq.lo + kBR - 1) / kBR;
+    const int i = (p.n_tiles + 1) / 2 - 1 - rest / p.num_seqs;
+    if (i >= (ntile + 1) / 2) return {0, 0, -1, -1};
+    const int t0 = ntile - 1 - i;
+    return {sq.lo, sq.hi, t0, (i == t0) ? -1 : i};
+}
+
 // NW = 4: two workgroups per CU, so each wave may use at most 256 registers.
 template <typename T, int D, int MASK, int NST, int RG, int NW = 8, bool O16 = false>
 __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdParams p) {
@@ -811,75 +875,29 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdPara
     }
     const int h = b % p.H;
     int rest = b / p.H;
-    if (varlen && p.sched_inline) {
-        // Item `rest` in a list of the tile pairs (T-1-i, i) that takes the
-        // sequences by tile count, most first (ties: lower index first), and
-        // each sequence's pairs in order of i; a pair scans about T + 1 key
-        // blocks, so this is the sorted work list without a separate launch.
-        // Lane s < num_seqs (at most 64) holds sequence s; every wave computes
-        // the same answer.
-        const int lane = threadIdx.x & 63, S = p.num_seqs;
-        int lo = 0, hi = 0;
-        if (lane < S) {
-            const Span sp = seq_bounds(p.cu, lane, p.n_q);
-            lo = sp.lo;
-            hi = sp.hi;
-        }
-        const int nt = (hi - lo + TR - 1) / TR, npair = (nt + 1) / 2;
-        const int key = (nt << 6) | (63 - lane);  // distinct per lane; nt < 2^24
-        int before = 0;                          // pairs listed ahead of this sequence's
-        for (int s2 = 0; s2 < S; ++s2) {
-            const int ks = __shfl(key, s2), ns = __shfl(npair, s2);
-            before += ks > key ? ns : 0;
-        }
-        const uint64_t own = __ballot(lane < S && rest >= before && rest < before + npair);
-        if (own == 0) return;  // past the last item
-        const int src = __ffsll((unsigned long long)own) - 1;
-        const int s_lo = __shfl(lo, src), s_hi = __shfl(hi, src), s_nt = __shfl(nt, src);
-        const int i = rest - __shfl(before, src);
-        const int ta = s_nt - 1 - i, tb = (i == ta) ? -1 : i;
+    if constexpr (varlen) {
+        const VarlenItem it = varlen_item(p, rest);
 #pragma unroll 1
         for (int k = 0; k < 2; ++k) {
-            const int tile = k == 0 ? ta : tb;
+            const int tile = k == 0 ? it.t0 : it.t1;
             if (tile < 0) break;
-            const int q_lo = s_lo + tile * TR, q_hi = min(q_lo + TR, s_hi);
-            fwd16_tile<T, D, MASK, NST, RG, NW, O16>(p, smem, h, q_lo, q_hi, s_lo, causal ? q_hi : s_hi, -1);
-        }
-        return;
-    }
-    if (varlen && p.sched) {  // item `rest` of the sorted work list
-        const int4 it = reinterpret_cast<const int4 *>(p.sched + 4)[rest];
-#pragma unroll 1
-        for (int k = 0; k < 2; ++k) {
-            const int tile = k == 0 ? it.z : it.w;
-            if (tile < 0) break;
-            const int q_lo = it.x + tile * TR, q_hi = min(q_lo + TR, it.y);
+            const int q_lo = it.lo + tile * TR, q_hi = min(q_lo + TR, it.hi);
             if (q_lo >= q_hi) break;
-            fwd16_tile<T, D, MASK, NST, RG, NW, O16>(p, smem, h, q_lo, q_hi, it.x, causal ? q_hi : it.y, -1);
+            fwd16_tile<T, D, MASK, NST, RG, NW, O16>(p, smem, h, q_lo, q_hi, it.lo, causal ? q_hi : it.hi, -1);
         }
         return;
-    }
-    int seq_lo = 0, seq_hi = p.n_q, ntile = p.n_tiles;
-    if (varlen) {
-        const Span s = seq_bounds(p.cu, rest % p.num_seqs, p.n_q);
-        rest /= p.num_seqs;
-        seq_lo = s.lo;
-        seq_hi = s.hi;
-        ntile = (seq_hi - seq_lo + TR - 1) / TR;
     }
     int t0, t1;
-    if (causal && !varlen && !p.pair) {
+    if (causal && !p.pair) {
         // one tile per workgroup, heaviest (last) tiles first: for grids too
         // small to fill the device, where a pair would double the serial work
         t0 = p.n_tiles - 1 - rest;
         t1 = -1;
-    } else if (causal || varlen) {
-        // pair (T-1-i, i): equal work per causal pair; the varlen grid walks
-        // i downwards from the middle tiles of the longest sequence
-        const int pairs_max = (p.n_tiles + 1) / 2;
-        const int i = varlen ? pairs_max - 1 - rest : rest;
-        if (i >= (ntile + 1) / 2) return;
-        t0 = ntile - 1 - i;
+    } else if (causal) {
+        // pair (T-1-i, i): equal work per causal pair
+        const int i = rest;
+        if (i >= (p.n_tiles + 1) / 2) return;
+        t0 = p.n_tiles - 1 - i;
         t1 = (i == t0) ? -1 : i;
     } else {
         t0 = rest;
@@ -889,9 +907,8 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdPara
     for (int k = 0; k < 2; ++k) {
         const int tile = k == 0 ? t0 : t1;
         if (tile < 0) break;
-        const int q_lo = seq_lo + tile * TR, q_hi = min(q_lo + TR, seq_hi);
-        const int kv_hi = causal ? q_hi : (varlen ? seq_hi : p.n_k);
-        fwd16_tile<T, D, MASK, NST, RG, NW, O16>(p, smem, h, q_lo, q_hi, seq_lo, kv_hi, -1);
+        const int q_lo = tile * TR, q_hi = min(q_lo + TR, p.n_q);
+        fwd16_tile<T, D, MASK, NST, RG, NW, O16>(p, smem, h, q_lo, q_hi, 0, causal ? q_hi : p.n_k, -1);
     }
 }
 
@@ -945,9 +962,13 @@ __global__ void __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) fwd16_kernel(FwdPara
 // two MFMAs, half the LDS bytes per MFMA, but the one wave per SIMD issues all
 // of the vector ALU work: 3-5 % slower (causal N=4096 H=16 bf16 77.0 against
 // 73.9 us).
-struct Wide128 {
-    static constexpr int D = 128, BC = 128, ROW = 256, KH = 64, RH = 1;
+template <int D_>
+struct WideCfg {
+    static constexpr int D = D_, BC = 128, ROW = 2 * D, KH = 64, RH = 1;
     static constexpr int NW = 8 / RH, RGN = NW / 2;   // waves; row groups (x 2 key groups)
+    static constexpr int NKK = D / 16, NDT = D / 32;  // 16-feature slices, 32-feature tiles
+    static constexpr int RPK = 1024 / ROW, CPR = ROW / 16;  // rows per KiB, 16-byte chunks per row
+    static constexpr int NSL = RH * (NKK + 2 * NDT);  // MFMA slots of a pipeline step
     static constexpr int KT = BC * ROW;  // bytes of one K (or V) block
     static constexpr int KS0 = 0, KS1 = KT, VS0 = 2 * KT, VS1 = 3 * KT;  // LDS slots
     static constexpr int NDMA = KT / (64 * NW * 16);  // 16-byte copies per lane per block
@@ -961,31 +982,33 @@ struct Wide128 {
 // Returns false when the tile must be recomputed (see above); then nothing
 // of o, m, l (or the partial state) has been written by this call.  With
 // exact_ref the reference of each row is its exact maximum, and the call
-// always succeeds.  kv_lo is a multiple of 128 and, for the causal relation,
-// the tile starts at a multiple of 128 with kv_lo = 0, so only the last block
-// can cross the diagonal or the tail.
+// always succeeds.  q_lo - kv_lo is a multiple of 128 and, for the causal
+// relations, kv_hi = q_hi, so only the last block can cross the diagonal or
+// the tail.
 // The key groups' merge of a tile whose waves own 32 rows each (8 waves):
-// wave (rg, kg) finalizes the feature tiles 2 kg and 2 kg + 1 of its rows.  It
-// hands its other two tiles, and per row m_ref, m_true and l, to its partner
-// (rg, 1 - kg) through region (rg, 1 - kg) of the merge buffer (8 KiB each)
-// and takes the partner's from region (rg, kg), which it then reuses to turn
-// its O tiles into whole-row stores.  Returns false (nothing written) when a
-// wave raised the recompute flag.
-template <typename T, bool O16>
+// wave (rg, kg) finalizes the feature tiles kg NH .. kg NH + NH - 1 (NH = NDT / 2)
+// of its rows.  It hands its other tiles, and per row m_ref, m_true and l, to
+// its partner (rg, 1 - kg) through region (rg, 1 - kg) of the merge buffer
+// (NH 4 KiB each) and takes the partner's from region (rg, kg), which it then
+// reuses to turn its O tiles into whole-row stores.  Returns false (nothing
+// written) when a wave raised the recompute flag.
+template <typename T, int D, bool O16>
 __device__ __forceinline__ bool wide_merge_rows32(const FwdParams &p, char *mbuf, char *stats,
                                                   int *flag, int h, int q_hi, int split,
                                                   int wrow_lo, int rg, int kg, int lane,
-                                                  f32x16 (&U)[4], float m_ref, float m_true,
+                                                  f32x16 (&U)[D / 32], float m_ref, float m_true,
                                                   float l_tot, float c) {
-    constexpr int D = 128;
+    constexpr int NH = D / 64;         // feature tiles each wave finalizes
+    constexpr int RW = NH * 4 * 64;    // float4 per region
+    constexpr int CH = D / 8;          // 16-byte chunks per row of this wave's half of O
     const int c32 = lane & 31, g = lane >> 5;
-    f32x4 *give = reinterpret_cast<f32x4 *>(mbuf) + (rg * 2 + 1 - kg) * 8 * 64 + lane;
-    const f32x4 *take = reinterpret_cast<const f32x4 *>(mbuf) + (rg * 2 + kg) * 8 * 64 + lane;
+    f32x4 *give = reinterpret_cast<f32x4 *>(mbuf) + (rg * 2 + 1 - kg) * RW + lane;
+    const f32x4 *take = reinterpret_cast<const f32x4 *>(mbuf) + (rg * 2 + kg) * RW + lane;
     f32x4 *sb = reinterpret_cast<f32x4 *>(stats) + lane;
     const auto hand = [&](auto d0c) {
         constexpr int d0 = decltype(d0c)::value;
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
+        for (int t2 = 0; t2 < NH; ++t2)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const f32x4 val = {U[d0 + t2][4 * j], U[d0 + t2][4 * j + 1], U[d0 + t2][4 * j + 2],
@@ -993,7 +1016,7 @@ __device__ __forceinline__ bool wide_merge_rows32(const FwdParams &p, char *mbuf
                 give[(t2 * 4 + j) * 64] = val;
             }
     };
-    if (kg == 0) hand(std::integral_constant<int, 2>{});
+    if (kg == 0) hand(std::integral_constant<int, NH>{});
     else hand(std::integral_constant<int, 0>{});
     const f32x4 mine = {m_ref, m_true, l_tot, 0.f};
     sb[(rg * 2 + kg) * 64] = mine;
@@ -1009,13 +1032,17 @@ __device__ __forceinline__ bool wide_merge_rows32(const FwdParams &p, char *mbuf
     const float lt = l_tot * a0 + st[2] * a1;
     const float mt = vmax(m_true, st[1]);
     const int qrow = wrow_lo + c32;
+    // Physical chunk of logical chunk ch in row r of a region (rows of CH
+    // chunks): 16 lanes that write one chunk of 16 rows, or read the chunks of
+    // a row (or two), hit 16 distinct bank groups.
+    const auto pch = [](int r, int ch) { return CH == 16 ? (ch ^ (r & 15)) : (ch ^ ((r >> 1) & 7)); };
     const auto finish = [&](auto d0c) {
         constexpr int d0 = decltype(d0c)::value;
         if (split >= 0) {
             if (qrow >= q_hi) return;
             float *prow = p.part + (((int64_t)split * p.H + h) * p.n_q + qrow) * (D + 4);
 #pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2)
+            for (int t2 = 0; t2 < NH; ++t2)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const f32x4 u1 = take[(t2 * 4 + j) * 64];
@@ -1031,9 +1058,9 @@ __device__ __forceinline__ bool wide_merge_rows32(const FwdParams &p, char *mbuf
             return;
         }
         const float b0 = a0 / lt, b1 = a1 / lt;
-        f32x4 val[2][4];
+        f32x4 val[NH][4];
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
+        for (int t2 = 0; t2 < NH; ++t2)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const f32x4 u1 = take[(t2 * 4 + j) * 64];
@@ -1044,41 +1071,43 @@ __device__ __forceinline__ bool wide_merge_rows32(const FwdParams &p, char *mbuf
             p.m[(int64_t)h * p.n_q + qrow] = mt * p.scale;
             p.l[(int64_t)h * p.n_q + qrow] = lt * fast_exp2((M - mt) * c);
         }
-        // Row c32 of the region: 16 chunks of 4 features (this wave's 64),
-        // chunk 8 t2 + 2 j + g at (chunk ^ (row & 15)).
+        // Row c32 of the region: CH chunks of 4 features (this wave's D / 2),
+        // chunk 8 t2 + 2 j + g.
         wait_lgkmcnt0();  // every read of the region has returned
-        f32x4 *obuf = reinterpret_cast<f32x4 *>(mbuf) + (rg * 2 + kg) * 8 * 64;
+        f32x4 *obuf = reinterpret_cast<f32x4 *>(mbuf) + (rg * 2 + kg) * RW;
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
+        for (int t2 = 0; t2 < NH; ++t2)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) obuf[c32 * 16 + ((8 * t2 + 2 * j + g) ^ (c32 & 15))] = val[t2][j];
+            for (int j = 0; j < 4; ++j) obuf[c32 * CH + pch(c32, 8 * t2 + 2 * j + g)] = val[t2][j];
         wait_lgkmcnt0();
         if constexpr (O16) {
+            constexpr int LPR = CH / 2, RPI = 64 / LPR;  // lanes per row, rows per instruction
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {  // 8 rows of 8 chunks of 8 values
-                const int r = 8 * i + (lane >> 3), c8 = lane & 7;
-                const f32x4 lo = obuf[r * 16 + ((2 * c8) ^ (r & 15))];
-                const f32x4 hi = obuf[r * 16 + ((2 * c8 + 1) ^ (r & 15))];
+            for (int i = 0; i < 32 / RPI; ++i) {  // 8 values per lane
+                const int r = RPI * i + lane / LPR, c8 = lane % LPR;
+                const f32x4 lo = obuf[r * CH + pch(r, 2 * c8)];
+                const f32x4 hi = obuf[r * CH + pch(r, 2 * c8 + 1)];
                 if (wrow_lo + r < q_hi) {
                     T *dst = static_cast<T *>(p.o) + (int64_t)h * p.o_sh + (int64_t)(wrow_lo + r) * p.o_sn +
-                             64 * kg + 8 * c8;
+                             (D / 2) * kg + 8 * c8;
                     store4_16(dst, lo);
                     store4_16(dst + 4, hi);
                 }
             }
         } else {
+            constexpr int RPI = 64 / CH;  // rows per instruction
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {  // 4 rows of 16 chunks of 4 values
-                const int r = 4 * i + (lane >> 4), ch = lane & 15;
-                const f32x4 v4 = obuf[r * 16 + (ch ^ (r & 15))];
+            for (int i = 0; i < 32 / RPI; ++i) {  // 4 values per lane
+                const int r = RPI * i + lane / CH, ch = lane % CH;
+                const f32x4 v4 = obuf[r * CH + pch(r, ch)];
                 if (wrow_lo + r < q_hi)
                     *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + (int64_t)h * p.o_sh +
-                                               (int64_t)(wrow_lo + r) * p.o_sn + 64 * kg + 4 * ch) = v4;
+                                               (int64_t)(wrow_lo + r) * p.o_sn + (D / 2) * kg + 4 * ch) = v4;
             }
         }
     };
     if (kg == 0) finish(std::integral_constant<int, 0>{});
-    else finish(std::integral_constant<int, 2>{});
+    else finish(std::integral_constant<int, NH>{});
     // The next tile's copies reuse the slots: a barrier without a memory
     // fence (the stores above need not have landed; every LDS read here has).
     wait_lgkmcnt0();
@@ -1086,15 +1115,15 @@ __device__ __forceinline__ bool wide_merge_rows32(const FwdParams &p, char *mbuf
     return true;
 }
 
-template <typename T, int MASK, bool O16>
+template <typename T, int D, int MASK, bool O16>
 __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, int h, int q_lo,
                                               int q_hi, int kv_lo, int kv_hi, int split,
                                               bool exact_ref) {
-    typedef Wide128 C;
-    constexpr int RH = C::RH;
+    typedef WideCfg<D> C;
+    constexpr int RH = C::RH, ROW = C::ROW;
     typedef typename Half8<T>::vec vec8;
-    constexpr bool causal = MASK == kCausal;
-    constexpr int D = C::D, NDT = D / 32, NKK = D / 16, esz = (int)sizeof(T);
+    constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
+    constexpr int NDT = C::NDT, NKK = C::NKK, esz = (int)sizeof(T);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rg = wave % C::RGN, kg = wave / C::RGN;  // row group of 32 RH rows, key group
@@ -1109,18 +1138,19 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
     const uint32_t lds0 = (uint32_t)(uintptr_t)(OSATTN_LDS char *)smem;
 
     // F1: copy i of this wave fills bytes [(NW i + wave) KiB, +1 KiB) of a
-    // block, i.e. rows 16 i + 4 wave + L / 16, 16-byte chunk L % 16 of each
-    // (stored at its swizzled place); rows at or past kv_hi arrive as zeros.
-    const int drow = 4 * wave + (lane >> 4);
-    const int k_goff = drow * rowb + ((lane & 15) ^ (drow & 15)) * 16;
-    const int v_goff = drow * rowb + ((lane & 15) ^ ((drow & 3) << 2)) * 16;
+    // block, i.e. rows RPK (NW i + wave) + L / CPR, 16-byte chunk L % CPR of
+    // each (stored at its swizzled place, the same for every copy i); rows at
+    // or past kv_hi arrive as zeros.
+    const int drow = C::RPK * wave + lane / C::CPR;
+    const int k_goff = drow * rowb + swz_k<ROW>(drow, lane % C::CPR) * 16;
+    const int v_goff = drow * rowb + swz_vt<ROW>(drow, lane % C::CPR) * 16;
     const int max_rows = 0x7ffffff0 / rowb;  // rows one buffer resource may span
     const auto desc = [&](const T *base, int b) {  // block b of K or V
         const int k0 = kv_lo + b * C::BC;
         return rsrc_words(base + (int64_t)k0 * p.kv_sn, min(kv_hi - k0, max_rows) * rowb);
     };
     const auto copy_one = [&](const i32x4 &r, uint32_t slot, int goff, int i) {
-        dma16_asm(r, lds0 + slot + (C::NW * i + wave) * 1024, goff + 4 * C::NW * i * rowb);
+        dma16_asm(r, lds0 + slot + (C::NW * i + wave) * 1024, goff + C::RPK * C::NW * i * rowb);
     };
     const auto copy = [&](const T *base, int b, uint32_t slot, int goff) {
         asm volatile("" : "+v"(goff));  // per-copy offsets are formed here, not hoisted
@@ -1185,20 +1215,20 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
     // driver flips the slot bit); cc, hf and the +8 rows are immediate offsets.
     int ka[NKK], va[NDT];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) ka[kk] = (C::KH * kg + c32) * C::ROW + (((2 * kk + g) ^ (c32 & 15)) * 16);
+    for (int kk = 0; kk < NKK; ++kk) ka[kk] = (C::KH * kg + c32) * ROW + swz_k<ROW>(c32, 2 * kk + g) * 16;
     {
         const int vr = C::KH * kg + 4 * g + ((lane & 15) >> 2);
         const int cq = lane & 3, hh = (lane >> 4) & 1;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
-            va[dt] = C::VS0 + vr * C::ROW + (((4 * dt + 2 * hh + (cq >> 1)) ^ (((lane >> 2) & 3) << 2)) * 16) + 8 * (cq & 1);
+            va[dt] = C::VS0 + vr * ROW + swz_vt<ROW>(vr, 4 * dt + 2 * hh + (cq >> 1)) * 16 + 8 * (cq & 1);
     }
     const auto kread = [&](int kk, int off) {
         return *reinterpret_cast<const vec8 *>(smem + ka[kk] + off);
     };
     const auto vread = [&](int dt, int off) {
         const i16x4 lo = lds_read_tr16(smem + va[dt] + off);
-        const i16x4 hi = lds_read_tr16(smem + va[dt] + off + 8 * C::ROW);
+        const i16x4 hi = lds_read_tr16(smem + va[dt] + off + 8 * ROW);
         return __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
@@ -1245,8 +1275,8 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
         constexpr bool CK = decltype(CKc)::value, CV = decltype(CVc)::value;
         constexpr bool FIRST = decltype(FIRSTc)::value;
         // S(s+1) and P(s-1) V read chunk 0 of their block on odd steps, 1 on even.
-        constexpr int KOFF = ODD ? 0 : 8192;
-        constexpr int VOFF = ODD ? 0 : 8192;
+        constexpr int KOFF = ODD ? 0 : 32 * ROW;
+        constexpr int VOFF = ODD ? 0 : 32 * ROW;
         // Block boundary (odd steps): K((s+1)/2) and V((s-1)/2) have landed;
         // the copies of K((s+3)/2) and V((s+1)/2) are issued one per slot in
         // slots 0 .. 15, beside the MFMAs.
@@ -1284,30 +1314,31 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
         // RH j + RH - 1 (one per row half).  The reads for S(s+1) come first (K, 16
         // features kk per read), so that S(s+1) is complete long before the
         // next step reads it, then those for P(s-1) V (V, 32 features dt,
-        // 16-key half hf).  Even slot 2j issues read j + FD; every slot then
+        // 16-key half hf).  Slot i issues read i / RH + FD; every slot then
         // issues its MFMA and its share of the softmax; a scheduling fence
         // after each slot keeps that order (it bounds the operands in flight).
-        constexpr int NRD = (HS ? 8 : 0) + (HP ? 8 : 0);  // operand reads
+        constexpr int NRD = (HS ? NKK : 0) + (HP ? 2 * NDT : 0);  // operand reads
         constexpr int FD = 4;                             // reads in flight ahead of use
-        // read code: 0..7 = K with kk, 8 + 4 hf + dt = V of (dt, hf)
-        constexpr auto rdc = [](int j) { return HS ? j : 8 + j; };
+        // read code: kk < NKK = K with kk, NKK + NDT hf + dt = V of (dt, hf)
+        constexpr auto rdc = [](int j) { return HS ? j : NKK + j; };
         vec8 opnd[FD + 1];
         const auto fetch = [&](auto jc) {
             constexpr int j = decltype(jc)::value;
             if constexpr (j < NRD) {
                 constexpr int o = rdc(j);
-                if constexpr (o < 8) opnd[j % (FD + 1)] = kread(o, KOFF);
-                else opnd[j % (FD + 1)] = vread(o & 3, VOFF + 4096 * ((o - 8) >> 2));
+                if constexpr (o < NKK) opnd[j % (FD + 1)] = kread(o, KOFF);
+                else opnd[j % (FD + 1)] = vread((o - NKK) % NDT, VOFF + 16 * ROW * ((o - NKK) / NDT));
             }
         };
         const auto mma = [&](auto ic) {
             constexpr int i = decltype(ic)::value, j = i / RH, qh = i % RH;
             if constexpr (j < NRD) {
                 constexpr int o = rdc(j);
-                if constexpr (o < 8)
+                if constexpr (o < NKK)
                     Sn[qh] = Half8<T>::mma(opnd[j % (FD + 1)], qreg[qh][o], o == 0 ? zero_vec<f32x16>() : Sn[qh]);
                 else
-                    U[qh][o & 3] = Half8<T>::mma(opnd[j % (FD + 1)], Pp[qh][(o - 8) >> 2], U[qh][o & 3]);
+                    U[qh][(o - NKK) % NDT] = Half8<T>::mma(opnd[j % (FD + 1)], Pp[qh][(o - NKK) / NDT],
+                                                           U[qh][(o - NKK) % NDT]);
             }
         };
         const auto dma = [&](auto ic) {
@@ -1317,13 +1348,14 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
         };
         float t[RH][4], ps[RH][4], y[RH][16];
         f32x8 x[RH][2];
-        // Softmax of chunk s in slot-sized pieces, slot i taking piece i / RH
-        // of row half i % RH: F4 (chunk maximum; on step 0 it becomes the
-        // reference), then F5 (probabilities: f32 into l, rounded to T as the
-        // P.V operand).  Each exponential is taken one piece after the
-        // multiply-add that forms its argument.
-        const auto valu = [&](auto ic) {
-            constexpr int i = decltype(ic)::value, qh = i % RH, pc = i / RH;
+        // Softmax of chunk s in 16 pieces per row half, slot i taking pieces
+        // PPS (i / RH) .. + PPS - 1 of row half i % RH: F4 (chunk maximum; on
+        // step 0 it becomes the reference), then F5 (probabilities: f32 into
+        // l, rounded to T as the P.V operand).  Each exponential is taken one
+        // piece after the multiply-add that forms its argument.
+        constexpr int PPS = 16 * RH / C::NSL;  // pieces per slot
+        const auto piece = [&](auto qhc, auto pcc) {
+            constexpr int qh = decltype(qhc)::value, pc = decltype(pcc)::value;
             const f32x16 &S = Sc[qh];
             if constexpr (pc == 0) {
                 t[qh][0] = vmax(vmax(S[0], S[1]), vmax(S[2], S[3]));
@@ -1367,6 +1399,12 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
                 l_run[qh] += (ps[qh][0] + ps[qh][1]) + (ps[qh][2] + ps[qh][3]);
             }
         };
+        const auto valu = [&](auto ic) {
+            constexpr int i = decltype(ic)::value, qh = i % RH, p0 = PPS * (i / RH);
+            for_each_index([&](auto kc) { piece(std::integral_constant<int, qh>{},
+                                                std::integral_constant<int, p0 + decltype(kc)::value>{}); },
+                           std::make_integer_sequence<int, PPS>{});
+        };
         const auto slot = [&](auto ic) {
             constexpr int i = decltype(ic)::value;
             if constexpr (i % RH == 0) fetch(std::integral_constant<int, i / RH + FD>{});
@@ -1376,7 +1414,7 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
             __builtin_amdgcn_sched_barrier(0);
         };
         for_each_index(fetch, std::make_integer_sequence<int, FD>{});
-        for_each_index(slot, std::make_integer_sequence<int, 16 * RH>{});
+        for_each_index(slot, std::make_integer_sequence<int, C::NSL>{});
     };
     using Y = std::true_type;
     using N = std::false_type;
@@ -1426,7 +1464,7 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
     for (int hf = 0; hf < 2; ++hf)  // P(2 nblk - 1) V: chunk 1 of the last block
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            const vec8 a = vread(dt, 8192 + 4096 * hf);
+            const vec8 a = vread(dt, 32 * ROW + 16 * ROW * hf);
 #pragma unroll
             for (int qh = 0; qh < RH; ++qh) U[qh][dt] = Half8<T>::mma(a, PB[qh][hf], U[qh][dt]);
         }
@@ -1439,36 +1477,49 @@ __device__ __forceinline__ bool fwd_wide_tile(const FwdParams &p, char *smem, in
     for (int qh = 0; qh < RH; ++qh) l_tot[qh] = xor32_sum(l_run[qh]);  // the lane halves' keys
     int *flag = reinterpret_cast<int *>(smem + C::FLAG);
     if (__any(bail) && lane == 0) *flag = 1;
-    return wide_merge_rows32<T, O16>(p, smem + C::KS0, smem + C::STATS, flag, h, q_hi, split, wrow_lo,
+    return wide_merge_rows32<T, D, O16>(p, smem + C::KS0, smem + C::STATS, flag, h, q_hi, split, wrow_lo,
                                      rg, kg, lane, U[0], m_ref[0], m_true[0], l_tot[0], c);
 }
 
 // A tile the wide routine hands back is run again with exact references (one
 // body of the routine in the kernel: the retry is the loop's second pass).
-template <typename T, int MASK, bool O16>
+template <typename T, int D, int MASK, bool O16>
 __device__ __forceinline__ void fwd_wide_or_retry(const FwdParams &p, char *smem, int h, int q_lo,
                                                   int q_hi, int kv_lo, int kv_hi, int split) {
 #pragma unroll 1
     for (int pass = 0; pass < 2; ++pass)
-        if (fwd_wide_tile<T, MASK, O16>(p, smem, h, q_lo, q_hi, kv_lo, kv_hi, split, pass == 1)) break;
+        if (fwd_wide_tile<T, D, MASK, O16>(p, smem, h, q_lo, q_hi, kv_lo, kv_hi, split, pass == 1)) break;
 }
 
 // The dense and causal 16-bit forward at D = 128 with 128-row tiles: one
 // workgroup of 8 waves per CU.  Work items as in fwd16_kernel: split-KV items
 // (dense), causal tile pairs (T-1-i, i) or single tiles heaviest first, dense
 // tiles.
-template <typename T, int MASK, bool O16>
-__global__ void __launch_bounds__(64 * Wide128::NW, 1) fwd_wide_kernel(FwdParams p) {
-    constexpr bool causal = MASK == kCausal;
-    __shared__ __attribute__((aligned(16))) char smem[Wide128::LDS];
+template <typename T, int D, int MASK, bool O16>
+__global__ void __launch_bounds__(64 * WideCfg<D>::NW, 1) fwd_wide_kernel(FwdParams p) {
+    constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
+    constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
+    __shared__ __attribute__((aligned(16))) char smem[WideCfg<D>::LDS];
     const int b = blockIdx.x;
+    if constexpr (varlen) {
+        const VarlenItem it = varlen_item(p, b / p.H);
+#pragma unroll 1
+        for (int k = 0; k < 2; ++k) {
+            const int tile = k == 0 ? it.t0 : it.t1;
+            if (tile < 0) break;
+            const int q_lo = it.lo + tile * kBR, q_hi = min(q_lo + kBR, it.hi);
+            if (q_lo >= q_hi) break;
+            fwd_wide_or_retry<T, D, MASK, O16>(p, smem, b % p.H, q_lo, q_hi, it.lo, causal ? q_hi : it.hi, -1);
+        }
+        return;
+    }
     if (!causal && p.splits > 1) {
         const int items = p.H * p.n_tiles;
         const int split = b / items, r = b % items;
         const int h = r % p.H, tile = r / p.H;
         const int q_lo = tile * kBR, q_hi = min(q_lo + kBR, p.n_q);
         const int k_lo = split * p.split_len, k_hi = min(k_lo + p.split_len, p.n_k);
-        fwd_wide_or_retry<T, MASK, O16>(p, smem, h, q_lo, q_hi, k_lo, k_hi, split);
+        fwd_wide_or_retry<T, D, MASK, O16>(p, smem, h, q_lo, q_hi, k_lo, k_hi, split);
         return;
     }
     const int h = b % p.H, rest = b / p.H;
@@ -1485,7 +1536,7 @@ __global__ void __launch_bounds__(64 * Wide128::NW, 1) fwd_wide_kernel(FwdParams
         const int tile = k == 0 ? t0 : t1;
         if (tile < 0) break;
         const int q_lo = tile * kBR, q_hi = min(q_lo + kBR, p.n_q);
-        fwd_wide_or_retry<T, MASK, O16>(p, smem, h, q_lo, q_hi, 0, causal ? q_hi : p.n_k, -1);
+        fwd_wide_or_retry<T, D, MASK, O16>(p, smem, h, q_lo, q_hi, 0, causal ? q_hi : p.n_k, -1);
     }
 }
 
@@ -1949,30 +2000,28 @@ __global__ void __launch_bounds__(kThreads, D == 64 ? 2 : 1) fwd32_kernel(FwdPar
 // ------------------------------------------------------------------ launch
 template <typename T, int D, int MASK, bool O16>
 static void launch_fwd16_o(const FwdParams &p, int grid, hipStream_t st) {
+    constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
     const dim3 g(grid), b(kT16);
-    if constexpr (D == 128 && (MASK == kDense || MASK == kCausal)) {
-        if (p.tile_rows == kBR) {  // 8 waves of 32 rows, one workgroup per CU
-            hipLaunchKernelGGL((fwd_wide_kernel<T, MASK, O16>), g, dim3(64 * Wide128::NW), 0, st, p);
-            return;
-        }
+    // 128-row tiles: the pipelined 8-wave kernel, one workgroup per CU.  Varlen
+    // problems whose sequences average under kWideVarlenRows rows stay on two
+    // 4-wave workgroups per CU instead, where one item's start and end overlap
+    // the other workgroup's scan (varlen causal, 16384 tokens in 20 sequences,
+    // H=8: D=64 fp16 48.9 us there against 58.5 us on the 8-wave kernel, D=128
+    // bf16 77.5 against 88.2 us; 6 sequences of 2000-8192 tokens, D=64: 255.6
+    // against 232.1 us).
+    if (p.tile_rows == kBR && (!varlen || (int64_t)p.n_q >= (int64_t)kWideVarlenRows * p.num_seqs)) {
+        hipLaunchKernelGGL((fwd_wide_kernel<T, D, MASK, O16>), g, dim3(64 * WideCfg<D>::NW), 0, st, p);
+        return;
     }
-    if constexpr (MASK == kDense || MASK == kCausal) {
-        if (p.tile_rows == 64) {
-            hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 2, 8, O16>), g, b, 0, st, p);
-            return;
-        }
-        if constexpr (D == 64) {
-            if (p.tile_rows == 32) {
-                hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 1, 8, O16>), g, b, 0, st, p);
-                return;
-            }
-        }
-    }
-    if constexpr (MASK == kVarlen || MASK == kVarlenCausal) {  // always four waves
+    if constexpr (varlen) {
         hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 4, 4, O16>), g, dim3(256), 0, st, p);
     } else {
-        if (p.waves == 4) hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 4, 4, O16>), g, dim3(256), 0, st, p);
-        else hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 4, 8, O16>), g, b, 0, st, p);
+        // 64- and (D = 64) 32-row tiles of small dense and causal grids
+        if (p.tile_rows == 64) {
+            hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 2, 8, O16>), g, b, 0, st, p);
+        } else if constexpr (D == 64) {
+            hipLaunchKernelGGL((fwd16_kernel<T, D, MASK, 2, 1, 8, O16>), g, b, 0, st, p);
+        }
     }
 }
 

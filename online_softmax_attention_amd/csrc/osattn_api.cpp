@@ -230,15 +230,12 @@ FwdPlan plan_forward(int dtype, int H, int64_t n_q, int64_t n_k, int d, int caus
         };
         while (pl.tile_rows > (d == 64 ? 32 : 64) && items(pl.tile_rows) < cus) pl.tile_rows /= 2;
     }
-    // Four-wave workgroups (64 KiB of LDS, two per CU, blocks of half as many
-    // keys) for varlen and for dense grids of 128-row tiles that fill two
-    // workgroups per CU.  Measured on MI355X: varlen causal 16k tokens H=8 D=64
-    // 62 -> 49 us, dense N=4096 H=16 D=128 144 -> 137 us; causal grids (tile
-    // pairs, one per CU) and smaller grids ran slower with four waves.
-    pl.waves = 8;
-    if (dtype != OSATTN_F32 && pl.splits == 1 && pl.tile_rows == 128 &&
-        (cu || (!causal && (int64_t)H * pl.n_tiles >= 2 * device_cus())))
-        pl.waves = 4;
+    // Dense and causal 128-row tiles run on the 8-wave pipelined kernel; the
+    // tiled kernel (fwd16) keeps the 64- and 32-row tiles with 8 waves and the
+    // varlen tiles of short sequences with four-wave workgroups (64 KiB of
+    // LDS, two per CU, blocks of half as many keys: varlen causal 16k tokens
+    // H=8 D=64 62 -> 49 us against 8 waves).
+    pl.waves = (dtype != OSATTN_F32 && cu) ? 4 : 8;
     // Varlen order: up to 64 sequences, each workgroup ranks its own tile pair
     // (sequences by tile count, no extra launch: 16k tokens in 20 sequences,
     // H=8 D=64: 47.4 + 4.9 us with the list kernel); more sequences use the
