@@ -172,6 +172,7 @@ __device__ __forceinline__ void dkdv16_tile(const BwdParams &p, char *smem, int 
     typedef Bwd16Cfg<D> C;
     typedef typename Half8<T>::vec vec8;
     constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
+    constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
     constexpr int esz = (int)sizeof(T);
     const int k_hi = min(k_lo + C::BK, ks.hi);
     const int qa = causal ? max(qs_all.lo, k_lo) : qs_all.lo;
@@ -186,20 +187,24 @@ __device__ __forceinline__ void dkdv16_tile(const BwdParams &p, char *smem, int 
     const int key = k_lo + 32 * kq + c32;      // this lane's key column
     const int kv_sn = (int)p.kv_sn, q_sn = (int)p.q_sn;
 
-    // Resident K and V of the tile (rows past k_hi arrive as zeros).
+    // Resident K and V of the tile (rows past k_hi arrive as zeros).  The
+    // copies are inline assembly (dma16_asm): the compiler, which would make
+    // the transposed operand reads of a block wait for the next block's copy
+    // in flight, leaves their order to the explicit waits and barriers.
     char *sK = smem, *sV = smem + C::BK * C::ROW;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(OSATTN_LDS char *)smem;
     {
         const T *kb = static_cast<const T *>(p.k) + (int64_t)h * p.kv_sh + (int64_t)k_lo * p.kv_sn;
         const T *vb = static_cast<const T *>(p.v) + (int64_t)h * p.kv_sh + (int64_t)k_lo * p.kv_sn;
         const int64_t bytes = (int64_t)(k_hi - k_lo) * p.kv_sn * esz;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, bytes), rv = make_rsrc(vb, bytes);
+        const i32x4 rk = rsrc_words64(kb, bytes), rv = rsrc_words64(vb, bytes);
 #pragma unroll
         for (int i = 0; i < C::NDMA_KV; ++i) {
             const int byte = (8 * i + wave) * 1024 + 16 * lane;
             const int row = byte / C::ROW, pch = (byte % C::ROW) / 16;
             const int off = row * kv_sn * esz + swz_k<C::ROW>(row, pch) * 16;
-            dma16(rk, sK + (8 * i + wave) * 1024, off);
-            dma16(rv, sV + (8 * i + wave) * 1024, off);
+            dma16_asm(rk, lds0 + (8 * i + wave) * 1024, off);
+            dma16_asm(rv, lds0 + C::BK * C::ROW + (8 * i + wave) * 1024, off);
         }
     }
 
@@ -210,27 +215,27 @@ __device__ __forceinline__ void dkdv16_tile(const BwdParams &p, char *smem, int 
     const float *dh = p.stat_delta + (int64_t)h * p.n_q;
     char *stage0 = smem + C::KVRES;
     auto issue = [&](int q0, int buf) {
-        char *sq = stage0 + buf * C::QSTAGE;
-        char *sdo = sq + C::QTILE;
-        float *sb = reinterpret_cast<float *>(sdo + C::QTILE);
-        float *sd = sb + C::BQ;
+        const uint32_t sq = lds0 + C::KVRES + buf * C::QSTAGE;
+        const uint32_t sdo = sq + C::QTILE;
+        const uint32_t sb = sdo + C::QTILE;  // beta, then D
+        const uint32_t sd = sb + 4 * C::BQ;
         const int64_t bytes = (int64_t)(qr.hi - q0) * p.q_sn * esz;
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(qh + (int64_t)q0 * p.q_sn, bytes);
-        const __amdgpu_buffer_rsrc_t rd = make_rsrc(doh + (int64_t)q0 * p.q_sn, bytes);
+        const i32x4 rq = rsrc_words64(qh + (int64_t)q0 * p.q_sn, bytes);
+        const i32x4 rd = rsrc_words64(doh + (int64_t)q0 * p.q_sn, bytes);
 #pragma unroll
         for (int i = 0; i < C::NDMA_K; ++i) {
             const int byte = (8 * i + wave) * 1024 + 16 * lane;
             const int row = byte / C::ROW, pch = (byte % C::ROW) / 16;
             const int off = row * q_sn * esz + swz_rt<C::ROW>(row, pch) * 16;
-            dma16(rq, sq + (8 * i + wave) * 1024, off);
-            dma16(rd, sdo + (8 * i + wave) * 1024, off);
+            dma16_asm(rq, sq + (8 * i + wave) * 1024, off);
+            dma16_asm(rd, sdo + (8 * i + wave) * 1024, off);
         }
         // beta and D: waves 0 .. BQ/64 - 1 move 64 floats each per array.
         if (wave < C::BQ / 64) {
             const int64_t sbytes = (int64_t)(qr.hi - q0) * 4;
-            const __amdgpu_buffer_rsrc_t rb = make_rsrc(bh + q0, sbytes), rdl = make_rsrc(dh + q0, sbytes);
-            dma4(rb, sb + 64 * wave, 4 * (64 * wave + lane));
-            dma4(rdl, sd + 64 * wave, 4 * (64 * wave + lane));
+            const i32x4 rb = rsrc_words64(bh + q0, sbytes), rdl = rsrc_words64(dh + q0, sbytes);
+            dma4_asm(rb, sb + 256 * wave, 4 * (64 * wave + lane));
+            dma4_asm(rdl, sd + 256 * wave, 4 * (64 * wave + lane));
         }
     };
 
@@ -348,7 +353,7 @@ __device__ __forceinline__ void dkdv16_tile(const BwdParams &p, char *smem, int 
                     dV[dt][4 * jj + e] += v[e];
                 }
             }
-        if (p.k_splits == 1) {
+        if (varlen || p.k_splits == 1) {  // varlen keys are never split
             const int64_t koff = (int64_t)h * p.kv_sh + (int64_t)opaque(key) * p.kv_sn;
             store_row16<T, C::NDT>(static_cast<T *>(p.dk) + koff, dK, g, p.scale);
             store_row16<T, C::NDT>(static_cast<T *>(p.dv) + koff, dV, g, 1.f);
@@ -372,8 +377,12 @@ __device__ __forceinline__ void dkdv16_item(const BwdParams &p, char *smem, int 
     // the query range [qlo, qhi) those keys meet.
     int split = 0, lo, hi, qlo, qhi, t0, t1 = -1;
     if constexpr (SCHED) {  // tiles (T-1-i, i) of one sequence, largest pairs first
+        // uniform: taken into scalar registers
         const int4 it = reinterpret_cast<const int4 *>(p.sched + 4)[rest];
-        lo = qlo = it.x; hi = qhi = it.y; t0 = it.z; t1 = it.w;
+        lo = qlo = __builtin_amdgcn_readfirstlane(it.x);
+        hi = qhi = __builtin_amdgcn_readfirstlane(it.y);
+        t0 = __builtin_amdgcn_readfirstlane(it.z);
+        t1 = __builtin_amdgcn_readfirstlane(it.w);
     } else {
         split = rest % p.k_splits;
         rest /= p.k_splits;
@@ -409,6 +418,7 @@ __device__ __forceinline__ void dq16_tile(const BwdParams &p, char *smem, int h,
     typedef Bwd16Cfg<D> C;
     typedef typename Half8<T>::vec vec8;
     constexpr bool causal = MASK == kCausal || MASK == kVarlenCausal;
+    constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
     constexpr int esz = (int)sizeof(T);
     const int q_hi = min(q_lo + 128, qs_all.hi);
     const int kv_end = causal ? q_hi : ks_all.hi;
@@ -440,18 +450,20 @@ __device__ __forceinline__ void dq16_tile(const BwdParams &p, char *smem, int h,
     const T *kh = static_cast<const T *>(p.k) + (int64_t)h * p.kv_sh;
     const T *vh = static_cast<const T *>(p.v) + (int64_t)h * p.kv_sh;
     const int kv_sn = (int)p.kv_sn;
+    // K and V copies as inline assembly (see dkdv16_tile).
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(OSATTN_LDS char *)smem;
     auto issue = [&](int k0, int buf) {
         const int64_t bytes = (int64_t)(kv_hi - k0) * kv_sn * esz;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh + (int64_t)k0 * kv_sn, bytes);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh + (int64_t)k0 * kv_sn, bytes);
-        char *sk = smem + buf * C::KSTAGE;
-        char *sv = sk + C::KTILE;
+        const i32x4 rk = rsrc_words64(kh + (int64_t)k0 * kv_sn, bytes);
+        const i32x4 rv = rsrc_words64(vh + (int64_t)k0 * kv_sn, bytes);
+        const uint32_t sk = lds0 + buf * C::KSTAGE;
+        const uint32_t sv = sk + C::KTILE;
 #pragma unroll
         for (int i = 0; i < C::NDMA_Q; ++i) {
             const int byte = (8 * i + wave) * 1024 + 16 * lane;
             const int row = byte / C::ROW, pch = (byte % C::ROW) / 16;
-            dma16(rk, sk + (8 * i + wave) * 1024, row * kv_sn * esz + swz_rt<C::ROW>(row, pch) * 16);
-            dma16(rv, sv + (8 * i + wave) * 1024, row * kv_sn * esz + swz_k<C::ROW>(row, pch) * 16);
+            dma16_asm(rk, sk + (8 * i + wave) * 1024, row * kv_sn * esz + swz_rt<C::ROW>(row, pch) * 16);
+            dma16_asm(rv, sv + (8 * i + wave) * 1024, row * kv_sn * esz + swz_k<C::ROW>(row, pch) * 16);
         }
     };
 
@@ -544,7 +556,7 @@ __device__ __forceinline__ void dq16_tile(const BwdParams &p, char *smem, int h,
 #pragma unroll
                 for (int e = 0; e < 4; ++e) dQ[dt][4 * jj + e] += a[e];
             }
-        if (p.q_splits == 1) {
+        if (varlen || p.q_splits == 1) {  // varlen queries are never split
             store_row16<T, C::NDT>(static_cast<T *>(p.dq) + (int64_t)h * p.q_sh + (int64_t)opaque(qrow) * p.q_sn, dQ, g, p.scale);
         } else {
             const int64_t off = (((int64_t)split * p.H + h) * p.n_q + qrow) * D;
@@ -566,7 +578,10 @@ __device__ __forceinline__ void dq16_item(const BwdParams &p, char *smem, int b)
     int split = 0, lo, hi, klo, khi, t0, t1 = -1;
     if constexpr (SCHED) {  // tiles (T-1-i, i) of one sequence, largest pairs first
         const int4 it = reinterpret_cast<const int4 *>(p.sched + 4)[rest];
-        lo = klo = it.x; hi = khi = it.y; t0 = it.z; t1 = it.w;
+        lo = klo = __builtin_amdgcn_readfirstlane(it.x);
+        hi = khi = __builtin_amdgcn_readfirstlane(it.y);
+        t0 = __builtin_amdgcn_readfirstlane(it.z);
+        t1 = __builtin_amdgcn_readfirstlane(it.w);
     } else {
         split = rest % p.q_splits;
         rest /= p.q_splits;

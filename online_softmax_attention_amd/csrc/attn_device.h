@@ -217,12 +217,28 @@ __device__ __forceinline__ i32x4 rsrc_words(const void *base, int bytes) {
 // lane L; lds is wave-uniform.  Completion is counted by vmcnt only.  As
 // inline assembly the copy leaves the ordering of LDS reads to the caller's
 // explicit waits and barriers (the compiler would make every LDS read wait for
-// every copy in flight).
+// every copy in flight).  The s_nop is the one wait state gfx9 requires
+// between a scalar write of M0 and an LDS copy that reads it (the compiler
+// inserts it for its own copies, not inside inline assembly).
 __device__ __forceinline__ void dma16_asm(i32x4 rsrc, uint32_t lds, int voff) {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
                  : "v"(voff), "s"(rsrc), "{m0}"(lds)
                  : "memory");
+}
+
+// The same copy with 4 bytes per lane: lane L writes LDS bytes [lds + 4 L, +4).
+__device__ __forceinline__ void dma4_asm(i32x4 rsrc, uint32_t lds, int voff) {
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(lds)
+                 : "memory");
+}
+
+// rsrc_words over [base, base + bytes) with bytes clamped to [0, 0x7ffffff0],
+// as make_rsrc clamps them.
+__device__ __forceinline__ i32x4 rsrc_words64(const void *base, int64_t bytes) {
+    return rsrc_words(base, bytes < 0 ? 0 : (bytes > 0x7ffffff0LL ? 0x7ffffff0 : (int)bytes));
 }
 
 // Row of the 32x32 MFMA result held in register r by lane half g.
