@@ -142,6 +142,38 @@ __device__ __forceinline__ void store_row16(T *rowp, const f32x16 (&acc)[NDT], i
             *reinterpret_cast<t4 *>(rowp + 32 * dt + 8 * j + 4 * g) = __builtin_convertvector(v, t4);
         }
 }
+// Rows [0, nrows) (at most 32) of a 16-bit output whose row 0 is `rows` (row
+// stride sn elements), from a wave's transposed accumulator tiles (lane = row,
+// registers = features), scaled and rounded to T.  The values pass through
+// `stg` (the wave's own LDS, 32 rows of 2 D + 16 bytes): stored straight from
+// the tiles every instruction would write 8 bytes into each of 32 rows, which
+// measured ~8K cycles for the 64 KiB of a dK/dV item; from the staging each
+// instruction writes whole rows.
+template <typename T, int D>
+__device__ __forceinline__ void store_rows16_staged(char *stg, T *rows, int64_t sn, int nrows,
+                                                    const f32x16 (&acc)[D / 32], float scale, int lane) {
+    constexpr int P = 2 * D + 16;  // staging pitch in bytes (16-byte aligned rows)
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    const int c32 = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f32x4 v = {acc[dt][4 * j] * scale, acc[dt][4 * j + 1] * scale, acc[dt][4 * j + 2] * scale,
+                       acc[dt][4 * j + 3] * scale};
+            *reinterpret_cast<t4 *>(stg + c32 * P + (32 * dt + 8 * j + 4 * g) * 2) = __builtin_convertvector(v, t4);
+        }
+    wait_lgkmcnt0();
+    asm volatile("" ::: "memory");
+    constexpr int LPR = 2 * D / 16, RPI = 64 / LPR;  // lanes per row, rows per instruction
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+        const int r = RPI * i + lane / LPR, c = lane % LPR;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + r * P + 16 * c);
+        if (r < nrows) *reinterpret_cast<u32x4 *>(rows + (int64_t)r * sn + 8 * c) = v;
+    }
+}
+
 template <int NDT>
 __device__ __forceinline__ void store_row_part(float *rowp, const f32x16 (&acc)[NDT], int g, float scale) {
 #pragma unroll
@@ -181,7 +213,7 @@ __device__ __forceinline__ void dkdv16_tile(const BwdParams &p, char *smem, int 
     // The wave index is uniform; taking it into a scalar register makes the
     // per-wave tests below (tail, diagonal chunk) scalar branches instead of
     // masked selects on every element.
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tid = threadIdx.x, lane = opaque(tid & 63), wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kq = wave & 3, qg = wave >> 2;  // key group, query half
     const int c32 = lane & 31, g = lane >> 5;
     const int key = k_lo + 32 * kq + c32;      // this lane's key column
@@ -340,7 +372,7 @@ __device__ __forceinline__ void dkdv16_tile(const BwdParams &p, char *smem, int 
             }
     }
     __syncthreads();
-    if (qg == 0 && key < k_hi) {
+    if (qg == 0) {
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
@@ -354,10 +386,17 @@ __device__ __forceinline__ void dkdv16_tile(const BwdParams &p, char *smem, int 
                 }
             }
         if (varlen || p.k_splits == 1) {  // varlen keys are never split
-            const int64_t koff = (int64_t)h * p.kv_sh + (int64_t)opaque(key) * p.kv_sn;
-            store_row16<T, C::NDT>(static_cast<T *>(p.dk) + koff, dK, g, p.scale);
-            store_row16<T, C::NDT>(static_cast<T *>(p.dv) + koff, dV, g, 1.f);
-        } else {
+            // The staging reuses this wave's own half of the merge buffer,
+            // once every read of it has returned.
+            wait_lgkmcnt0();
+            asm volatile("" ::: "memory");
+            char *stg = smem + kq * 2 * (D / 8) * 64 * 16;
+            const int r0 = k_lo + 32 * kq;
+            const int64_t koff = (int64_t)h * p.kv_sh + (int64_t)opaque(r0) * p.kv_sn;
+            store_rows16_staged<T, D>(stg, static_cast<T *>(p.dk) + koff, p.kv_sn, k_hi - r0, dK, p.scale, lane);
+            store_rows16_staged<T, D>(stg + 32 * (2 * D + 16), static_cast<T *>(p.dv) + koff, p.kv_sn,
+                                      k_hi - r0, dV, 1.f, lane);
+        } else if (key < k_hi) {
             const int64_t off = (((int64_t)split * p.H + h) * p.n_k + key) * D;
             store_row_part<C::NDT>(p.dk_part + off, dK, g, p.scale);
             store_row_part<C::NDT>(p.dv_part + off, dV, g, 1.f);
@@ -425,7 +464,7 @@ __device__ __forceinline__ void dq16_tile(const BwdParams &p, char *smem, int h,
     const Range16 kr = split16(ks_all.lo, kv_end, split, p.q_splits, C::BC);
     const int kv_lo = kr.lo, kv_hi = kr.hi;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
+    const int tid = threadIdx.x, lane = opaque(tid & 63), wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
     const int rg = wave & 3, kg = wave >> 2;
     const int c32 = lane & 31, g = lane >> 5;
     const int qrow = q_lo + 32 * rg + c32;
@@ -547,7 +586,7 @@ __device__ __forceinline__ void dq16_tile(const BwdParams &p, char *smem, int h,
             }
     }
     __syncthreads();
-    if (kg == 0 && qok) {
+    if (kg == 0) {
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
@@ -557,8 +596,14 @@ __device__ __forceinline__ void dq16_tile(const BwdParams &p, char *smem, int h,
                 for (int e = 0; e < 4; ++e) dQ[dt][4 * jj + e] += a[e];
             }
         if (varlen || p.q_splits == 1) {  // varlen queries are never split
-            store_row16<T, C::NDT>(static_cast<T *>(p.dq) + (int64_t)h * p.q_sh + (int64_t)opaque(qrow) * p.q_sn, dQ, g, p.scale);
-        } else {
+            // staged through this wave's own part of the merge buffer
+            wait_lgkmcnt0();
+            asm volatile("" ::: "memory");
+            char *stg = smem + rg * (D / 8) * 64 * 16;
+            const int r0 = q_lo + 32 * rg;
+            store_rows16_staged<T, D>(stg, static_cast<T *>(p.dq) + (int64_t)h * p.q_sh + (int64_t)opaque(r0) * p.q_sn,
+                                      p.q_sn, q_hi - r0, dQ, p.scale, lane);
+        } else if (qok) {
             const int64_t off = (((int64_t)split * p.H + h) * p.n_q + qrow) * D;
             store_row_part<C::NDT>(p.dq_part + off, dQ, g, p.scale);
         }
