@@ -222,10 +222,14 @@ __device__ __forceinline__ void dkdv16_tile(const BwdParams &p, char *smem, int 
     // Resident K and V of the tile (rows past k_hi arrive as zeros).  The
     // copies are inline assembly (dma16_asm): the compiler, which would make
     // the transposed operand reads of a block wait for the next block's copy
-    // in flight, leaves their order to the explicit waits and barriers.
+    // in flight, leaves their order to the explicit waits and barriers, and
+    // the compiler's fences no longer wait for them either.  A tile with no
+    // query block (an empty part of a split query range) copies nothing: its
+    // merge writes this LDS at once.
     char *sK = smem, *sV = smem + C::BK * C::ROW;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(OSATTN_LDS char *)smem;
-    {
+    const int nblk = (qr.hi - qr.lo + C::BQ - 1) / C::BQ;
+    if (nblk > 0) {
         const T *kb = static_cast<const T *>(p.k) + (int64_t)h * p.kv_sh + (int64_t)k_lo * p.kv_sn;
         const T *vb = static_cast<const T *>(p.v) + (int64_t)h * p.kv_sh + (int64_t)k_lo * p.kv_sn;
         const int64_t bytes = (int64_t)(k_hi - k_lo) * p.kv_sn * esz;
@@ -278,7 +282,6 @@ __device__ __forceinline__ void dkdv16_tile(const BwdParams &p, char *smem, int 
         dV[dt] = zero_vec<f32x16>();
     }
     const float c = p.scale_log2;
-    const int nblk = (qr.hi - qr.lo + C::BQ - 1) / C::BQ;
     const int krow = 32 * kq + c32;  // this lane's row of the resident tiles
 
     if (nblk > 0) issue(qr.lo, 0);
@@ -356,6 +359,7 @@ __device__ __forceinline__ void dkdv16_tile(const BwdParams &p, char *smem, int 
             }
         }
     }
+    wait_vmcnt<0>();  // no copy is in flight (each was waited for in the loop)
     __syncthreads();  // every wave is done with the stages and the resident tiles
 
     // Merge the two query halves: half 1 leaves dK^T, dV^T in LDS.
@@ -572,6 +576,7 @@ __device__ __forceinline__ void dq16_tile(const BwdParams &p, char *smem, int h,
             }
         }
     }
+    wait_vmcnt<0>();  // no copy is in flight (each was waited for in the loop)
     __syncthreads();
 
     // Merge the two key halves: half 1 leaves dQ^T in LDS.

@@ -483,6 +483,27 @@ def test_workload_bwd_full_size(osattn, oracle, name, heads):
             assert_grad_close(got[i][h], ref[i], w.dtype, "%s %s head %d" % (name, nm, h))
 
 
+
+# Causal problems small enough to split their query ranges: the dK/dV items of
+# the last key tiles get empty parts of a split, which copy no K/V block and go
+# straight to their merge.  (Once, such an item left its K/V copies in flight
+# and they could land on the merge buffer: reruns then disagreed.)  Eight
+# reruns must agree bit for bit, and with the oracle.
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64)])
+def test_bwd_split_reruns_identical(osattn, oracle, dtype, D):
+    w = small("splitrr", 4, 1024, 1024, D, dtype, True, 8300 + D, backward=True)
+    inp = W.make_inputs(w)
+    q, k, v, do = (to_dev(x, dtype) for x in (inp.q, inp.k, inp.v, inp.do))
+    o, m, l = osattn.fwd(q, k, v, scale=w.softmax_scale, causal=True)
+    runs = [osattn.bwd(q, k, v, o, do, m, l, scale=w.softmax_scale, causal=True) for _ in range(8)]
+    torch.cuda.synchronize()
+    for i, r in enumerate(runs[1:]):
+        for name, a, b in zip(("dq", "dk", "dv"), r, runs[0]):
+            assert torch.equal(a, b), "rerun %d: %s differs" % (i + 1, name)
+    ref = oracle.attn_bwd(inp.q32, inp.k32, inp.v32, inp.do32, w.softmax_scale, causal=True)
+    for name, g, r in zip(("dq", "dk", "dv"), runs[0], ref[:3]):
+        assert_grad_close(host(g), r, dtype, "split reruns %s %s" % (dtype, name))
+
 # ------------------------------------------------------------ split-KV forward
 @pytest.mark.parametrize("dtype,D,n_q,n_k,H", [("f16", 64, 128, 16384, 4), ("bf16", 128, 300, 2100, 2),
                                                ("f16", 128, 129, 4097, 1), ("bf16", 64, 1, 8191, 3),
