@@ -410,7 +410,8 @@ __device__ __forceinline__ void dkdv16_tile(const BwdParams &p, char *smem, int 
 }
 
 // Work item b of the dK/dV pass.  SCHED: varlen items from the sorted work
-// list (one or two tiles each); otherwise one tile of the natural grid.
+// list (one or two tiles each); otherwise one tile of the natural grid, or
+// with pair_k (causal) the tiles i and T-1-i, T-i and i+1 query tiles of work.
 template <typename T, int D, int MASK, bool SCHED>
 __device__ __forceinline__ void dkdv16_item(const BwdParams &p, char *smem, int b) {
     constexpr bool varlen = MASK == kVarlen || MASK == kVarlenCausal;
@@ -437,18 +438,13 @@ __device__ __forceinline__ void dkdv16_item(const BwdParams &p, char *smem, int 
         const Range16 ks = axis16<varlen>(p, seq, p.n_k), qs = axis16<varlen>(p, seq, p.n_q);
         lo = ks.lo; hi = ks.hi; qlo = qs.lo; qhi = qs.hi;
         t0 = rest;  // causal: key tile 0 (the most queries) first
+        if (MASK == kCausal && p.pair_k && p.k_tiles - 1 - rest != rest) t1 = p.k_tiles - 1 - rest;
     }
-    if constexpr (SCHED) {
 #pragma unroll 1
-        for (int k = 0; k < 2; ++k) {
-            const int t = k == 0 ? t0 : t1;
-            if (t < 0 || lo + t * 128 >= hi) break;
-            dkdv16_tile<T, D, MASK>(p, smem, h, split, {lo, hi}, {qlo, qhi}, lo + t * 128);
-        }
-    } else {
-        (void)t1;
-        if (t0 < 0 || lo + t0 * 128 >= hi) return;
-        dkdv16_tile<T, D, MASK>(p, smem, h, split, {lo, hi}, {qlo, qhi}, lo + t0 * 128);
+    for (int k = 0; k < 2; ++k) {
+        const int t = k == 0 ? t0 : t1;
+        if (t < 0 || lo + t * 128 >= hi) break;
+        dkdv16_tile<T, D, MASK>(p, smem, h, split, {lo, hi}, {qlo, qhi}, lo + t * 128);
     }
 }
 
@@ -643,18 +639,13 @@ __device__ __forceinline__ void dq16_item(const BwdParams &p, char *smem, int b)
         const Range16 qs = axis16<varlen>(p, seq, p.n_q), ks = axis16<varlen>(p, seq, p.n_k);
         lo = qs.lo; hi = qs.hi; klo = ks.lo; khi = ks.hi;
         t0 = causal ? (p.q_tiles - 1 - rest) : rest;  // causal: heaviest first
+        if (MASK == kCausal && p.pair_q && p.q_tiles - 1 - rest != rest) t1 = rest;
     }
-    if constexpr (SCHED) {
 #pragma unroll 1
-        for (int k = 0; k < 2; ++k) {
-            const int t = k == 0 ? t0 : t1;
-            if (t < 0 || lo + t * 128 >= hi) break;
-            dq16_tile<T, D, MASK>(p, smem, h, split, {lo, hi}, {klo, khi}, lo + t * 128);
-        }
-    } else {
-        (void)t1;
-        if (t0 < 0 || lo + t0 * 128 >= hi) return;
-        dq16_tile<T, D, MASK>(p, smem, h, split, {lo, hi}, {klo, khi}, lo + t0 * 128);
+    for (int k = 0; k < 2; ++k) {
+        const int t = k == 0 ? t0 : t1;
+        if (t < 0 || lo + t * 128 >= hi) break;
+        dq16_tile<T, D, MASK>(p, smem, h, split, {lo, hi}, {klo, khi}, lo + t * 128);
     }
 }
 
@@ -718,8 +709,8 @@ static hipError_t launch_bwd16_typed(int mask, const BwdParams &p, int seqs, hip
     hipLaunchKernelGGL((bwd16_pre_kernel<T, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    int64_t grid_k = (int64_t)p.H * p.k_splits * seqs * p.k_tiles;
-    int64_t grid_q = (int64_t)p.H * p.q_splits * seqs * p.q_tiles;
+    int64_t grid_k = (int64_t)p.H * p.k_splits * seqs * (p.pair_k ? (p.k_tiles + 1) / 2 : p.k_tiles);
+    int64_t grid_q = (int64_t)p.H * p.q_splits * seqs * (p.pair_q ? (p.q_tiles + 1) / 2 : p.q_tiles);
     if (p.sched) grid_k = grid_q = (int64_t)p.H * p.sched_max;  // one workgroup per listed pair
     if (grid_k + grid_q > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     BwdParams pf = p;

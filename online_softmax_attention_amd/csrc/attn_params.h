@@ -86,6 +86,9 @@ struct BwdParams {
     const int32_t *sched;
     int sched_max;
     int grid_k;            // fp16/bf16: blocks of the one launch that run dK/dV items
+    // fp16/bf16 causal, one split: each dK/dV (dQ) item runs the tiles i and
+    // T-1-i of its head, so that every item holds the same work.
+    int pair_k, pair_q;
 };
 
 // CSR segment softmax over given edge scores.

@@ -257,6 +257,7 @@ int mask_kind(int causal, const int32_t *cu) {
 // ---------------------------------------------------------------- bwd plan
 struct BwdPlan {
     int q_tiles, k_tiles, q_splits, k_splits, seqs;
+    int pair_k, pair_q;          // fp16/bf16 causal: items of two tiles (i, T-1-i)
     int sched_max, sched_shift;  // fp16/bf16 varlen work list (0: none)
     size_t off_delta, off_mlog2, off_linv, off_dq, off_dk, off_dv, off_sched, total;
 };
@@ -287,6 +288,8 @@ BwdPlan plan_backward(int dtype, int H, int64_t n_q, int64_t n_k, int d, int cau
     const int64_t base_q = (int64_t)H * pl.seqs * pl.q_tiles;
     pl.k_splits = varlen ? 1 : clampi((target + base_k - 1) / base_k, 1, clampi(n_q / 256, 1, 16));
     pl.q_splits = varlen ? 1 : clampi((target + base_q - 1) / base_q, 1, clampi(n_k / 256, 1, 16));
+    pl.pair_k = dtype != OSATTN_F32 && causal && !varlen && pl.k_splits == 1;
+    pl.pair_q = dtype != OSATTN_F32 && causal && !varlen && pl.q_splits == 1;
     size_t off = 0;
     const size_t rowbytes = round256((size_t)H * n_q * sizeof(float));
     pl.off_delta = off; off += rowbytes;
@@ -387,6 +390,7 @@ int bwd_launch(int dtype, size_t es_o, int H, int64_t n_q, int64_t n_k, int d, c
     p.dv_part = reinterpret_cast<float *>(ws + pl.off_dv);
     p.q_tiles = pl.q_tiles; p.k_tiles = pl.k_tiles;
     p.q_splits = pl.q_splits; p.k_splits = pl.k_splits;
+    p.pair_k = pl.pair_k; p.pair_q = pl.pair_q;
     if (pl.sched_max > 0) {
         p.sched = reinterpret_cast<int32_t *>(ws + pl.off_sched);
         p.sched_max = pl.sched_max;
