@@ -362,6 +362,9 @@ BWD16_CASES = [
     (False, 1024, 256, 1, None), (False, 200, 1024, 1, None), (False, 1, 1, 1, None),
     (True, 0, 0, 2, [384, 1, 96, 640, 57]), (False, 0, 0, 1, [130, 0, 7, 300]),
     (True, 0, 0, 2, [256, 256, 256]),  # equal lengths: the natural varlen grid (no work list)
+    # causal, unsplit (32 heads x 9 tiles fill the device): items of two tiles
+    # (i, 8 - i) and the middle tile alone, with a ragged last tile
+    (True, 1100, 1100, 32, None),
 ]
 
 
