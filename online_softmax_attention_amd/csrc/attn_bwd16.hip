@@ -732,11 +732,16 @@ static hipError_t launch_bwd16_typed(int mask, const BwdParams &p, int seqs, hip
     hipLaunchKernelGGL((bwd16_pre_kernel<T, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    int64_t grid_k = (int64_t)p.H * p.k_splits * seqs * (p.pair_k ? (p.k_tiles + 1) / 2 : p.k_tiles);
-    int64_t grid_q = (int64_t)p.H * p.q_splits * seqs * (p.pair_q ? (p.q_tiles + 1) / 2 : p.q_tiles);
+    // Tile pairs only where the items read them: the causal relation, one split.
+    const int pair_k = p.pair_k && mask == kCausal && p.k_splits == 1;
+    const int pair_q = p.pair_q && mask == kCausal && p.q_splits == 1;
+    int64_t grid_k = (int64_t)p.H * p.k_splits * seqs * (pair_k ? (p.k_tiles + 1) / 2 : p.k_tiles);
+    int64_t grid_q = (int64_t)p.H * p.q_splits * seqs * (pair_q ? (p.q_tiles + 1) / 2 : p.q_tiles);
     if (p.sched) grid_k = grid_q = (int64_t)p.H * p.sched_max;  // one workgroup per listed pair
     if (grid_k + grid_q > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     BwdParams pf = p;
+    pf.pair_k = pair_k;
+    pf.pair_q = pair_q;
     pf.grid_k = (int)grid_k;
     const int grid = (int)(grid_k + grid_q);
     switch (mask) {
