@@ -596,6 +596,7 @@ TILE_CASES = [  # (causal, H, n_q, n_k, tile rows selected at D = 64)
     (False, 32, 1100, 333, 128), (False, 16, 1100, 333, 64), (False, 8, 1100, 333, 32),
     (False, 2, 700, 1500, 32),
     (True, 64, 1000, 1000, 128),  # paired
+    (True, 64, 1100, 1100, 128),  # paired, 9 tiles: the middle tile alone, a ragged last tile
     (True, 32, 1000, 1000, 64),   # paired
     (True, 16, 1000, 1000, 64), (True, 8, 1000, 1000, 32), (True, 2, 777, 777, 32),
 ]
