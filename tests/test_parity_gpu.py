@@ -507,6 +507,29 @@ def test_bwd_split_reruns_identical(osattn, oracle, dtype, D):
     for name, g, r in zip(("dq", "dk", "dv"), runs[0], ref[:3]):
         assert_grad_close(host(g), r, dtype, "split reruns %s %s" % (dtype, name))
 
+# A long causal sequence: N=8192 (64 tiles of 128 rows, up to 64 key blocks in
+# one tile's scan), H=4, so both passes of the backward run unsplit on the
+# paired grid.  Every forward row is compared; the backward on two heads (the
+# oracle materialises a head's score matrix).
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64)])
+def test_long_causal_sequence(osattn, oracle, dtype, D):
+    w = small("long", 4, 8192, 8192, D, dtype, True, 8800 + D, backward=True)
+    inp = W.make_inputs(w)
+    q, k, v, do = (to_dev(x, dtype) for x in (inp.q, inp.k, inp.v, inp.do))
+    o, m, l = osattn.fwd(q, k, v, scale=w.softmax_scale, causal=True)
+    dq, dk, dv = osattn.bwd(q, k, v, o, do, m, l, scale=w.softmax_scale, causal=True)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.attn_fwd(inp.q32, inp.k32, inp.v32, w.softmax_scale, causal=True)
+    assert_fwd_close(host(o), host(m), host(l), ro, rm, rl, dtype, "long causal %s D=%d" % (dtype, D))
+    got = [host(t) for t in (dq, dk, dv)]
+    for h in (0, 3):
+        sl = lambda x: np.ascontiguousarray(x[h:h + 1])
+        ref = oracle.attn_bwd(sl(inp.q32), sl(inp.k32), sl(inp.v32), sl(inp.do32), w.softmax_scale,
+                              causal=True)
+        for i, nm in enumerate(("dq", "dk", "dv")):
+            assert_grad_close(got[i][h], ref[i][0], dtype, "long causal %s D=%d %s head %d" % (dtype, D, nm, h))
+
+
 # ------------------------------------------------------------ split-KV forward
 @pytest.mark.parametrize("dtype,D,n_q,n_k,H", [("f16", 64, 128, 16384, 4), ("bf16", 128, 300, 2100, 2),
                                                ("f16", 128, 129, 4097, 1), ("bf16", 64, 1, 8191, 3),
