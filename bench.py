@@ -15,14 +15,18 @@ TFLOP/s of the whole step (forward 4 N_q N_k D H, halved for causal, summed per
 sequence for varlen; backward 2.5x the forward).  Rank 0 prints ONE JSON line
 (one per workload with --all) that also carries:
 
-  roofline     : the forward kernel's algorithmic FLOPs per launch over its
+  forward      : the forward kernel's algorithmic FLOPs per launch over its
                  average device duration (HIP events around a replayed graph of
                  back-to-back launches on the launch stream), against MI355X's
                  dense MFMA peak for its dtype;
                  traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE /
                  WRITE_SIZE counters recorded in profiles/traffic.json, or null
                  when the kernel sources changed since they were recorded;
-  backward     : the same record for the backward's kernels;
+  backward     : the same record for the backward's kernels (its pre-pass, the
+                 dK/dV and dQ kernel, a split reduction where one runs);
+  roofline     : the record, of those two, whose launch takes the longer: the
+                 step's dominant kernel (the backward's, on a forward and
+                 backward step);
   cpu_baseline : the f64 CPU oracle timed on this host's cores on a bounded
                  row sample of the same workload (a reported baseline only),
                  with the CPU model and the OpenMP thread setting;
@@ -383,7 +387,7 @@ def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True, 
                            "grad_head": grad_head,
                            "ok": bool(parity_rec["ok"] and gerr <= TOL[w.dtype])})
 
-    # Roofline of the forward kernel: FLOPs per launch over its average device
+    # The forward kernel's record: FLOPs per launch over its average device
     # duration, from HIP events around replays of a graph of back-to-back
     # forward launches on the launch stream.
     kern = fwd_kernel_name(w, torch, bool(fws_bytes) and not w.lengths)
@@ -402,13 +406,13 @@ def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True, 
     avg_ms = f0.elapsed_time(f1) / (n_per * reps)
     achieved = fwd_flops(w) / (avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": recorded_traffic(name, kern),
-                "kernel": kern, "launch_us_avg": avg_ms * 1e3, "launches": n_per * reps,
-                "flops_per_launch": fwd_flops(w)}
+    fwd_rec = {"pass": "forward", "bound": "mfma", "achieved": achieved, "peak": peak,
+               "unit": "TFLOP/s", "frac": achieved / peak, "traffic": recorded_traffic(name, kern),
+               "kernel": kern, "launch_us_avg": avg_ms * 1e3, "launches": n_per * reps,
+               "flops_per_launch": fwd_flops(w)}
     bwd_rec = None
     if bw is not None:
-        # Backward alone: same protocol as the forward roofline above.
+        # Backward alone: same protocol as the forward's record above.
         g_bwd = capture(bw, n_per, torch, stream)
         with torch.cuda.stream(stream):
             g_bwd.replay()
@@ -423,10 +427,15 @@ def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True, 
         bkern = BWD_KERNELS[w.dtype == "f32"]
         if w.lengths:
             bkern = "varlen_schedule_kernel+" + bkern
-        bwd_rec = {"bound": "mfma", "launch_us_avg": bwd_ms * 1e3, "achieved": bwd_ach,
-                   "peak": peak, "unit": "TFLOP/s", "frac": bwd_ach / peak,
-                   "flops_per_launch": bwd_flops(w), "kernel": bkern,
-                   "traffic": recorded_traffic(name + "+bwd", bkern)}
+        bwd_rec = {"pass": "backward", "bound": "mfma", "achieved": bwd_ach, "peak": peak,
+                   "unit": "TFLOP/s", "frac": bwd_ach / peak,
+                   "traffic": recorded_traffic(name + "+bwd", bkern), "kernel": bkern,
+                   "launch_us_avg": bwd_ms * 1e3, "launches": n_per * reps,
+                   "flops_per_launch": bwd_flops(w)}
+    # The step's dominant kernel: the launch that takes the longer.
+    roofline = fwd_rec
+    if bwd_rec is not None and bwd_rec["launch_us_avg"] > fwd_rec["launch_us_avg"]:
+        roofline = bwd_rec
     if not parity_rec["ok"]:
         value = None  # a step that computes the wrong result has no throughput
     out = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
@@ -441,7 +450,7 @@ def run_workload(name, steps, warmup, torch, np, osa, W, oracle, with_cpu=True, 
                       "launch": "graphs of %d steps replayed" % G},
            "pct_of_peak": None if value is None else 100.0 * value / peak,
            "event_ms_per_step": e0.elapsed_time(e1) / steps,
-           "roofline": roofline, "parity": parity_rec}
+           "roofline": roofline, "forward": fwd_rec, "parity": parity_rec}
     if bwd_rec is not None:
         out["backward"] = bwd_rec
     if with_cpu:
